@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of the DSpark draft-head-and-verify chain on one MI355X.
+
+One step = one pass of the whole chain over one batch: Markov draft (gamma
+slots), confidence + survival, global top-B schedule, ragged pack, and
+rejection-sampling verify, all on the GPU with inputs resident in HBM. The
+target forward that sits between pack and verify in a serving engine is not
+part of the chain; its output (the packed target logits) is prepared once
+before timing -- every timed step processes the same batch, so the schedule
+and pack are the same each step, and this is checked after timing.
+
+Prints one JSON line: the metric (verified draft slots per second), the
+roofline of the dominant kernel (the per-slot bias GEMM + softmax-partials
+pass, timed with HIP events on the chain's stream), and the CPU oracle timed
+on a bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--config qwen3] [--mode static]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft slots/s (draft+schedule+verify chain) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, published
+MFMA_F32_PEAK_TFS = 157.3
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(arr):
+    import numpy as np
+    import torch
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+    if arr.dtype == np.uint32:
+        return torch.from_numpy(arr.view(np.int32)).cuda()
+    return torch.from_numpy(arr).cuda()
+
+
+def cpu_baseline(spec, inp, mode_name: str, budget_s: float = 12.0, n_req: int = 8):
+    """The oracle as it stands, on the first n_req requests of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    n = min(n_req, spec.R)
+    sub = {k: inp[k][:n] for k in ("U", "target", "h", "anchor", "req_ids")}
+    sub.update({k: inp[k] for k in ("W1", "W2", "w", "b", "raw_T")})
+    vmode = {"static": oracle.VERIFY_STATIC, "compact": oracle.VERIFY_COMPACT,
+             "cap_accept": oracle.VERIFY_CAP_ACCEPT}[mode_name]
+    slots, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        out = oracle.chain(sub, tiers=spec.tiers, staircase=spec.staircase,
+                           B_cap=min(spec.budgets[0], n * spec.gamma), verify_mode=vmode)
+        reps += 1
+        slots += n * spec.gamma if vmode != oracle.VERIFY_COMPACT else int(out["sched"]["K"])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": slots / dt, "unit": "slots/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {spec.R} requests of the {spec.name} workload, full "
+                      f"vocabulary V={spec.V}, {mode_name} verify; {reps} oracle chain steps in "
+                      f"{dt:.1f} s (float64 numpy, BLAS threads={threads})"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3")
+    ap.add_argument("--mode", default="static", choices=["static", "compact", "cap_accept"])
+    ap.add_argument("--budget", type=int, default=None, help="cap B on selected slots")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=None,
+                    help="steps of per-kernel event timing (default: --steps)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the chain has no multi-GPU path).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import synth
+    import draft_verify_sampling_markov_amd as dv
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    dv.load_library()
+    spec = synth.CONFIGS[args.config]
+    mode = dv.VERIFY_MODES[args.mode]
+    B_cap = spec.budgets[0] if args.budget is None else args.budget
+    t0 = time.time()
+    inp = synth.generate(spec)
+    log(f"[bench] generated {spec.name} inputs in {time.time() - t0:.1f} s")
+    dev = {k: to_dev(inp[k]) for k in ("U", "W1", "W2", "target", "h", "anchor", "w", "req_ids")}
+    sps = dv.cost_table_prepare(inp["raw_T"], spec.tiers, spec.staircase)
+    dev["sps_milli"] = to_dev(sps)
+    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B_cap, verify_mode=mode)
+
+    # one step with the target stand-in, to lay out the packed target rows
+    ch.run(gather=True)
+    torch.cuda.synchronize()
+    first = ch.results()
+    if first["totals"][1] < 0:
+        log(f"[bench] packed total {first['totals'][0]} exceeds every tier: failed workload")
+        return 1
+    K_sel = int(first["K"][0])
+    slots_per_step = spec.R * spec.gamma if mode != dv.VERIFY_COMPACT else K_sel
+
+    for _ in range(args.warmup):
+        ch.run(gather=False)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ----
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        ch.run(gather=False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    after = ch.results()
+    for key in ("win_len", "cu_seqlens", "totals", "tokens"):
+        if not np.array_equal(first[key], after[key]):
+            log(f"[bench] {key} changed between steps: the pre-laid target rows are stale")
+            return 1
+    value = slots_per_step / (wall / args.steps)
+    log(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms -> {ms_per_step:.4f} ms/step")
+
+    # ---- per-kernel / per-stage event timing on the chain's stream ----
+    P = args.profile_steps or args.steps
+    g = spec.gamma
+    gemm_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(g)] for _ in range(P)]
+    stage_names = ["draft", "confidence", "schedule", "pack", "verify"]
+    st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
+             for _ in range(P)]
+    for s in range(P):
+        ev = st_ev[s]
+        ev[0].record()
+        ch.draft_split(gemm_ev[s])
+        ev[1].record()
+        ch.confidence()
+        ev[2].record()
+        ch.schedule()
+        ev[3].record()
+        ch.pack()
+        ev[4].record()
+        ch.verify()
+        ev[5].record()
+    torch.cuda.synchronize()
+    gemm_ms = [a.elapsed_time(b) for row in gemm_ev for (a, b) in row]
+    gemm_avg_ms = float(np.mean(gemm_ms))
+    stages = {n: float(np.mean([st_ev[s][i].elapsed_time(st_ev[s][i + 1]) for s in range(P)]))
+              for i, n in enumerate(stage_names)}
+    prof = ch.results()
+    if not np.array_equal(prof["tokens"], first["tokens"]):
+        log("[bench] the per-slot draft differs from the draft call")
+        return 1
+
+    # ---- roofline of the dominant kernel (one slot's GEMM + softmax partials) ----
+    b = 2 if spec.dtype == "bf16" else 4
+    R, V, r = spec.R, spec.V, spec.r
+    n_t = -(-V // 64)
+    bytes_per_launch = R * V * b + r * V * b + R * r * b + n_t * R * 8
+    flops_per_launch = 2 * R * r * V
+    achieved_gbs = bytes_per_launch / (gemm_avg_ms * 1e-3) / 1e9
+    achieved_tfs = flops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFS
+    roofline = {"kernel": "markov_partials_kernel (per-slot bias GEMM + U add + softmax partials)",
+                "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(gemm_avg_ms * 1e3, 2),
+                "launches_timed": len(gemm_ms),
+                "mfma": {"achieved": round(achieved_tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                         "frac": round(achieved_tfs / mfma_peak, 4), "flops_per_launch": flops_per_launch}}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "slots/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": f"{spec.name}: R={R} gamma={g} V={V} r={r} d={spec.d} {spec.dtype}, "
+                               f"{args.mode} verify, B={B_cap}",
+                   "R": R, "gamma": g, "V": V, "r": r, "d": spec.d, "mode": args.mode,
+                   "B_cap": B_cap, "verified_slots_per_step": slots_per_step,
+                   "packed_total": int(first["totals"][0]), "tier": int(first["totals"][1])},
+        "accepted_tokens_per_s": round(float(first["n_out"].sum()) / (wall / args.steps), 1),
+        "mean_accept_len": round(float(first["accept_len"].mean()), 3),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(spec, inp, args.mode)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,338 @@
+"""Python binding of libdspark.so, the MI355X (gfx950) DSpark draft-head-and-verify chain.
+
+Argument marshalling only: every step of the chain runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. The binding
+raises if the library is missing -- there is no fallback path.
+
+Calls (same names as the C ABI in include/dspark.h, without the prefix):
+    prepack_w2, markov_draft, confidence, schedule_topb, pack_ragged, verify,
+    cost_table_prepare, workspace_bytes, markov_logits
+and ``Chain``, which holds preallocated buffers for repeated steps.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdspark.so")
+
+F32, BF16 = 0, 1
+VERIFY_STATIC, VERIFY_COMPACT, VERIFY_CAP_ACCEPT = 0, 1, 2
+SCHED_ARGMAX, SCHED_GREEDY, SCHED_FIXED = 0, 1, 2
+CALL_MARKOV_DRAFT, CALL_VERIFY = 0, 1
+
+VERIFY_MODES = {"static": VERIFY_STATIC, "compact": VERIFY_COMPACT, "cap_accept": VERIFY_CAP_ACCEPT}
+SCHED_MODES = {"argmax": SCHED_ARGMAX, "greedy": SCHED_GREEDY, "fixed": SCHED_FIXED}
+
+_c = ctypes
+_vp, _i, _u64, _sz, _f = _c.c_void_p, _c.c_int, _c.c_uint64, _c.c_size_t, _c.c_float
+
+_SIGNATURES = {
+    "dspark_status_string": (_c.c_char_p, [_i]),
+    "dspark_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "dspark_prepacked_w2_bytes": (_sz, [_i, _i, _i]),
+    "dspark_prepack_w2": (_i, [_vp, _i, _i, _i, _vp, _sz, _vp]),
+    "dspark_cost_table_prepare": (_i, [_vp, _i, _vp, _i, _i, _vp]),
+    "dspark_markov_draft": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _i, _i, _i, _i, _i,
+                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dspark_confidence": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i,
+                               _vp, _vp, _vp]),
+    "dspark_schedule_topb": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "dspark_pack_ragged": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                                _vp]),
+    "dspark_verify": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _u64,
+                           _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dspark_markov_logits": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "dspark_markov_partials": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz,
+                                    _vp]),
+    "dspark_markov_select": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _vp, _u64, _u64, _vp, _i, _i,
+                                  _i, _i, _i, _vp, _vp, _vp, _i, _vp]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdspark.so (build it with ``python -m draft_verify_sampling_markov_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP library first "
+                           "(python -m draft_verify_sampling_markov_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class DsparkError(RuntimeError):
+    pass
+
+
+def status_string(rc: int) -> str:
+    return load_library().dspark_status_string(rc).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise DsparkError(status_string(rc))
+
+
+# ---------------------------------------------------------------------------
+# tensor helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _dev(t, name: str, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype=None, shape=None):
+    return None if t is None else _dev(t, name, dtype, shape)
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _empty(shape, dtype, device):
+    return _torch().empty(shape, dtype=dtype, device=device)
+
+
+# ---------------------------------------------------------------------------
+# utilities
+# ---------------------------------------------------------------------------
+
+def workspace_bytes(call: int, R: int, gamma: int, V: int, r: int) -> int:
+    return int(load_library().dspark_workspace_bytes(call, R, gamma, V, r))
+
+
+def prepacked_w2_bytes(r: int, V: int, dtype: int) -> int:
+    return int(load_library().dspark_prepacked_w2_bytes(r, V, dtype))
+
+
+def prepack_w2(W2, stream=None):
+    """W2 [r, V] (float32 or bfloat16) -> pre-packed operand buffer (same dtype)."""
+    torch = _torch()
+    r, V = W2.shape
+    dt = _dtype_code(W2)
+    nbytes = prepacked_w2_bytes(r, V, dt)
+    if nbytes == 0:
+        raise DsparkError("unsupported W2 shape")
+    out = torch.empty(nbytes // W2.element_size(), dtype=W2.dtype, device=W2.device)
+    _check(load_library().dspark_prepack_w2(_dev(W2, "W2"), r, V, dt, out.data_ptr(), nbytes,
+                                            _stream(stream)))
+    return out
+
+
+def cost_table_prepare(raw_step_time_s: Sequence[float], tiers: Sequence[int],
+                       staircase: bool) -> np.ndarray:
+    """Host call: raw step time T(M), M = 0..M_max -> sps_milli (uint32)."""
+    raw = np.ascontiguousarray(raw_step_time_s, dtype=np.float64)
+    tr = np.ascontiguousarray(tiers, dtype=np.int32)
+    out = np.zeros(raw.shape[0], dtype=np.uint32)
+    _check(load_library().dspark_cost_table_prepare(raw.ctypes.data, raw.shape[0] - 1,
+                                                    tr.ctypes.data, tr.shape[0], int(bool(staircase)),
+                                                    out.ctypes.data))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# hot calls
+# ---------------------------------------------------------------------------
+
+def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, req_ids=None,
+                 out=None, ws=None, stream=None):
+    """U [R, gamma, V]; W1 [V, r]; W2p pre-packed; anchor [R] int32.
+    Returns (tokens int32 [R, gamma], p_draft f32, lse_draft f32)."""
+    torch = _torch()
+    R, gamma, V = U.shape
+    dt = _dtype_code(U)
+    dev = U.device
+    if req_ids is None:
+        req_ids = torch.arange(R, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (_empty((R, gamma), torch.int32, dev), _empty((R, gamma), torch.float32, dev),
+               _empty((R, gamma), torch.float32, dev))
+    need = workspace_bytes(CALL_MARKOV_DRAFT, R, gamma, V, r)
+    if ws is None:
+        ws = _empty((max(need, 1),), torch.uint8, dev)
+    tokens, p, lse = out
+    _check(load_library().dspark_markov_draft(
+        _dev(U, "U"), _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
+        _dev(anchor, "anchor", torch.int32, (R,)), seed, step, _dev(req_ids, "req_ids", None, (R,)),
+        R, gamma, V, r, dt, _dev(tokens, "tokens", torch.int32, (R, gamma)),
+        _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
+        _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return tokens, p, lse
+
+
+def confidence(h, W1, anchor, tokens, w, b: float, inv_temp=None, out=None, stream=None):
+    """h [R, gamma, d]; W1 [V, r]; w [d + r] f32. Returns (conf, surv) f32 [R, gamma]."""
+    torch = _torch()
+    R, gamma, d = h.shape
+    V, r = W1.shape
+    dev = h.device
+    if out is None:
+        out = (_empty((R, gamma), torch.float32, dev), _empty((R, gamma), torch.float32, dev))
+    conf, surv = out
+    _check(load_library().dspark_confidence(
+        _dev(h, "h"), _dev(W1, "W1", h.dtype), _dev(anchor, "anchor", torch.int32, (R,)),
+        _dev(tokens, "tokens", torch.int32, (R, gamma)), _dev(w, "w", torch.float32, (d + r,)),
+        float(b), _opt(inv_temp, "inv_temp", torch.float32, (gamma,)), R, gamma, d, V, r,
+        _dtype_code(h), _dev(conf, "conf", torch.float32, (R, gamma)),
+        _dev(surv, "surv", torch.float32, (R, gamma)), _stream(stream)))
+    return conf, surv
+
+
+def schedule_topb(surv, sps_milli, *, B_cap: int, mode: int, K_fixed: int = 0, surv_budget=None,
+                  out=None, stream=None):
+    """surv [R, gamma] f32; sps_milli [M_max+1] (int32/uint32 device tensor).
+    Returns (win_len int32 [R], K int32 [1])."""
+    torch = _torch()
+    R, gamma = surv.shape
+    M_max = sps_milli.numel() - 1
+    if out is None:
+        out = (_empty((R,), torch.int32, surv.device), _empty((1,), torch.int32, surv.device))
+    win, K = out
+    _check(load_library().dspark_schedule_topb(
+        _dev(surv, "surv", torch.float32), _opt(surv_budget, "surv_budget", torch.float32, (R, gamma)),
+        _dev(sps_milli, "sps_milli"), M_max, R, gamma, int(B_cap), int(mode), int(K_fixed),
+        _dev(win, "win_len", torch.int32, (R,)), _dev(K, "K_out", torch.int32, (1,)), _stream(stream)))
+    return win, K
+
+
+def pack_ragged(anchor, tokens, win_len, tiers: Sequence[int], M_cap: int, out=None, stream=None):
+    """Returns dict of cu_seqlens [R+1], packed_tokens/req/slot [M_cap], totals [2] (int32)."""
+    torch = _torch()
+    R, gamma = tokens.shape
+    dev = tokens.device
+    if out is None:
+        out = {"cu_seqlens": _empty((R + 1,), torch.int32, dev),
+               "packed_tokens": _empty((M_cap,), torch.int32, dev),
+               "packed_req": _empty((M_cap,), torch.int32, dev),
+               "packed_slot": _empty((M_cap,), torch.int32, dev),
+               "totals": _empty((2,), torch.int32, dev)}
+    tr = np.ascontiguousarray(tiers, dtype=np.int32)
+    _check(load_library().dspark_pack_ragged(
+        _dev(anchor, "anchor", torch.int32, (R,)), _dev(tokens, "tokens", torch.int32),
+        _opt(win_len, "win_len", torch.int32, (R,)), R, gamma, tr.ctypes.data, tr.shape[0], M_cap,
+        _dev(out["cu_seqlens"], "cu_seqlens", torch.int32, (R + 1,)),
+        _dev(out["packed_tokens"], "packed_tokens", torch.int32),
+        _dev(out["packed_req"], "packed_req", torch.int32),
+        _dev(out["packed_slot"], "packed_slot", torch.int32),
+        _dev(out["totals"], "totals", torch.int32, (2,)), _stream(stream)))
+    return out
+
+
+def verify(target_packed, cu_seqlens, anchor, tokens, p_draft, lse_draft, U, W1, W2p, *, r: int,
+           mode: int, win_len=None, seed: int = 0, step: int = 0, req_ids=None,
+           with_ceiling: bool = True, out=None, ws=None, stream=None):
+    """Returns dict: accept_len [R], out_tokens [R, gamma+1], n_out [R], ceiling_len [R] or None."""
+    torch = _torch()
+    R, gamma, V = U.shape
+    M_cap = target_packed.shape[0]
+    dev = U.device
+    if req_ids is None:
+        req_ids = torch.arange(R, dtype=torch.int32, device=dev)
+    if out is None:
+        out = {"accept_len": _empty((R,), torch.int32, dev),
+               "out_tokens": _empty((R, gamma + 1), torch.int32, dev),
+               "n_out": _empty((R,), torch.int32, dev),
+               "ceiling_len": _empty((R,), torch.int32, dev) if with_ceiling else None}
+    need = workspace_bytes(CALL_VERIFY, R, gamma, V, r)
+    if ws is None:
+        ws = _empty((max(need, 1),), torch.uint8, dev)
+    _check(load_library().dspark_verify(
+        _dev(target_packed, "target_packed", U.dtype, (M_cap, V)), M_cap,
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)), _dev(anchor, "anchor", torch.int32, (R,)),
+        _dev(tokens, "tokens", torch.int32, (R, gamma)), _dev(p_draft, "p_draft", torch.float32, (R, gamma)),
+        _dev(lse_draft, "lse_draft", torch.float32, (R, gamma)), _dev(U, "U"),
+        _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
+        _opt(win_len, "win_len", torch.int32, (R,)), int(mode), seed, step,
+        _dev(req_ids, "req_ids", None, (R,)), R, gamma, V, r, _dtype_code(U),
+        _dev(out["accept_len"], "accept_len", torch.int32, (R,)),
+        _dev(out["out_tokens"], "out_tokens", torch.int32, (R, gamma + 1)),
+        _dev(out["n_out"], "n_out", torch.int32, (R,)),
+        _opt(out["ceiling_len"], "ceiling_len", torch.int32, (R,)),
+        _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def markov_partials(U_k, ldU: int, W1, W2p, x_prev, xstride: int, *, R: int, V: int, r: int,
+                    part, stream=None):
+    """One slot's GEMM + per-tile softmax partials into ``part`` (uint8 buffer)."""
+    _check(load_library().dspark_markov_partials(
+        U_k.data_ptr(), int(ldU), _dev(W1, "W1", U_k.dtype, (V, r)), _dev(W2p, "W2p", U_k.dtype),
+        x_prev.data_ptr(), int(xstride), R, V, r, _dtype_code(U_k), _dev(part, "part"),
+        part.numel() * part.element_size(), _stream(stream)))
+
+
+def markov_select(U_k, ldU: int, W1, W2p, x_prev, xstride: int, part, *, k: int, R: int, V: int,
+                  r: int, seed: int, step: int, req_ids, tok_out, p_out, lse_out, ostride: int,
+                  stream=None):
+    """One slot's draw from the partials of markov_partials (pointer-level outputs:
+    tok_out/p_out/lse_out may be strided views' base pointers given as tensors)."""
+    _check(load_library().dspark_markov_select(
+        U_k.data_ptr(), int(ldU), _dev(W1, "W1", U_k.dtype, (V, r)), _dev(W2p, "W2p", U_k.dtype),
+        x_prev.data_ptr(), int(xstride), _dev(part, "part"), seed, step, req_ids.data_ptr(), int(k),
+        R, V, r, _dtype_code(U_k), tok_out.data_ptr(), p_out.data_ptr(), lse_out.data_ptr(),
+        int(ostride), _stream(stream)))
+
+
+def markov_logits(U_k, ldU: int, W1, W2p, x_prev, *, R: int, V: int, r: int, stream=None):
+    """Diagnostic: full Markov logits z [R, V] f32 of one slot."""
+    torch = _torch()
+    z = _empty((R, V), torch.float32, U_k.device)
+    _check(load_library().dspark_markov_logits(
+        U_k.data_ptr(), int(ldU), _dev(W1, "W1", U_k.dtype, (V, r)), _dev(W2p, "W2p", U_k.dtype),
+        _dev(x_prev, "x_prev", torch.int32, (R,)), R, V, r, _dtype_code(U_k), z.data_ptr(),
+        _stream(stream)))
+    return z
+
+
+from .chain import Chain  # noqa: E402  (needs the functions above)
+
+__all__ = [
+    "load_library", "status_string", "DsparkError", "workspace_bytes", "prepacked_w2_bytes",
+    "prepack_w2", "cost_table_prepare", "markov_draft", "confidence", "schedule_topb",
+    "pack_ragged", "verify", "markov_logits", "markov_partials",
+    "markov_select", "Chain", "EXPORTS", "F32", "BF16",
+    "VERIFY_STATIC", "VERIFY_COMPACT", "VERIFY_CAP_ACCEPT", "SCHED_ARGMAX", "SCHED_GREEDY",
+    "SCHED_FIXED", "VERIFY_MODES", "SCHED_MODES",
+]

@@ -1,0 +1,284 @@
+// Device-side building blocks shared by the DSpark kernels (gfx950 / CDNA4).
+//
+// - element access for float32 and bfloat16 storage
+// - Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11), written from its
+//   published definition
+// - deterministic wave reductions (fixed butterfly order)
+// - the Markov bias tile: a 64-vocabulary x 16-request block of
+//   W1[x_prev] . W2 on the matrix cores (v_mfma_f32_16x16x32_bf16 for bf16,
+//   v_mfma_f32_16x16x4_f32 for f32)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kWave = 64;
+constexpr int kTileV = 64;     // vocabulary entries per Markov tile
+constexpr int kTileN = 16;     // requests per Markov tile
+constexpr int kChunkK = 32;    // rank entries per matrix-core step
+constexpr int kLdsPad = 8;     // elements of padding per W1 row in LDS
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+
+template <bool BF16> struct Elem;
+template <> struct Elem<true> {
+  typedef uint16_t T;       // bfloat16 bit pattern
+  typedef bf16x8 Frag;      // 8 values = one matrix-core operand
+  static constexpr int kVec = 8;  // elements per 16-byte load
+};
+template <> struct Elem<false> {
+  typedef float T;
+  typedef f32x8 Frag;
+  static constexpr int kVec = 4;
+};
+
+__device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float to_f32(float f) { return f; }
+
+// 16 consecutive elements p[0..15] as float; `n` of them are in range
+// (n >= 16: all). `vec` says p is 16-byte aligned for vector loads.
+template <bool BF16>
+__device__ __forceinline__ void load16(const typename Elem<BF16>::T* __restrict__ p, int n, bool vec,
+                                       float out[16]) {
+  if (vec && n >= 16) {
+    if constexpr (BF16) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(p);
+      u32x4 a = __builtin_nontemporal_load(q);
+      u32x4 b = __builtin_nontemporal_load(q + 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(a[i] << 16);
+        out[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+        out[8 + 2 * i] = __uint_as_float(b[i] << 16);
+        out[8 + 2 * i + 1] = __uint_as_float(b[i] & 0xFFFF0000u);
+      }
+    } else {
+      const f32x4* q = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a = __builtin_nontemporal_load(q + i);
+        out[4 * i] = a[0];
+        out[4 * i + 1] = a[1];
+        out[4 * i + 2] = a[2];
+        out[4 * i + 3] = a[3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = (i < n) ? to_f32(p[i]) : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10
+// ---------------------------------------------------------------------------
+
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;  // golden ratio
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;  // sqrt(3) - 1
+
+struct U64x4 { uint64_t w[4]; };
+
+__device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                               uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  U64x4 r;
+  r.w[0] = c0;
+  r.w[1] = c1;
+  r.w[2] = c2;
+  r.w[3] = c3;
+  return r;
+}
+
+enum { kPurposeDraft = 0, kPurposeAccept = 1, kPurposeResidual = 2, kPurposeBonus = 3 };
+
+// Uniform in [0, 1 - 2^-24] for slot k of request req_id: word `purpose` of the
+// Philox block with counter (k, req_id, step, 0) and key (seed, 0).
+__device__ __forceinline__ float slot_uniform(uint64_t seed, uint64_t step, uint32_t req_id, int k,
+                                              int purpose) {
+  const U64x4 b = philox4x64_10((uint64_t)k, (uint64_t)req_id, step, 0ull, seed, 0ull);
+  const uint32_t top = (uint32_t)(b.w[purpose] >> 40);
+  return (float)top * 5.9604644775390625e-8f;  // 2^-24, exact
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions (fixed order, deterministic)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele; fixed order).
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Merge two (max, sum of exp(z - max)) softmax partials.
+__device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) {
+    m = mm;
+    s = 0.0f;
+    return;
+  }
+  s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+  m = mm;
+}
+
+__device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
+
+// ---------------------------------------------------------------------------
+// Markov bias tile on the matrix cores
+// ---------------------------------------------------------------------------
+//
+// Pre-packed W2 layout (written by the prepack kernel): for tile t (64
+// vocabulary entries), rank chunk kc (32 ranks), sub-tile j (0..3) and lane l:
+// 8 consecutive elements
+//     W2p[(((t * KC + kc) * 4 + j) * 64 + l) * 8 + e] = W2[kc*32 + 8*(l/16) + e, v]
+//     v = 64 t + 16 (rho / 4) + 4 j + (rho % 4),  rho = l % 16
+// (zero outside r x V). With the matrix-core output layout (lane l holds
+// column l % 16 and rows 4 (l/16) .. 4 (l/16) + 3 of each 16 x 16 sub-tile),
+// lane l of a 16-request tile then ends up holding the 16 consecutive
+// vocabulary entries v = 64 t + 16 (l/16) + [0, 16) of request l % 16, entry
+// 4 j + i in acc[j][i].
+//
+// The W1 rows of the tile's 16 requests sit in LDS, row n at lds + n * ldw,
+// with ldw = KC * 32 + kLdsPad elements (padding spreads rows over banks).
+// Lane l reads ranks kc*32 + 8 (l/16) .. +8 of row l % 16.
+//
+// For float32 the 32-rank chunk is eight 16x16x4 steps; in step s, lane l
+// contributes rank kc*32 + 8 (l/16) + s on both operands, so the two operands
+// stay matched.
+
+template <bool BF16, int KC>
+struct ATile {
+  typename Elem<BF16>::Frag a[KC][4];
+};
+
+template <bool BF16, int KC>
+__device__ __forceinline__ void load_a_tile(const typename Elem<BF16>::T* __restrict__ W2p, int t,
+                                            int lane, ATile<BF16, KC>& at) {
+  typedef typename Elem<BF16>::Frag Frag;
+  const Frag* base = reinterpret_cast<const Frag*>(W2p) + (size_t)t * KC * 4 * kWave;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) at.a[kc][j] = base[(kc * 4 + j) * kWave + lane];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void mma_step(f32x4& acc, const typename Elem<BF16>::Frag& a,
+                                         const typename Elem<BF16>::Frag& b) {
+  if constexpr (BF16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+  }
+}
+
+// acc[j] = sum over ranks of W2-tile x W1-rows for the 16 requests whose rows
+// start at lds_rows (row stride ldw).
+template <bool BF16, int KC>
+__device__ __forceinline__ void tile_mma(const ATile<BF16, KC>& at,
+                                         const typename Elem<BF16>::T* lds_rows, int ldw, int lane,
+                                         f32x4 acc[4]) {
+  typedef typename Elem<BF16>::Frag Frag;
+  const typename Elem<BF16>::T* brow = lds_rows + (lane & 15) * ldw + 8 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const Frag b = *reinterpret_cast<const Frag*>(brow + kc * kChunkK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mma_step<BF16>(acc[j], at.a[kc][j], b);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// W1 row staging: rows of `count` requests whose tokens are xprev[n*xstride]
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__device__ __forceinline__ void stage_rows(const typename Elem<BF16>::T* __restrict__ W1,
+                                           const int* __restrict__ xprev, int xstride, int count,
+                                           int rows, int r, int V, int kpad, int ldw,
+                                           typename Elem<BF16>::T* lds) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int VEC = Elem<BF16>::kVec;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  if ((r % VEC) == 0) {
+    const int per_row = kpad / VEC;
+    const int total = rows * per_row;
+    for (int idx = tid; idx < total; idx += nth) {
+      const int n = idx / per_row, c = idx - n * per_row;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (n < count && c * VEC < r) {
+        const int tok = clamp_token(xprev[(size_t)n * xstride], V);
+        v = *reinterpret_cast<const u32x4*>(W1 + (size_t)tok * r + c * VEC);
+      }
+      *reinterpret_cast<u32x4*>(lds + n * ldw + c * VEC) = v;
+    }
+  } else {
+    const int total = rows * kpad;
+    for (int idx = tid; idx < total; idx += nth) {
+      const int n = idx / kpad, k = idx - n * kpad;
+      T v = (T)0;
+      if (n < count && k < r) v = W1[(size_t)clamp_token(xprev[(size_t)n * xstride], V) * r + k];
+      lds[n * ldw + k] = v;
+    }
+  }
+}
+
+// z values of one tile for the lane's request (lane & 15) and entries
+// v0 + [0, 16), v0 = 64 t + 16 (lane >> 4); invalid entries get -inf.
+template <bool BF16>
+__device__ __forceinline__ void tile_logits(const f32x4 acc[4], const float u16[16], int nvalid,
+                                            bool active, float z[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = 4 * j + i;
+      const float val = acc[j][i] + u16[idx];
+      z[idx] = (active && idx < nvalid) ? val : -INFINITY;
+    }
+}
+
+
+}  // namespace dspark

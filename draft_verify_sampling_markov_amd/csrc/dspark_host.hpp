@@ -1,0 +1,56 @@
+// Host-side helpers shared by the C ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dspark.h"
+
+namespace dspark {
+
+constexpr int kMaxGamma = 16;
+constexpr int kMaxRows = 4096;      // R * (gamma + 1)
+constexpr int kMaxRankBf16 = 256;
+constexpr int kMaxRankF32 = 128;
+constexpr int kMaxTiers = 32;
+constexpr int kReqGroup = 256;      // requests whose W1 rows share one LDS stage
+
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int rank_chunks(int r) { return ceil_div(r, 32); }
+// KC rounded up to the instantiated set {1, 2, 4, 8}.
+inline int kc_instance(int r) {
+  const int kc = rank_chunks(r);
+  return kc <= 1 ? 1 : kc <= 2 ? 2 : kc <= 4 ? 4 : 8;
+}
+inline int n_vtiles(int V) { return ceil_div(V, 64); }
+
+inline bool dtype_ok(int dt) { return dt == DSPARK_F32 || dt == DSPARK_BF16; }
+inline size_t dtype_bytes(int dt) { return dt == DSPARK_BF16 ? 2 : 4; }
+
+// Compute units of the current device (cached per device id).
+int device_cu_count();
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP; }
+
+// Check the launch that was just enqueued.
+inline int launch_status() { return hip_status(hipGetLastError()); }
+
+// Sizes shared by several calls.
+inline int check_sizes(int R, int gamma, int V, int r, int dt) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (R < 1 || gamma < 1 || V < 1 || r < 1) return DSPARK_ESIZE;
+  if (gamma > kMaxGamma) return DSPARK_ESIZE;
+  if ((long long)R * (gamma + 1) > kMaxRows) return DSPARK_ESIZE;
+  if (r > (dt == DSPARK_BF16 ? kMaxRankBf16 : kMaxRankF32)) return DSPARK_ESIZE;
+  if ((long long)V * (long long)R * (gamma + 1) > (1ll << 40)) return DSPARK_ESIZE;
+  return DSPARK_OK;
+}
+
+// Workspace layout pieces (bytes, 256-aligned).
+size_t markov_ws_bytes(int R, int V);
+size_t verify_ws_bytes(int R, int gamma, int V);
+
+}  // namespace dspark

@@ -1,0 +1,565 @@
+// Markov sequential draft head on gfx950.
+//
+// DSpark digest ("DSpark: Confidence-Scheduled Speculative Decoding with
+// Semi-Autoregressive Generation", zhao9797.github.io), section "Architecture
+// (drafter)": the block's base logits U_1..U_gamma come from one parallel
+// backbone forward; a Markov head adds the previous-token transition bias
+// B = W1 W2 (W1 in R^{V x r} read as a row lookup, W2 in R^{r x V} a
+// projection) and the block is sampled left to right from
+// softmax(U_k + W1[x_{k-1}] W2). The SGLang DSpark blog ("Performance
+// optimisation and zero-overhead scheduling") fuses this sampling path into
+// kernels; here it is two launches per slot:
+//
+//   markov_partials  the [R, r] x [r, V] bias GEMM on the matrix cores, with
+//                    W2 tiles streamed straight into registers (pre-packed
+//                    operand order) and the R gathered W1 rows staged in LDS;
+//                    each 64-entry vocabulary tile adds U_k and emits a softmax
+//                    partial (max, sum of exp) per request -- the [R, V]
+//                    logits never reach memory;
+//   markov_select    per request: merge the partials into (m, S), draw
+//                    u * S with the slot's Philox uniform, find the tile where
+//                    the cumulative mass crosses it, recompute that one tile
+//                    with the same matrix-core code (bit-identical logits) and
+//                    finish the inverse-CDF search inside it.
+#include "dspark_device.hpp"
+#include "dspark_host.hpp"
+
+#include <algorithm>
+
+namespace dspark {
+
+// ---------------------------------------------------------------------------
+// W2 pre-packing (layout documented in dspark_device.hpp)
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ void prepack_w2_kernel(const T* __restrict__ W2, int r, int V, int KC, int n_t,
+                                  T* __restrict__ W2p) {
+  const long long groups = (long long)n_t * KC * 4 * kWave;
+  for (long long gidx = (long long)blockIdx.x * blockDim.x + threadIdx.x; gidx < groups;
+       gidx += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(gidx % kWave);
+    const int j = (int)((gidx / kWave) % 4);
+    const int kc = (int)((gidx / (4 * kWave)) % KC);
+    const long long t = gidx / ((long long)4 * kWave * KC);
+    const int rho = lane & 15;
+    const long long v = 64 * t + 16 * (rho >> 2) + 4 * j + (rho & 3);
+    const int kb = kc * kChunkK + 8 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = kb + e;
+      W2p[gidx * 8 + e] = (k < r && v < V) ? W2[(size_t)k * V + v] : (T)0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pass A: bias GEMM + U add + per-tile softmax partials
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(512) void markov_partials_kernel(
+    const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
+    float2* __restrict__ part, int ldp) {
+  typedef typename Elem<BF16>::T T;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* w1s = reinterpret_cast<T*>(smem);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int g = lane >> 4, nl = lane & 15;
+  constexpr int kpad = KC * kChunkK;
+  constexpr int ldw = kpad + kLdsPad;
+  const int rows = (R + 15) & ~15;
+
+  stage_rows<BF16>(W1, xprev, xstride, R, rows, r, V, kpad, ldw, w1s);
+  __syncthreads();
+
+  for (int t = blockIdx.x * nwaves + wave; t < n_t; t += gridDim.x * nwaves) {
+    ATile<BF16, KC> at;
+    load_a_tile<BF16, KC>(W2p, t, lane, at);
+    const int v0 = t * kTileV + 16 * g;
+    const int nvalid = min(16, V - v0);
+    for (int nb = 0; nb < rows; nb += kTileN) {
+      const int n = nb + nl;
+      const bool active = n < R;
+      float u16[16];
+      if (active && nvalid > 0) {
+        load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
+      }
+      f32x4 acc[4];
+      tile_mma<BF16, KC>(at, w1s + nb * ldw, ldw, lane, acc);
+      float z[16];
+      tile_logits<BF16>(acc, u16, nvalid, active, z);
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, z[i]);
+      float s = 0.0f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += __expf(z[i] - m);
+      }
+      softmax_merge(m, s, __shfl_xor(m, 16, kWave), __shfl_xor(s, 16, kWave));
+      softmax_merge(m, s, __shfl_xor(m, 32, kWave), __shfl_xor(s, 32, kWave));
+      if (g == 0 && active) part[(size_t)t * ldp + n] = make_float2(m, s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pass B: per-request draw
+// ---------------------------------------------------------------------------
+
+struct SelectShared {
+  float m[16][16];     // [part][request]
+  float s[16][16];
+  float off[17][16];
+  int last[16][16];
+  float mrow[16], S[16], T[16], pb[16];
+  int tstar[16];
+};
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(256) void markov_select_kernel(
+    const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
+    const float2* __restrict__ part, int ldp, uint64_t seed, uint64_t step,
+    const uint32_t* __restrict__ req_ids, int k, int* __restrict__ tok_out,
+    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int kpad = KC * kChunkK;
+  constexpr int ldw = kpad + kLdsPad;
+  __shared__ __align__(16) T w1s[16 * ldw];
+  __shared__ SelectShared sh;
+
+  const int tid = threadIdx.x;
+  const int nb0 = blockIdx.x * kTileN;
+  const int count = min(kTileN, R - nb0);
+  stage_rows<BF16>(W1, xprev + (size_t)nb0 * xstride, xstride, count, 16, r, V, kpad, ldw, w1s);
+
+  // ---- phase 1: merge partials, find the crossing tile ----
+  const int q = tid & 15, p = tid >> 4;
+  const int n = nb0 + q;
+  const bool active = q < count;
+  const int c = (n_t + 15) / 16;
+  const int t0 = min(n_t, p * c), t1 = min(n_t, t0 + c);
+  float lm = -INFINITY;
+  if (active)
+    for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[(size_t)t * ldp + n].x);
+  sh.m[p][q] = lm;
+  __syncthreads();
+  float m = -INFINITY;
+#pragma unroll
+  for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, sh.m[pp][q]);
+  float ls = 0.0f;
+  int last = -1;
+  if (active && m != -INFINITY) {
+    for (int t = t0; t < t1; ++t) {
+      const float2 pv = part[(size_t)t * ldp + n];
+      const float w = pv.y * __expf(pv.x - m);
+      if (w > 0.0f) last = t;
+      ls += w;
+    }
+  }
+  sh.s[p][q] = ls;
+  sh.last[p][q] = last;
+  __syncthreads();
+  if (p == 0) {
+    float off = 0.0f;
+    int lst = -1;
+    for (int pp = 0; pp < 16; ++pp) {
+      sh.off[pp][q] = off;
+      off += sh.s[pp][q];
+      lst = max(lst, sh.last[pp][q]);
+    }
+    sh.off[16][q] = off;
+    sh.S[q] = off;
+    sh.mrow[q] = m;
+    float Tq = 0.0f;
+    if (active) Tq = slot_uniform(seed, step, req_ids[n], k, kPurposeDraft) * off;
+    sh.T[q] = Tq;
+    // fallback (no part owns T): last tile with mass, searched to its end
+    sh.tstar[q] = lst;
+    sh.pb[q] = -INFINITY;   // never crosses: the search ends at the last positive entry
+  }
+  __syncthreads();
+  if (active) {
+    const float Tq = sh.T[q], o0 = sh.off[p][q], o1 = sh.off[p + 1][q];
+    if (Tq >= o0 && Tq < o1) {
+      float lc = 0.0f;
+      for (int t = t0; t < t1; ++t) {
+        const float2 pv = part[(size_t)t * ldp + n];
+        const float lcn = lc + pv.y * __expf(pv.x - m);
+        if (o0 + lcn > Tq) {
+          sh.tstar[q] = t;
+          sh.pb[q] = o0 + lc;
+          break;
+        }
+        lc = lcn;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: recompute the crossing tile, finish the search ----
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int g = lane >> 4, nl = lane & 15;
+  for (int it = 0; it < 4; ++it) {
+    const int qq = wave + 4 * it;
+    if (qq >= count) continue;  // wave-uniform
+    const int nn = nb0 + qq;
+    const int t = min(max(sh.tstar[qq], 0), n_t - 1);
+    ATile<BF16, KC> at;
+    load_a_tile<BF16, KC>(W2p, t, lane, at);
+    f32x4 acc[4];
+    tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+    const int v0 = t * kTileV + 16 * g;
+    const int nvalid = min(16, V - v0);
+    float u16[16];
+    const bool mine = (nl == qq);
+    if (mine && nvalid > 0) {
+      load16<BF16>(U + (size_t)nn * ldU + v0, nvalid, vec, u16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
+    }
+    float z[16];
+    tile_logits<BF16>(acc, u16, nvalid, true, z);
+    // lane i of the wave takes entry v = 64 t + i from lane qq + 16 (i / 16)
+    const int src = qq + 16 * (lane >> 4);
+    float zi = -INFINITY;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const float val = __shfl(z[idx], src, kWave);
+      if ((lane & 15) == idx) zi = val;
+    }
+    const int v = t * kTileV + lane;
+    const bool valid = v < V;
+    const float mrow = sh.mrow[qq], S = sh.S[qq], Tq = sh.T[qq], pb = sh.pb[qq];
+    const float e = valid ? __expf(zi - mrow) : 0.0f;
+    const float sc = wave_inclusive_scan(e, lane);
+    const bool cross = valid && (pb + sc > Tq);
+    const unsigned long long cm = __ballot(cross);
+    int sel;
+    if (cm) {
+      sel = __ffsll((long long)cm) - 1;
+    } else {
+      const unsigned long long pm = __ballot(e > 0.0f);
+      sel = pm ? 63 - __clzll((long long)pm) : 0;
+    }
+    const float esel = __shfl(e, sel, kWave);
+    if (lane == 0) {
+      tok_out[(size_t)nn * ostride] = t * kTileV + sel;
+      p_out[(size_t)nn * ostride] = esel / S;
+      lse_out[(size_t)nn * ostride] = mrow + __logf(S);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// diagnostic: full logits of one slot
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(256) void markov_logits_kernel(
+    const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    const int* __restrict__ xprev, int R, int V, int r, int n_t, float* __restrict__ zout) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int kpad = KC * kChunkK;
+  constexpr int ldw = kpad + kLdsPad;
+  __shared__ __align__(16) T w1s[16 * ldw];
+  const int nb0 = blockIdx.y * kTileN;
+  const int count = min(kTileN, R - nb0);
+  stage_rows<BF16>(W1, xprev + nb0, 1, count, 16, r, V, kpad, ldw, w1s);
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int g = lane >> 4, nl = lane & 15;
+  const int t = blockIdx.x * (blockDim.x / kWave) + wave;
+  if (t >= n_t) return;  // wave-uniform; no barrier follows
+  ATile<BF16, KC> at;
+  load_a_tile<BF16, KC>(W2p, t, lane, at);
+  f32x4 acc[4];
+  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+  const int n = nb0 + nl;
+  const int v0 = t * kTileV + 16 * g;
+  const int nvalid = min(16, V - v0);
+  if (nl >= count || nvalid <= 0) return;
+  float u16[16];
+  load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
+  float z[16];
+  tile_logits<BF16>(acc, u16, nvalid, true, z);
+  for (int i = 0; i < nvalid; ++i) zout[(size_t)n * V + v0 + i] = z[i];
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+size_t markov_ws_bytes(int R, int V) { return align_up((size_t)n_vtiles(V) * R * sizeof(float2), 256); }
+
+template <bool BF16, int KC>
+static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
+                           const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
+                           const int32_t* xprev, int xstride, int R, int V, int r, float2* part,
+                           hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int ldw = KC * kChunkK + kLdsPad;
+  constexpr int threads = 512;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t max_lds = (size_t)((kReqGroup + 15) & ~15) * ldw * sizeof(T);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_partials_kernel<BF16, KC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds) != hipSuccess)
+      return DSPARK_EHIP;
+    attr_set = true;
+  }
+  const int n_t = n_vtiles(V);
+  const int ncu = device_cu_count();
+  for (int g0 = 0; g0 < R; g0 += kReqGroup) {
+    const int Rg = std::min(kReqGroup, R - g0);
+    const size_t lds = (size_t)((Rg + 15) & ~15) * ldw * sizeof(T);
+    const int per_cu = lds > 80 * 1024 ? 1 : 2;
+    const int grid = std::max(1, std::min(ceil_div(n_t, threads / kWave), ncu * per_cu));
+    hipLaunchKernelGGL((markov_partials_kernel<BF16, KC>), dim3(grid), dim3(threads), lds, s,
+                       Uk + (size_t)g0 * ldU, ldU, vec, W1, W2p, xprev + (size_t)g0 * xstride,
+                       xstride, Rg, V, r, n_t, part + g0, R);
+    const int st = launch_status();
+    if (st) return st;
+  }
+  return DSPARK_OK;
+}
+
+template <bool BF16, int KC>
+static int launch_markov(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
+                         uint64_t seed, uint64_t step, const uint32_t* req_ids, int R, int gamma,
+                         int V, int r, int32_t* tokens, float* p_draft, float* lse_draft,
+                         float2* part, hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  const T* Ub = static_cast<const T*>(U);
+  const T* W1b = static_cast<const T*>(W1);
+  const T* W2b = static_cast<const T*>(W2p);
+  const int n_t = n_vtiles(V);
+  const long long ldU = (long long)gamma * V;
+  const bool vec = (V % Elem<BF16>::kVec) == 0 && (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  for (int k = 1; k <= gamma; ++k) {
+    const int* xprev = (k == 1) ? anchor : tokens + (k - 2);
+    const int xstride = (k == 1) ? 1 : gamma;
+    const T* Uk = Ub + (size_t)(k - 1) * V;
+    int st = launch_partials<BF16, KC>(Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, part, s);
+    if (st) return st;
+    hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(ceil_div(R, kTileN)), dim3(256), 0, s,
+                       Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, n_t, part, R, seed, step,
+                       req_ids, k, tokens + (k - 1), p_draft + (k - 1), lse_draft + (k - 1), gamma);
+    st = launch_status();
+    if (st) return st;
+  }
+  return DSPARK_OK;
+}
+
+template <bool BF16, int KC>
+static int launch_partials_api(const void* U, long long ldU, const void* W1, const void* W2p,
+                               const int32_t* x_prev, int xstride, int R, int V, int r,
+                               float2* part, hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
+                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
+                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, s);
+}
+
+template <bool BF16, int KC>
+static int launch_logits(const void* U, long long ldU, const void* W1, const void* W2p,
+                         const int32_t* x_prev, int R, int V, int r, float* z, hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  const int n_t = n_vtiles(V);
+  const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
+                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  dim3 grid(ceil_div(n_t, 4), ceil_div(R, kTileN));
+  hipLaunchKernelGGL((markov_logits_kernel<BF16, KC>), grid, dim3(256), 0, s,
+                     static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
+                     static_cast<const T*>(W2p), x_prev, R, V, r, n_t, z);
+  return launch_status();
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" size_t dspark_prepacked_w2_bytes(int r, int V, int dtype) {
+  if (!dtype_ok(dtype) || r < 1 || V < 1) return 0;
+  if (r > (dtype == DSPARK_BF16 ? kMaxRankBf16 : kMaxRankF32)) return 0;
+  return (size_t)n_vtiles(V) * kc_instance(r) * 4 * kWave * 8 * dtype_bytes(dtype);
+}
+
+extern "C" int dspark_prepack_w2(const void* W2, int r, int V, int dtype, void* W2p,
+                                 size_t W2p_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return DSPARK_EDTYPE;
+  if (!W2 || !W2p) return DSPARK_EINVAL;
+  const size_t need = dspark_prepacked_w2_bytes(r, V, dtype);
+  if (need == 0) return DSPARK_ESIZE;
+  if (W2p_bytes < need) return DSPARK_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int KC = kc_instance(r), n_t = n_vtiles(V);
+  const long long groups = (long long)n_t * KC * 4 * kWave;
+  const int grid = (int)std::min<long long>((groups + 255) / 256, 65535);
+  if (dtype == DSPARK_BF16)
+    hipLaunchKernelGGL(prepack_w2_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(W2), r, V, KC, n_t, static_cast<uint16_t*>(W2p));
+  else
+    hipLaunchKernelGGL(prepack_w2_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const float*>(W2), r, V, KC, n_t, static_cast<float*>(W2p));
+  return launch_status();
+}
+
+#define DSPARK_KC_DISPATCH(BF, fn, ...)                         \
+  switch (kc_instance(r)) {                                     \
+    case 1: return fn<BF, 1>(__VA_ARGS__);                      \
+    case 2: return fn<BF, 2>(__VA_ARGS__);                      \
+    case 4: return fn<BF, 4>(__VA_ARGS__);                      \
+    default: return fn<BF, 8>(__VA_ARGS__);                     \
+  }
+
+static int markov_dispatch(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
+                           uint64_t seed, uint64_t step, const uint32_t* req_ids, int R, int gamma,
+                           int V, int r, int dtype, int32_t* tokens, float* p, float* lse,
+                           float2* part, hipStream_t s) {
+  if (dtype == DSPARK_BF16) {
+    DSPARK_KC_DISPATCH(true, launch_markov, U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V,
+                       r, tokens, p, lse, part, s)
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_markov<false, 1>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, s);
+    case 2: return launch_markov<false, 2>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, s);
+    default: return launch_markov<false, 4>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, s);
+  }
+}
+
+extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2p,
+                                   const int32_t* anchor, uint64_t seed, uint64_t step,
+                                   const uint32_t* req_ids, int R, int gamma, int V, int r,
+                                   int dtype, int32_t* tokens, float* p_draft, float* lse_draft,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(R, gamma, V, r, dtype);
+  if (st) return st;
+  if (!U || !W1 || !W2p || !anchor || !req_ids || !tokens || !p_draft || !lse_draft)
+    return DSPARK_EINVAL;
+  if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
+  return markov_dispatch(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, dtype, tokens,
+                         p_draft, lse_draft, static_cast<float2*>(ws),
+                         static_cast<hipStream_t>(stream));
+}
+
+static int logits_dispatch(const void* U, long long ldU, const void* W1, const void* W2p,
+                           const int32_t* x_prev, int R, int V, int r, int dtype, float* z,
+                           hipStream_t s) {
+  if (dtype == DSPARK_BF16) {
+    DSPARK_KC_DISPATCH(true, launch_logits, U, ldU, W1, W2p, x_prev, R, V, r, z, s)
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_logits<false, 1>(U, ldU, W1, W2p, x_prev, R, V, r, z, s);
+    case 2: return launch_logits<false, 2>(U, ldU, W1, W2p, x_prev, R, V, r, z, s);
+    default: return launch_logits<false, 4>(U, ldU, W1, W2p, x_prev, R, V, r, z, s);
+  }
+}
+
+extern "C" int dspark_markov_logits(const void* U_k, long long ldU, const void* W1,
+                                    const void* W2p, const int32_t* x_prev, int R, int V, int r,
+                                    int dtype, float* z, void* stream) {
+  int st = check_sizes(R, 1, V, r, dtype);
+  if (st) return st;
+  if (!U_k || !W1 || !W2p || !x_prev || !z) return DSPARK_EINVAL;
+  if (ldU < V) return DSPARK_ESIZE;
+  return logits_dispatch(U_k, ldU, W1, W2p, x_prev, R, V, r, dtype, z,
+                         static_cast<hipStream_t>(stream));
+}
+
+static int partials_dispatch(const void* U, long long ldU, const void* W1, const void* W2p,
+                             const int32_t* x_prev, int xstride, int R, int V, int r, int dtype,
+                             float2* part, hipStream_t s) {
+  if (dtype == DSPARK_BF16) {
+    DSPARK_KC_DISPATCH(true, launch_partials_api, U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s)
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_partials_api<false, 1>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s);
+    case 2: return launch_partials_api<false, 2>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s);
+    default: return launch_partials_api<false, 4>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s);
+  }
+}
+
+extern "C" int dspark_markov_partials(const void* U_k, long long ldU, const void* W1,
+                                      const void* W2p, const int32_t* x_prev, int xstride, int R,
+                                      int V, int r, int dtype, void* part, size_t part_bytes,
+                                      void* stream) {
+  int st = check_sizes(R, 1, V, r, dtype);
+  if (st) return st;
+  if (!U_k || !W1 || !W2p || !x_prev || !part) return DSPARK_EINVAL;
+  if (ldU < V || xstride < 1) return DSPARK_ESIZE;
+  if (part_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
+  return partials_dispatch(U_k, ldU, W1, W2p, x_prev, xstride, R, V, r, dtype,
+                           static_cast<float2*>(part), static_cast<hipStream_t>(stream));
+}
+
+template <bool BF16, int KC>
+static int launch_select_api(const void* U, long long ldU, const void* W1, const void* W2p,
+                             const int32_t* x_prev, int xstride, const float2* part, uint64_t seed,
+                             uint64_t step, const uint32_t* req_ids, int k, int R, int V, int r,
+                             int32_t* tok, float* p, float* lse, int ostride, hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
+                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(ceil_div(R, kTileN)), dim3(256), 0, s,
+                     static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
+                     static_cast<const T*>(W2p), x_prev, xstride, R, V, r, n_vtiles(V), part, R,
+                     seed, step, req_ids, k, tok, p, lse, ostride);
+  return launch_status();
+}
+
+extern "C" int dspark_markov_select(const void* U_k, long long ldU, const void* W1,
+                                    const void* W2p, const int32_t* x_prev, int xstride,
+                                    const void* part, uint64_t seed, uint64_t step,
+                                    const uint32_t* req_ids, int k, int R, int V, int r, int dtype,
+                                    int32_t* tok_out, float* p_out, float* lse_out, int ostride,
+                                    void* stream) {
+  int st = check_sizes(R, 1, V, r, dtype);
+  if (st) return st;
+  if (!U_k || !W1 || !W2p || !x_prev || !part || !req_ids || !tok_out || !p_out || !lse_out)
+    return DSPARK_EINVAL;
+  if (ldU < V || xstride < 1 || ostride < 1 || k < 1 || k > kMaxGamma + 1) return DSPARK_ESIZE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float2* pt = static_cast<const float2*>(part);
+#define DSPARK_SEL_ARGS U_k, ldU, W1, W2p, x_prev, xstride, pt, seed, step, req_ids, k, R, V, r, \
+                        tok_out, p_out, lse_out, ostride, s
+  if (dtype == DSPARK_BF16) {
+    switch (kc_instance(r)) {
+      case 1: return launch_select_api<true, 1>(DSPARK_SEL_ARGS);
+      case 2: return launch_select_api<true, 2>(DSPARK_SEL_ARGS);
+      case 4: return launch_select_api<true, 4>(DSPARK_SEL_ARGS);
+      default: return launch_select_api<true, 8>(DSPARK_SEL_ARGS);
+    }
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_select_api<false, 1>(DSPARK_SEL_ARGS);
+    case 2: return launch_select_api<false, 2>(DSPARK_SEL_ARGS);
+    default: return launch_select_api<false, 4>(DSPARK_SEL_ARGS);
+  }
+#undef DSPARK_SEL_ARGS
+}

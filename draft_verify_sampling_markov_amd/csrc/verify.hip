@@ -1,0 +1,576 @@
+// Lossless rejection-sampling verification on gfx950.
+//
+// DSpark digest ("DSpark: Confidence-Scheduled Speculative Decoding with
+// Semi-Autoregressive Generation", zhao9797.github.io): the target checks the
+// drafted block in one forward and rejection sampling keeps the longest prefix
+// that conforms; every draft probability is an exact softmax ("Architecture
+// (drafter)"), which is what makes the check lossless. SGLang DSpark blog,
+// "Verify modes": static verifies the whole block, compact the scheduled
+// window, cap-accept the whole block while committing only the window (same
+// commit as compact, plus the ceiling).
+//
+// Four launches, no host read-back:
+//   row_partials      every packed target row, split in vocabulary chunks:
+//                     (max, sum of exp) partials -- the bandwidth-bound pass
+//   decide            one wave per request: merge a row's partials into its
+//                     log-sum-exp, p_t(x_k), the accept test u < p_t / p_d per
+//                     slot, the accepted length, and the correction job
+//                     (residual at slot A+1, or bonus at slot L+1)
+//   residual_partials per 64-entry vocabulary tile: recompute the draft logits
+//                     of each request's job slot on the matrix cores, form
+//                     q = max(0, p_t - p_d) (or p_t for a bonus), and emit
+//                     per-tile sums of q and of p_t
+//   residual_select   per request: find the tile where the cumulative mass
+//                     crosses u * sum, recompute that tile with the same code
+//                     and finish the inverse-CDF search; write the token
+#include "dspark_device.hpp"
+#include "dspark_host.hpp"
+
+#include <algorithm>
+
+namespace dspark {
+
+constexpr int kRowChunk = 8192;  // vocabulary entries per row-partial workgroup
+constexpr int kRowThreads = 256;
+
+inline int n_row_chunks(int V) { return ceil_div(V, kRowChunk); }
+
+// correction job of one request (structure of arrays in the workspace)
+struct Jobs {
+  int* kind;    // 0 residual, 1 bonus
+  int* slot;    // 1-based slot of the correction token
+  int* trow;    // packed target row of that slot
+  int* xprev;   // token before the slot (anchor for slot 1)
+  float* u;     // uniform of the draw
+  float* lse_t; // target log-sum-exp of trow
+  float* lse_d; // draft log-sum-exp of the slot (residual only)
+};
+
+// ---------------------------------------------------------------------------
+// row partials
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void row_partials_kernel(
+    const typename Elem<BF16>::T* __restrict__ target, int V, bool vec, int n_chunks,
+    const int* __restrict__ cu_seqlens, int R, int rows_ws, float2* __restrict__ part) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int VEC = Elem<BF16>::kVec;
+  constexpr int PER = kRowChunk / kRowThreads;  // 32 entries per thread
+  __shared__ float red[kRowThreads / kWave];
+  const int row = blockIdx.y;
+  if (row >= min(cu_seqlens[R], rows_ws)) return;  // block-uniform
+  const int c = blockIdx.x;
+  const int v_begin = c * kRowChunk;
+  const int v_end = min(V, v_begin + kRowChunk);
+  const T* z = target + (size_t)row * V;
+  const int tid = threadIdx.x;
+  float vals[PER];
+  if (vec) {
+#pragma unroll
+    for (int it = 0; it < PER / VEC; ++it) {
+      const int v = v_begin + (it * kRowThreads + tid) * VEC;
+      if (v + VEC <= v_end) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + v));
+        if constexpr (BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vals[it * VEC + 2 * i] = __uint_as_float(q[i] << 16);
+            vals[it * VEC + 2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vals[it * VEC + i] = __uint_as_float(q[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) vals[it * VEC + i] = (v + i < v_end) ? to_f32(z[v + i]) : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int v = v_begin + it * kRowThreads + tid;
+      vals[it] = v < v_end ? to_f32(z[v]) : -INFINITY;
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) m = fmaxf(m, vals[i]);
+  m = wave_max(m);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float mb = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / kWave; ++w) mb = fmaxf(mb, red[w]);
+  __syncthreads();
+  float s = 0.0f;
+  if (mb != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s += __expf(vals[i] - mb);
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float sb = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / kWave; ++w) sb += red[w];
+    part[(size_t)row * n_chunks + c] = make_float2(mb, sb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decide
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void decide_kernel(
+    const typename Elem<BF16>::T* __restrict__ target, int V, int n_chunks,
+    const float2* __restrict__ part, const int* __restrict__ cu_seqlens,
+    const int* __restrict__ anchor, const int* __restrict__ tokens,
+    const float* __restrict__ p_draft, const float* __restrict__ lse_draft,
+    const int* __restrict__ win_len, int mode, uint64_t seed, uint64_t step,
+    const uint32_t* __restrict__ req_ids, int R, int gamma, int rows_ws, Jobs jobs,
+    int* __restrict__ accept_len,
+    int* __restrict__ out_tokens, int* __restrict__ n_out, int* __restrict__ ceiling) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int req = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (req >= R) return;  // wave-uniform, no barriers below
+  // rows of this request, clamped into the row workspace (a well-formed
+  // cu_seqlens never needs the clamp)
+  const int c0 = min(max(cu_seqlens[req], 0), rows_ws - 1);
+  const int c1 = min(max(cu_seqlens[req + 1], c0 + 1), rows_ws);
+  const int Lv = min(c1 - c0 - 1, gamma);
+  float lse = 0.0f;
+  bool acc = false;
+  if (lane <= Lv) {
+    const int row = c0 + lane;
+    float m = -INFINITY;
+    for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, part[(size_t)row * n_chunks + c].x);
+    float S = 0.0f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float2 pv = part[(size_t)row * n_chunks + c];
+      S += pv.y * __expf(pv.x - m);
+    }
+    lse = m + __logf(S);
+    if (lane < Lv) {
+      const int x = clamp_token(tokens[(size_t)req * gamma + lane], V);
+      const float zt = to_f32(target[(size_t)row * V + x]);
+      const float pt = __expf(zt - lse);
+      const float ratio = pt / p_draft[(size_t)req * gamma + lane];
+      const float u1 = slot_uniform(seed, step, req_ids[req], lane + 1, kPurposeAccept);
+      acc = u1 < ratio;
+    }
+  }
+  const unsigned long long mask = __ballot(acc);
+  const int A_full = min(__ffsll((long long)~mask) - 1, Lv);
+  int Lc = Lv;
+  if (mode == DSPARK_VERIFY_CAP_ACCEPT) Lc = min(min(max(win_len[req], 0), gamma), Lv);
+  const int A = min(A_full, Lc);
+  const bool residual = A < Lc;
+  const int slot = residual ? A + 1 : Lc + 1;
+  const int rel = slot - 1;  // packed row offset of the slot's target row
+  const float lse_t = __shfl(lse, rel, kWave);
+  if (lane == 0) {
+    jobs.kind[req] = residual ? 0 : 1;
+    jobs.slot[req] = slot;
+    jobs.trow[req] = c0 + rel;
+    jobs.xprev[req] = A == 0 ? anchor[req] : tokens[(size_t)req * gamma + A - 1];
+    jobs.u[req] = slot_uniform(seed, step, req_ids[req], slot, residual ? kPurposeResidual : kPurposeBonus);
+    jobs.lse_t[req] = lse_t;
+    jobs.lse_d[req] = residual ? lse_draft[(size_t)req * gamma + A] : 0.0f;
+    accept_len[req] = A;
+    n_out[req] = A + 1;
+    if (ceiling) ceiling[req] = A_full;
+  }
+  if (lane <= gamma && lane != A)
+    out_tokens[(size_t)req * (gamma + 1) + lane] = lane < A ? tokens[(size_t)req * gamma + lane] : -1;
+}
+
+// ---------------------------------------------------------------------------
+// residual / bonus weights
+// ---------------------------------------------------------------------------
+
+// q for one entry: max(0, p_t - p_d) for a residual, p_t for a bonus.
+__device__ __forceinline__ float corr_weight(float zt, float zd, float lse_t, float lse_d,
+                                             bool residual) {
+  const float pt = __expf(zt - lse_t);
+  if (!residual) return pt;
+  const float pd = __expf(zd - lse_d);
+  return fmaxf(pt - pd, 0.0f);
+}
+
+// q and p_t for the 16 entries a lane holds (invalid entries: 0).
+template <bool BF16>
+__device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float zt16[16],
+                                                 const float u16[16], int nvalid, float lse_t,
+                                                 float lse_d, bool residual, float q[16],
+                                                 float pt[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = 4 * j + i;
+      const bool ok = idx < nvalid;
+      const float zd = acc[j][i] + u16[idx];
+      q[idx] = ok ? corr_weight(zt16[idx], zd, lse_t, lse_d, residual) : 0.0f;
+      pt[idx] = ok ? __expf(zt16[idx] - lse_t) : 0.0f;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_corr_inputs(const typename Elem<BF16>::T* __restrict__ target,
+                                                 const typename Elem<BF16>::T* __restrict__ U,
+                                                 int V, int gamma, bool vec, int n, int v0,
+                                                 int nvalid, int trow, int dslot, bool residual,
+                                                 float zt16[16], float u16[16]) {
+  load16<BF16>(target + (size_t)trow * V + v0, nvalid, vec, zt16);
+  if (residual) {
+    load16<BF16>(U + ((size_t)n * gamma + dslot) * V + v0, nvalid, vec, u16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// residual partials
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(512) void residual_partials_kernel(
+    const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
+    bool vec, const typename Elem<BF16>::T* __restrict__ W1,
+    const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int g0, int R, int gamma, int V,
+    int r, int n_t, float2* __restrict__ rpart, int ldp) {
+  typedef typename Elem<BF16>::T T;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* w1s = reinterpret_cast<T*>(smem);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int g = lane >> 4, nl = lane & 15;
+  constexpr int kpad = KC * kChunkK;
+  constexpr int ldw = kpad + kLdsPad;
+  const int rows = (R + 15) & ~15;
+  stage_rows<BF16>(W1, jobs.xprev + g0, 1, R, rows, r, V, kpad, ldw, w1s);
+  __syncthreads();
+  for (int t = blockIdx.x * nwaves + wave; t < n_t; t += gridDim.x * nwaves) {
+    ATile<BF16, KC> at;
+    load_a_tile<BF16, KC>(W2p, t, lane, at);
+    const int v0 = t * kTileV + 16 * g;
+    const int nvalid = min(16, V - v0);
+    for (int nb = 0; nb < rows; nb += kTileN) {
+      const int nloc = nb + nl;
+      const bool active = nloc < R;
+      const int n = g0 + nloc;
+      bool residual = false;
+      int trow = 0, dslot = 0;
+      float lse_t = 0.f, lse_d = 0.f;
+      float zt16[16], u16[16];
+      if (active) {
+        residual = jobs.kind[n] == 0;
+        trow = jobs.trow[n];
+        dslot = jobs.slot[n] - 1;
+        lse_t = jobs.lse_t[n];
+        lse_d = jobs.lse_d[n];
+      }
+      if (active && nvalid > 0) {
+        load_corr_inputs<BF16>(target, U, V, gamma, vec, n, v0, nvalid, trow, dslot, residual, zt16, u16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zt16[i] = u16[i] = 0.0f;
+      }
+      f32x4 acc[4];
+      tile_mma<BF16, KC>(at, w1s + nb * ldw, ldw, lane, acc);
+      float q[16], pt[16];
+      corr_tile_values<BF16>(acc, zt16, u16, (active ? nvalid : 0), lse_t, lse_d, residual, q, pt);
+      float sq = 0.0f, sp = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sq += q[i];
+        sp += pt[i];
+      }
+      sq += __shfl_xor(sq, 16, kWave);
+      sp += __shfl_xor(sp, 16, kWave);
+      sq += __shfl_xor(sq, 32, kWave);
+      sp += __shfl_xor(sp, 32, kWave);
+      if (g == 0 && active) rpart[(size_t)t * ldp + n] = make_float2(sq, sp);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// residual select
+// ---------------------------------------------------------------------------
+
+struct RSelShared {
+  float sq[16][16];  // [part][request]
+  float sp[16][16];
+  float off[17][16];
+  int lastq[16][16];
+  int lastp[16][16];
+  float S[16], T[16], pb[16];
+  int tstar[16], usept[16];
+};
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(256) void residual_select_kernel(
+    const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
+    bool vec, const typename Elem<BF16>::T* __restrict__ W1,
+    const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int R, int gamma, int V, int r,
+    int n_t, const float2* __restrict__ rpart, int ldp, int* __restrict__ out_tokens) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int kpad = KC * kChunkK;
+  constexpr int ldw = kpad + kLdsPad;
+  __shared__ __align__(16) T w1s[16 * ldw];
+  __shared__ RSelShared sh;
+  const int tid = threadIdx.x;
+  const int nb0 = blockIdx.x * kTileN;
+  const int count = min(kTileN, R - nb0);
+  stage_rows<BF16>(W1, jobs.xprev + nb0, 1, count, 16, r, V, kpad, ldw, w1s);
+
+  const int q = tid & 15, p = tid >> 4;
+  const int n = nb0 + q;
+  const bool active = q < count;
+  const int c = (n_t + 15) / 16;
+  const int t0 = min(n_t, p * c), t1 = min(n_t, t0 + c);
+  float lq = 0.0f, lp = 0.0f;
+  int lastq = -1, lastp = -1;
+  if (active)
+    for (int t = t0; t < t1; ++t) {
+      const float2 pv = rpart[(size_t)t * ldp + n];
+      if (pv.x > 0.0f) lastq = t;
+      if (pv.y > 0.0f) lastp = t;
+      lq += pv.x;
+      lp += pv.y;
+    }
+  sh.sq[p][q] = lq;
+  sh.sp[p][q] = lp;
+  sh.lastq[p][q] = lastq;
+  sh.lastp[p][q] = lastp;
+  __syncthreads();
+  if (p == 0) {
+    float tq = 0.0f;
+    for (int pp = 0; pp < 16; ++pp) tq += sh.sq[pp][q];
+    const int use_pt = !(tq > 0.0f);  // no residual mass left: draw from p_t
+    float off = 0.0f;
+    int lst = -1;
+    for (int pp = 0; pp < 16; ++pp) {
+      sh.off[pp][q] = off;
+      off += use_pt ? sh.sp[pp][q] : sh.sq[pp][q];
+      lst = max(lst, use_pt ? sh.lastp[pp][q] : sh.lastq[pp][q]);
+    }
+    sh.off[16][q] = off;
+    sh.S[q] = off;
+    sh.usept[q] = use_pt;
+    sh.T[q] = active ? jobs.u[n] * off : 0.0f;
+    sh.tstar[q] = lst;
+    sh.pb[q] = -INFINITY;  // fallback never crosses: last positive entry
+  }
+  __syncthreads();
+  if (active) {
+    const float Tq = sh.T[q], o0 = sh.off[p][q], o1 = sh.off[p + 1][q];
+    const int use_pt = sh.usept[q];
+    if (Tq >= o0 && Tq < o1) {
+      float lc = 0.0f;
+      for (int t = t0; t < t1; ++t) {
+        const float2 pv = rpart[(size_t)t * ldp + n];
+        const float lcn = lc + (use_pt ? pv.y : pv.x);
+        if (o0 + lcn > Tq) {
+          sh.tstar[q] = t;
+          sh.pb[q] = o0 + lc;
+          break;
+        }
+        lc = lcn;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int g = lane >> 4, nl = lane & 15;
+  for (int it = 0; it < 4; ++it) {
+    const int qq = wave + 4 * it;
+    if (qq >= count) continue;  // wave-uniform
+    const int nn = nb0 + qq;
+    const int t = min(max(sh.tstar[qq], 0), n_t - 1);
+    ATile<BF16, KC> at;
+    load_a_tile<BF16, KC>(W2p, t, lane, at);
+    f32x4 acc[4];
+    tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+    const int v0 = t * kTileV + 16 * g;
+    const int nvalid = min(16, V - v0);
+    const bool residual = jobs.kind[nn] == 0;
+    const int trow = jobs.trow[nn], dslot = jobs.slot[nn] - 1;
+    const float lse_t = jobs.lse_t[nn], lse_d = jobs.lse_d[nn];
+    float zt16[16], u16[16];
+    const bool mine = nl == qq;
+    if (mine && nvalid > 0) {
+      load_corr_inputs<BF16>(target, U, V, gamma, vec, nn, v0, nvalid, trow, dslot, residual, zt16, u16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zt16[i] = u16[i] = 0.0f;
+    }
+    float qv[16], pv[16];
+    corr_tile_values<BF16>(acc, zt16, u16, (mine ? nvalid : 0), lse_t, lse_d, residual, qv, pv);
+    const int use_pt = sh.usept[qq];
+    const int src = qq + 16 * (lane >> 4);
+    float wi = 0.0f;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const float val = __shfl(use_pt ? pv[idx] : qv[idx], src, kWave);
+      if ((lane & 15) == idx) wi = val;
+    }
+    const int v = t * kTileV + lane;
+    const bool valid = v < V;
+    if (!valid) wi = 0.0f;
+    const float sc = wave_inclusive_scan(wi, lane);
+    const bool cross = valid && (sh.pb[qq] + sc > sh.T[qq]);
+    const unsigned long long cm = __ballot(cross);
+    int sel;
+    if (cm) {
+      sel = __ffsll((long long)cm) - 1;
+    } else {
+      const unsigned long long pm = __ballot(wi > 0.0f);
+      sel = pm ? 63 - __clzll((long long)pm) : 0;
+    }
+    if (lane == 0) out_tokens[(size_t)nn * (gamma + 1) + jobs.slot[nn] - 1] = t * kTileV + sel;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+struct VerifyWs {
+  float2* rowpart;
+  float2* rpart;
+  Jobs jobs;
+};
+
+// Row partials cover R * (gamma + 1) packed rows: no well-formed pack has more.
+static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
+  const int rows_ws = R * (gamma + 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
+  const size_t o_rp = take((size_t)n_vtiles(V) * R * sizeof(float2));
+  size_t o_j[7];
+  for (int i = 0; i < 7; ++i) o_j[i] = take((size_t)R * 4);
+  if (w && base) {
+    char* b = static_cast<char*>(base);
+    w->rowpart = reinterpret_cast<float2*>(b + o_row);
+    w->rpart = reinterpret_cast<float2*>(b + o_rp);
+    w->jobs.kind = reinterpret_cast<int*>(b + o_j[0]);
+    w->jobs.slot = reinterpret_cast<int*>(b + o_j[1]);
+    w->jobs.trow = reinterpret_cast<int*>(b + o_j[2]);
+    w->jobs.xprev = reinterpret_cast<int*>(b + o_j[3]);
+    w->jobs.u = reinterpret_cast<float*>(b + o_j[4]);
+    w->jobs.lse_t = reinterpret_cast<float*>(b + o_j[5]);
+    w->jobs.lse_d = reinterpret_cast<float*>(b + o_j[6]);
+  }
+  return off;
+}
+
+size_t verify_ws_bytes(int R, int gamma, int V) { return carve(nullptr, nullptr, R, gamma, V); }
+
+template <bool BF16, int KC>
+static int launch_verify(const void* target, int M_cap, const int32_t* cu, const int32_t* anchor,
+                         const int32_t* tokens, const float* p_draft, const float* lse_draft,
+                         const void* U, const void* W1, const void* W2p, const int32_t* win_len,
+                         int mode, uint64_t seed, uint64_t step, const uint32_t* req_ids, int R,
+                         int gamma, int V, int r, int32_t* accept_len, int32_t* out_tokens,
+                         int32_t* n_out, int32_t* ceiling, const VerifyWs& ws, hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int kpad = KC * kChunkK;
+  constexpr int ldw = kpad + kLdsPad;
+  const T* tg = static_cast<const T*>(target);
+  const T* Ub = static_cast<const T*>(U);
+  const T* W1b = static_cast<const T*>(W1);
+  const T* W2b = static_cast<const T*>(W2p);
+  const int nch = n_row_chunks(V), n_t = n_vtiles(V);
+  const bool vec = (V % Elem<BF16>::kVec) == 0 && (reinterpret_cast<uintptr_t>(target) % 16) == 0 &&
+                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  const int rows_ws = R * (gamma + 1);
+  (void)M_cap;
+  hipLaunchKernelGGL((row_partials_kernel<BF16>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s, tg, V,
+                     vec, nch, cu, R, rows_ws, ws.rowpart);
+  int st = launch_status();
+  if (st) return st;
+  hipLaunchKernelGGL((decide_kernel<BF16>), dim3(ceil_div(R, 4)), dim3(256), 0, s, tg, V, nch,
+                     ws.rowpart, cu, anchor, tokens, p_draft, lse_draft, win_len, mode, seed, step,
+                     req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
+  st = launch_status();
+  if (st) return st;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t max_lds = (size_t)((kReqGroup + 15) & ~15) * ldw * sizeof(T);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&residual_partials_kernel<BF16, KC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds) != hipSuccess)
+      return DSPARK_EHIP;
+    attr_set = true;
+  }
+  const int ncu = device_cu_count();
+  for (int g0 = 0; g0 < R; g0 += kReqGroup) {
+    const int Rg = std::min(kReqGroup, R - g0);
+    const size_t lds = (size_t)((Rg + 15) & ~15) * ldw * sizeof(T);
+    const int per_cu = lds > 80 * 1024 ? 1 : 2;
+    const int grid = std::max(1, std::min(ceil_div(n_t, 8), ncu * per_cu));
+    hipLaunchKernelGGL((residual_partials_kernel<BF16, KC>), dim3(grid), dim3(512), lds, s, tg, Ub,
+                       vec, W1b, W2b, ws.jobs, g0, Rg, gamma, V, r, n_t, ws.rpart, R);
+    st = launch_status();
+    if (st) return st;
+  }
+  hipLaunchKernelGGL((residual_select_kernel<BF16, KC>), dim3(ceil_div(R, kTileN)), dim3(256), 0, s,
+                     tg, Ub, vec, W1b, W2b, ws.jobs, R, gamma, V, r, n_t, ws.rpart, R, out_tokens);
+  return launch_status();
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" int dspark_verify(const void* target_packed, int M_cap, const int32_t* cu_seqlens,
+                             const int32_t* anchor, const int32_t* tokens, const float* p_draft,
+                             const float* lse_draft, const void* U, const void* W1,
+                             const void* W2p, const int32_t* win_len, int mode, uint64_t seed,
+                             uint64_t step, const uint32_t* req_ids, int R, int gamma, int V,
+                             int r, int dtype, int32_t* accept_len, int32_t* out_tokens,
+                             int32_t* n_out, int32_t* ceiling_len, void* ws, size_t ws_bytes,
+                             void* stream) {
+  int st = check_sizes(R, gamma, V, r, dtype);
+  if (st) return st;
+  if (mode < DSPARK_VERIFY_STATIC || mode > DSPARK_VERIFY_CAP_ACCEPT) return DSPARK_EINVAL;
+  if (!target_packed || !cu_seqlens || !anchor || !tokens || !p_draft || !lse_draft || !U || !W1 ||
+      !W2p || !req_ids || !accept_len || !out_tokens || !n_out)
+    return DSPARK_EINVAL;
+  if (mode == DSPARK_VERIFY_CAP_ACCEPT && !win_len) return DSPARK_EINVAL;
+  if (M_cap < R * (gamma + 1)) return DSPARK_ESIZE;
+  if (!ws || ws_bytes < verify_ws_bytes(R, gamma, V)) return DSPARK_EWORKSPACE;
+  VerifyWs w;
+  carve(&w, ws, R, gamma, V);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define DSPARK_VERIFY_ARGS                                                                        \
+  target_packed, M_cap, cu_seqlens, anchor, tokens, p_draft, lse_draft, U, W1, W2p, win_len, mode, \
+      seed, step, req_ids, R, gamma, V, r, accept_len, out_tokens, n_out, ceiling_len, w, s
+  if (dtype == DSPARK_BF16) {
+    switch (kc_instance(r)) {
+      case 1: return launch_verify<true, 1>(DSPARK_VERIFY_ARGS);
+      case 2: return launch_verify<true, 2>(DSPARK_VERIFY_ARGS);
+      case 4: return launch_verify<true, 4>(DSPARK_VERIFY_ARGS);
+      default: return launch_verify<true, 8>(DSPARK_VERIFY_ARGS);
+    }
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_verify<false, 1>(DSPARK_VERIFY_ARGS);
+    case 2: return launch_verify<false, 2>(DSPARK_VERIFY_ARGS);
+    default: return launch_verify<false, 4>(DSPARK_VERIFY_ARGS);
+  }
+#undef DSPARK_VERIFY_ARGS
+}

@@ -1,0 +1,279 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) DSpark draft-head-and-verify chain.
+ *
+ * One decode step of DSpark's confidence-scheduled speculative decoding, as
+ * five calls that run on the caller's HIP stream:
+ *
+ *   dspark_markov_draft   draft a gamma-token block with the Markov head
+ *   dspark_confidence     confidence c_k and prefix survival a_{r,j}
+ *   dspark_schedule_topb  global top-B prefix selection (verify windows)
+ *   dspark_pack_ragged    cu_seqlens packing rounded up to a capture tier
+ *   dspark_verify         lossless rejection-sampling verification
+ *
+ * plus host/device utilities (W2 pre-packing, cost-table preparation,
+ * workspace sizing, status strings) and one diagnostic call.
+ *
+ * Sources, cited by page title and section:
+ *   [digest]  "DSpark: Confidence-Scheduled Speculative Decoding with
+ *             Semi-Autoregressive Generation", technical digest
+ *             (zhao9797.github.io).
+ *   [sglang]  "SGLang integrates DSpark" blog (aihot.vn; Chinese copy at
+ *             aihot.virxact.com).
+ *   [vllm]    "vLLM adaptive verification with DSpark" (agentlenshq.com).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host]. The caller allocates
+ *     and owns every buffer; the library never allocates, frees or
+ *     synchronises inside a call, and keeps no state besides a per-device
+ *     cache of the compute-unit count.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Each
+ *     call enqueues its kernels on it and returns at once; outputs are valid
+ *     once the stream has reached that point.
+ *   - Arrays are row-major and contiguous. Token ids are int32 in [0, V).
+ *   - dtype selects the storage type of the large float inputs (U, W1, W2,
+ *     h, target logits): DSPARK_F32 (float32) or DSPARK_BF16 (bfloat16 bit
+ *     patterns, 2 bytes). All arithmetic is float32 (bf16 products are exact
+ *     in fp32; sums accumulate in fp32).
+ *   - Arguments are checked on the host. A failed check returns a negative
+ *     dspark_status and launches nothing. Device-side preconditions (token ids
+ *     in range, a monotone cost table) are not checked; violating them gives
+ *     unspecified values but no out-of-bounds access for token ids (they are
+ *     clamped into [0, V) before any indexing).
+ *   - Limits: 1 <= gamma <= 16, R * (gamma + 1) <= 4096, 1 <= r <= 256 for
+ *     bf16 and 1 <= r <= 128 for f32, V >= 1.
+ *   - Random numbers: Philox4x64-10 (Salmon et al., SC'11) keyed by
+ *     (seed, 0) with counter (k, req_ids[r], step, 0) for slot k of request
+ *     r; its four 64-bit words drive, in order, the draft sample, the accept
+ *     test, the residual resample and the bonus sample at slot k. A word x
+ *     becomes the uniform (x >> 40) * 2^-24. Outputs are a pure function of
+ *     the inputs and (seed, step, req_ids).
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = -1,     /* null pointer or bad argument                    */
+  DSPARK_EDTYPE = -2,     /* unknown dtype                                   */
+  DSPARK_ETIER = -3,      /* bad capture-tier list (empty, unsorted, <= 0)   */
+  DSPARK_ESIZE = -4,      /* a size is outside the documented limits         */
+  DSPARK_EWORKSPACE = -5, /* workspace missing or smaller than required      */
+  DSPARK_EHIP = -6        /* a HIP runtime call or kernel launch failed      */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* [sglang] "Verify modes". */
+typedef enum {
+  DSPARK_VERIFY_STATIC = 0,    /* verify and commit the whole block          */
+  DSPARK_VERIFY_COMPACT = 1,   /* verify and commit the packed window        */
+  DSPARK_VERIFY_CAP_ACCEPT = 2 /* verify the whole block, commit the window  */
+} dspark_verify_mode;
+
+/* [digest] "Verification scheduling" (greedy early stop) and "Infra"
+ * (unconstrained search over a budget array); [vllm] "DSpark
+ * confidence-scheduling mechanism" (budget given from the host). */
+typedef enum {
+  DSPARK_SCHED_ARGMAX = 0, /* smallest K maximising Theta over the budget array */
+  DSPARK_SCHED_GREEDY = 1, /* admit while Theta strictly increases               */
+  DSPARK_SCHED_FIXED = 2   /* K given by the caller                              */
+} dspark_sched_mode;
+
+/* Selector for dspark_workspace_bytes. */
+typedef enum {
+  DSPARK_CALL_MARKOV_DRAFT = 0,
+  DSPARK_CALL_VERIFY = 1
+} dspark_call;
+
+/* ------------------------------------------------------------------------ */
+/* Utilities                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Human-readable text for a dspark_status value (static storage). */
+const char* dspark_status_string(int status);
+
+/* Bytes of workspace `call` needs for these sizes (0 for calls that need
+ * none, and for invalid sizes). The verify workspace does not depend on M_cap:
+ * a well-formed pack never has more than R * (gamma + 1) rows. */
+size_t dspark_workspace_bytes(int call, int R, int gamma, int V, int r);
+
+/* Bytes of the pre-packed W2 buffer for rank r, vocabulary V and dtype. */
+size_t dspark_prepacked_w2_bytes(int r, int V, int dtype);
+
+/* Re-lay the Markov projection W2 [r, V] ([digest] "Architecture (drafter)":
+ * B = W1 W2, W2 in R^{r x V}) into the matrix-core operand order used by the
+ * draft and verify kernels. Weights are static across steps, so this runs
+ * once per model. W2 and W2p are device buffers of the given dtype; W2p must
+ * hold dspark_prepacked_w2_bytes(r, V, dtype) bytes. Zero padding fills the
+ * rank up to a multiple of 32 and the vocabulary up to a multiple of 64. */
+int dspark_prepack_w2(const void* W2, int r, int V, int dtype, void* W2p, size_t W2p_bytes,
+                      void* stream);
+
+/* Host cost-table preparation ([sglang] "Cost-table profiling": additive step
+ * time with M = bs + K verify tokens; [vllm] "Technical implementation & CUDA
+ * graphs": profiled curves are forced monotone and graph padding makes them
+ * staircases).
+ *   raw_step_time_s [host, M_max+1]  profiled step time T(M), seconds
+ *   tiers           [host, n_tiers]  ascending captured pack totals
+ *   staircase       nonzero: T(M) is read at the smallest tier >= M (capped
+ *                   at M_max) and M above the top tier is infeasible (0)
+ *   sps_milli       [host, M_max+1]  out: floor(1000 / T + 0.5), i.e. steps
+ *                   per second x 1000, after T has been made monotone by a
+ *                   running maximum over M; 0 marks an infeasible M.
+ * Returns DSPARK_ETIER for an empty/unsorted/non-positive tier list. */
+int dspark_cost_table_prepare(const double* raw_step_time_s, int M_max, const int32_t* tiers,
+                              int n_tiers, int staircase, uint32_t* sps_milli);
+
+/* ------------------------------------------------------------------------ */
+/* Hot calls                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Draft one block with the Markov sequential head ([digest] "Architecture
+ * (drafter)": p_k(v | x_0, x_<k) = softmax(U_k(v) + W1[x_{k-1}] W2 (v)),
+ * sampled left to right; the anchor x_0 is the last committed token).
+ *   U        [R, gamma, V]  base logits of slots 1..gamma (dtype)
+ *   W1       [V, r]         Markov lookup factor (dtype)
+ *   W2p      pre-packed W2  (dspark_prepack_w2)
+ *   anchor   [R] int32      x_0
+ *   req_ids  [R] uint32     Philox request ids
+ *   tokens   [R, gamma] int32  out: x_1..x_gamma
+ *   p_draft  [R, gamma] f32    out: draft probability of the sampled token
+ *   lse_draft[R, gamma] f32    out: log-sum-exp of the slot's draft logits
+ *   ws       workspace of dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, ...)
+ * Sampling: inverse CDF over ascending ids with a strict comparison,
+ * x = min{v : C_v > u S}, on the draft uniform of slot k. */
+int dspark_markov_draft(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
+                        uint64_t seed, uint64_t step, const uint32_t* req_ids, int R, int gamma,
+                        int V, int r, int dtype, int32_t* tokens, float* p_draft,
+                        float* lse_draft, void* ws, size_t ws_bytes, void* stream);
+
+/* Confidence head and prefix survival ([digest] "Verification scheduling
+ * (system side)"): c_k = sigmoid((w . [h_k ; W1[x_{k-1}]] + b) * inv_temp_k),
+ * a_{r,k} = a_{r,k-1} * c_k in float32, a_{r,0} = 1.
+ *   h        [R, gamma, d]  hidden states (dtype)
+ *   W1       [V, r]         (dtype)
+ *   anchor   [R], tokens [R, gamma]
+ *   w        [d + r] f32    head weight, hidden part first
+ *   b        head bias
+ *   inv_temp [gamma] f32 or NULL (NULL: 1; a per-position temperature hook)
+ *   conf, surv [R, gamma] f32  out */
+int dspark_confidence(const void* h, const void* W1, const int32_t* anchor, const int32_t* tokens,
+                      const float* w, float b, const float* inv_temp, int R, int gamma, int d,
+                      int V, int r, int dtype, float* conf, float* surv, void* stream);
+
+/* Global top-B prefix scheduler ([vllm] "DSpark confidence-scheduling
+ * mechanism"; [digest] "Verification scheduling" and "Infra"). Integer fixed
+ * point, so any evaluation order gives the same result:
+ *   a_q = floor(clamp(a, 0, 1) * 2^20) (NaN -> 0), made non-increasing along
+ *   each request by a running minimum; keys ordered by (a_q desc, request asc,
+ *   slot asc); tau_K = R * 2^20 + sum of the K largest a_q of the budget array;
+ *   Theta_K = tau_K * sps_milli[R + K] (uint64); K in [0, min(B_cap, R*gamma,
+ *   M_max - R)].
+ *   ARGMAX: smallest K maximising Theta_K.  GREEDY: stop at the first K with
+ *   Theta_{K+1} <= Theta_K.  FIXED: K = clamp(K_fixed).
+ * The K selected slots are always the K best keys of the CURRENT survivals;
+ * win_len[r] counts request r's selected slots (a prefix).
+ *   surv        [R, gamma] f32
+ *   surv_budget [R, gamma] f32 or NULL (NULL: surv), e.g. stale confidences
+ *   sps_milli   [M_max + 1] u32 (device copy of dspark_cost_table_prepare)
+ *   win_len     [R] int32 out;  K_out [1] int32 out
+ * Runs as one workgroup; nothing is read back to the host. */
+int dspark_schedule_topb(const float* surv, const float* surv_budget, const uint32_t* sps_milli,
+                         int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
+                         int32_t* win_len, int32_t* K_out, void* stream);
+
+/* Ragged pack ([sglang] "Ragged verify under full CUDA graphs": windows packed
+ * front to back into a cu_seqlens buffer whose total is rounded up to the
+ * nearest captured tier; [vllm] "Configuration & reproduction": the largest
+ * verify batch is (gamma + 1) * R).
+ *   win_len [R] or NULL (NULL: gamma, the full block); values clamped to
+ *           [0, gamma]
+ *   tiers   [host, n_tiers <= 32] ascending
+ *   M_cap   rows of the packed buffers, >= R * (gamma + 1)
+ *   cu_seqlens [R+1]: cu[0] = 0, cu[r+1] = cu[r] + 1 + L_r
+ *   packed_tokens/req/slot [M_cap]: row cu[r] + j holds x_j (j = 0: anchor),
+ *           request r, slot j; rows >= M hold 0, -1, -1
+ *   totals  [2]: M = cu[R] and M_pad = smallest tier >= M, or -1 if M
+ *           exceeds every tier */
+int dspark_pack_ragged(const int32_t* anchor, const int32_t* tokens, const int32_t* win_len,
+                       int R, int gamma, const int32_t* tiers, int n_tiers, int M_cap,
+                       int32_t* cu_seqlens, int32_t* packed_tokens, int32_t* packed_req,
+                       int32_t* packed_slot, int32_t* totals, void* stream);
+
+/* Rejection-sampling verification ([digest] summary and "Architecture": the
+ * longest conforming prefix is accepted by rejection sampling, lossless
+ * because every draft probability is an exact softmax; [sglang] "Verify
+ * modes"). Packed target row cu[r] + j holds the target's logits for slot
+ * j + 1; a request has Lv = cu[r+1] - cu[r] - 1 verified slots.
+ *   slot k accepted iff u_accept < p_t(x_k) / p_draft[r, k] (float32);
+ *   A_full = leading accepted slots; commit window L = Lv (STATIC, COMPACT)
+ *   or min(win_len[r], Lv) (CAP_ACCEPT); A = min(A_full, L);
+ *   A < L: resample slot A+1 from max(0, p_t - p_d) (p_d recomputed from U,
+ *          W1[x_A], W2 with lse_draft; from p_t if no residual mass is left);
+ *   A = L: bonus token for slot L+1 from p_t.
+ *   target_packed [M_cap, V] (dtype), cu_seqlens [R+1], anchor [R],
+ *   tokens, p_draft, lse_draft [R, gamma] (from dspark_markov_draft),
+ *   U [R, gamma, V], W1 [V, r], W2p (pre-packed), win_len [R] (CAP_ACCEPT
+ *   only, else may be NULL)
+ *   accept_len [R] out: A;  n_out [R] out: A + 1
+ *   out_tokens [R, gamma + 1] out: x_1..x_A, the correction/bonus token, then
+ *              -1 padding
+ *   ceiling_len [R] out or NULL: A_full (the cap-accept ceiling)
+ *   ws  workspace of dspark_workspace_bytes(DSPARK_CALL_VERIFY, ...) */
+int dspark_verify(const void* target_packed, int M_cap, const int32_t* cu_seqlens,
+                  const int32_t* anchor, const int32_t* tokens, const float* p_draft,
+                  const float* lse_draft, const void* U, const void* W1, const void* W2p,
+                  const int32_t* win_len, int mode, uint64_t seed, uint64_t step,
+                  const uint32_t* req_ids, int R, int gamma, int V, int r, int dtype,
+                  int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                  int32_t* ceiling_len, void* ws, size_t ws_bytes, void* stream);
+
+/* The first of the two passes dspark_markov_draft runs for every slot, as a
+ * call of its own (for callers that time or fuse it): the bias GEMM
+ * W1[x_prev] W2 on the matrix cores plus U_k, reduced per 64-entry vocabulary
+ * tile t to a softmax partial part[t * R + n] = (max_v z, sum_v exp(z - max))
+ * of request n (two floats). U_k rows are ldU elements apart; x_prev[n *
+ * xstride] is the previous token of request n. part must hold
+ * dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, R, 1, V, r) bytes. */
+int dspark_markov_partials(const void* U_k, long long ldU, const void* W1, const void* W2p,
+                           const int32_t* x_prev, int xstride, int R, int V, int r, int dtype,
+                           void* part, size_t part_bytes, void* stream);
+
+/* The second pass of a draft slot, as a call of its own: per request n, merge
+ * the tile partials of dspark_markov_partials into (m, S), draw u * S with the
+ * slot-k draft uniform of req_ids[n], find the tile where the cumulative mass
+ * crosses it, recompute that tile with the same matrix-core code and finish
+ * the inverse-CDF search. Writes tok_out[n * ostride] (the token),
+ * p_out[n * ostride] (its draft probability) and lse_out[n * ostride]
+ * (m + ln S). dspark_markov_draft is dspark_markov_partials followed by this
+ * call, for k = 1..gamma. */
+int dspark_markov_select(const void* U_k, long long ldU, const void* W1, const void* W2p,
+                         const int32_t* x_prev, int xstride, const void* part, uint64_t seed,
+                         uint64_t step, const uint32_t* req_ids, int k, int R, int V, int r,
+                         int dtype, int32_t* tok_out, float* p_out, float* lse_out, int ostride,
+                         void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostic                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Markov logits of one slot, written out in full: z[n, v] = U_k[n, v] +
+ * W1[x_prev[n]] . W2[:, v] (float32), computed by the same matrix-core tile
+ * code as dspark_markov_draft. U_k rows are `ldU` elements apart (gamma * V
+ * for a slot of a [R, gamma, V] block). For tests; not on the hot path. */
+int dspark_markov_logits(const void* U_k, long long ldU, const void* W1, const void* W2p,
+                         const int32_t* x_prev, int R, int V, int r, int dtype, float* z,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -21,6 +21,7 @@ Every array is drawn from its own child stream of ``numpy.random.SeedSequence``
 from __future__ import annotations
 
 import dataclasses
+import os
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -167,8 +168,18 @@ def small_spec(name: str = "small", *, R: int = 20, gamma: int = 5, V: int = 300
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 with round-to-nearest-even; returns the 16-bit
-    patterns as uint16. Inputs here are finite normals (no NaN handling)."""
+    patterns as uint16. Inputs here are finite normals (no NaN handling).
+    Uses torch's CPU conversion (the same rounding, multi-threaded) when torch
+    is importable, else the bit-level definition below."""
     x = np.ascontiguousarray(x, dtype=np.float32)
+    try:
+        import torch
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    except ImportError:  # pragma: no cover
+        return _to_bf16_bits_np(x)
+
+
+def _to_bf16_bits_np(x: np.ndarray) -> np.ndarray:
     u = x.view(np.uint32)
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
@@ -195,10 +206,42 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 _STREAMS = ("anchor", "W1", "W2", "target", "zipf", "noise", "h", "w", "cost")
 
 
-def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
-    out = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        out *= np.float32(std)
+_CHUNK = 1 << 20          # elements per independently seeded chunk
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def _rows_per_chunk(shape) -> Tuple[int, int]:
+    rows = int(shape[0])
+    inner = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    return rows, max(1, _CHUNK // max(1, inner))
+
+
+def _normal(ss: np.random.SeedSequence, shape, std: float) -> np.ndarray:
+    """N(0, std^2) float32 of `shape`, drawn in fixed row chunks along axis 0,
+    chunk i from child stream i of `ss` (so the result does not depend on the
+    number of threads)."""
+    out = np.empty(shape, dtype=np.float32)
+    rows, per = _rows_per_chunk(shape)
+    starts = list(range(0, rows, per))
+    kids = ss.spawn(len(starts))
+
+    def fill(i):
+        s0 = starts[i]
+        s1 = min(rows, s0 + per)
+        g = np.random.default_rng(kids[i])
+        g.standard_normal(size=out[s0:s1].shape, dtype=np.float32, out=out[s0:s1])
+        if std != 1.0:
+            out[s0:s1] *= np.float32(std)
+
+    list(_pool().map(fill, range(len(starts))))
     return out
 
 
@@ -260,40 +303,48 @@ def generate(spec: Spec, *, with_h: bool = True) -> Dict[str, np.ndarray]:
     "store" is float32 for dtype f32 and uint16 bfloat16 bit patterns for bf16.
     """
     R, g, V, r, d = spec.R, spec.gamma, spec.V, spec.r, spec.d
-    ss = np.random.SeedSequence(spec.seed).spawn(len(_STREAMS))
-    rngs = {name: np.random.default_rng(s) for name, s in zip(_STREAMS, ss)}
+    ss = dict(zip(_STREAMS, np.random.SeedSequence(spec.seed).spawn(len(_STREAMS))))
 
     out: Dict[str, np.ndarray] = {}
-    out["anchor"] = rngs["anchor"].integers(0, V, size=R, dtype=np.int64).astype(np.int32)
-    out["W1"] = _store(_normal(rngs["W1"], (V, r), spec.W_std), spec.dtype)
-    out["W2"] = _store(_normal(rngs["W2"], (r, V), spec.W_std), spec.dtype)
+    out["anchor"] = np.random.default_rng(ss["anchor"]).integers(0, V, size=R, dtype=np.int64).astype(np.int32)
+    out["W1"] = _store(_normal(ss["W1"], (V, r), spec.W_std), spec.dtype)
+    out["W2"] = _store(_normal(ss["W2"], (r, V), spec.W_std), spec.dtype)
 
-    target = _normal(rngs["target"], (R, g + 1, V), spec.target_std)
+    target = _normal(ss["target"], (R, g + 1, V), spec.target_std)
+    rows = target.reshape(R * (g + 1), V)
     if spec.zipf_s is not None:
         # Zipf(s) log-pmf over a per-row random ranking of the vocabulary:
         # the token ranked i (0-based) gets -s * ln(1 + i).
         table = (-spec.zipf_s * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
-        zr = rngs["zipf"]
         base = np.arange(V, dtype=np.int32)
-        rows = target.reshape(R * (g + 1), V)
-        chunk = 64
-        for s in range(0, rows.shape[0], chunk):
-            e = min(rows.shape[0], s + chunk)
-            ranks = zr.permuted(np.broadcast_to(base, (e - s, V)), axis=1)
-            rows[s:e] += table[ranks]
-    noise = _normal(rngs["noise"], (R, g, V), 1.0)
-    noise *= _noise_std(spec)[:, :, None]
-    U = target[:, :g, :] + noise
-    del noise
+        per = 8
+        starts = list(range(0, rows.shape[0], per))
+        kids = ss["zipf"].spawn(len(starts))
+
+        def add_bias(i):
+            s0 = starts[i]
+            s1 = min(rows.shape[0], s0 + per)
+            ranks = np.random.default_rng(kids[i]).permuted(np.broadcast_to(base, (s1 - s0, V)), axis=1)
+            rows[s0:s1] += table[ranks]
+
+        list(_pool().map(add_bias, range(len(starts))))
+    U = _normal(ss["noise"], (R, g, V), 1.0)
+    std = _noise_std(spec)
+
+    def add_target(i):
+        U[i] *= std[i][:, None]
+        U[i] += target[i, :g, :]
+
+    list(_pool().map(add_target, range(R)))
     out["target"] = _store(target, spec.dtype)
-    del target
+    del target, rows
     out["U"] = _store(U, spec.dtype)
     del U
     if with_h:
-        out["h"] = _store(_normal(rngs["h"], (R, g, d), 1.0), spec.dtype)
+        out["h"] = _store(_normal(ss["h"], (R, g, d), 1.0), spec.dtype)
     w_std = spec.w_std if spec.w_std is not None else float(1.0 / np.sqrt(d + r))
-    out["w"] = _normal(rngs["w"], (d + r,), w_std)
+    out["w"] = _normal(ss["w"], (d + r,), w_std)
     out["b"] = np.float32(spec.b)
-    out["raw_T"] = raw_step_time(spec, rngs["cost"])
+    out["raw_T"] = raw_step_time(spec, np.random.default_rng(ss["cost"]))
     out["req_ids"] = np.arange(R, dtype=np.uint32)
     return out

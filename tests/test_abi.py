@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dspark.h declares, rejects bad arguments on the host before touching
+the device, and its host cost-table utility matches the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+def _lib():
+    import draft_verify_sampling_markov_amd as dv
+    if not os.path.exists(dv.LIB_PATH):
+        pytest.skip("libdspark.so not built (run __graft_entry__.build())")
+    return dv, dv.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    dv, lib = _lib()
+    names = _declared()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(dv.EXPORTS) == names
+
+
+def test_status_strings():
+    dv, lib = _lib()
+    for rc in range(0, -7, -1):
+        s = dv.status_string(rc)
+        assert s.startswith("DSPARK")
+    assert "unknown" in dv.status_string(-99)
+
+
+def test_workspace_sizes():
+    dv, lib = _lib()
+    R, g, V, r = 64, 7, 151936, 256
+    n_t = -(-V // 64)
+    assert dv.workspace_bytes(dv.CALL_MARKOV_DRAFT, R, g, V, r) >= n_t * R * 8
+    assert dv.workspace_bytes(dv.CALL_VERIFY, R, g, V, r) > R * (g + 1) * 8
+    assert dv.workspace_bytes(dv.CALL_VERIFY, 4096, 1, V, r) == 0   # R(g+1) > 4096
+    assert dv.workspace_bytes(99, R, g, V, r) == 0
+    assert dv.prepacked_w2_bytes(256, V, dv.BF16) == n_t * 8 * 4 * 64 * 8 * 2
+    assert dv.prepacked_w2_bytes(300, V, dv.BF16) == 0
+    assert dv.prepacked_w2_bytes(200, V, dv.F32) == 0
+
+
+def test_host_validation_rejects_before_launch():
+    dv, lib = _lib()
+    EINVAL, EDTYPE, ETIER, ESIZE, EWS = -1, -2, -3, -4, -5
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
+    # markov_draft: bad dtype, bad sizes, null pointers, missing workspace
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 5, p, p, p, p, 1 << 30, None) == EDTYPE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 17, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 600, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 129, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_draft(None, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == EINVAL
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, p, 8, None) == EWS
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, None, 1 << 30, None) == EWS
+    # confidence
+    assert lib.dspark_confidence(p, p, p, p, p, 0.0, None, 4, 7, 0, 1024, 32, 0, p, p, None) == ESIZE
+    assert lib.dspark_confidence(p, None, p, p, p, 0.0, None, 4, 7, 64, 1024, 32, 0, p, p, None) == EINVAL
+    # schedule
+    assert lib.dspark_schedule_topb(p, None, p, 32, 4, 7, 12, 3, 0, p, p, None) == EINVAL
+    assert lib.dspark_schedule_topb(p, None, p, 3, 4, 7, 12, 0, 0, p, p, None) == ESIZE
+    assert lib.dspark_schedule_topb(None, None, p, 32, 4, 7, 12, 0, 0, p, p, None) == EINVAL
+    # pack: tiers
+    tiers = (ctypes.c_int32 * 3)(16, 8, 32)
+    assert lib.dspark_pack_ragged(p, p, None, 4, 7, tiers, 3, 32, p, p, p, p, p, None) == ETIER
+    tiers = (ctypes.c_int32 * 3)(8, 16, 32)
+    assert lib.dspark_pack_ragged(p, p, None, 4, 7, tiers, 0, 32, p, p, p, p, p, None) == ETIER
+    assert lib.dspark_pack_ragged(p, p, None, 4, 7, tiers, 3, 31, p, p, p, p, p, None) == ESIZE
+    # verify
+    args = [p, 32, p, p, p, p, p, p, p, p, None, 2, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, None, p, 1 << 30, None]
+    assert lib.dspark_verify(*args) == EINVAL          # cap-accept needs win_len
+    args[11] = 7
+    assert lib.dspark_verify(*args) == EINVAL          # bad mode
+    args[11] = 0
+    args[1] = 31
+    assert lib.dspark_verify(*args) == ESIZE           # M_cap < R (gamma + 1)
+    args[1] = 32
+    args[-2] = 16
+    assert lib.dspark_verify(*args) == EWS
+    # prepack
+    assert lib.dspark_prepack_w2(p, 32, 1024, 1, p, 10, None) == EWS
+    assert lib.dspark_prepack_w2(p, 32, 1024, 3, p, 1 << 30, None) == EDTYPE
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3", "dsv4", "mixed", "long"])
+def test_cost_table_matches_oracle(name):
+    dv, lib = _lib()
+    sp = synth.CONFIGS[name]
+    raw = synth.raw_step_time(sp)
+    got = dv.cost_table_prepare(raw, sp.tiers, sp.staircase)
+    ref = oracle.cost_table_prepare(raw, sp.tiers, sp.staircase)
+    assert got.tolist() == ref
+    assert got.shape[0] == sp.M_max + 1
+
+
+def test_cost_table_rejects_bad_tiers():
+    dv, lib = _lib()
+    with pytest.raises(dv.DsparkError):
+        dv.cost_table_prepare([1.0, 2.0, 3.0], [2, 1], True)
+    with pytest.raises(dv.DsparkError):
+        dv.cost_table_prepare([1.0, 2.0, 3.0], [], True)

@@ -1,0 +1,173 @@
+"""GPU parity of every stage against the oracle (teacher-forced stage by
+stage on the GPU's own chain outputs), through the C ABI.
+
+Small workloads span several 16-request blocks, several 64-entry vocabulary
+tiles and ragged tails in both; the five named workloads run at full size in
+the configuration bench.py times, with the oracle checking a sample of
+requests for the per-request stages and every request for schedule and pack.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (log, upload, PackedView, check_draft, check_confidence,
+                            check_schedule, check_pack, check_verify, sample_requests, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dv():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_verify_sampling_markov_amd as dv
+    dv.load_library()          # raises if the HIP library is missing
+    return dv
+
+
+MODES = {"static": 0, "compact": 1, "cap_accept": 2}
+
+
+def run_and_check(dv, spec, vmode: str, smode: int = oracle.SCHED_ARGMAX, B_cap=None, K_fixed=0,
+                  sample=None, seed=0, step=0, inp=None):
+    import torch
+    label = f"{spec.name}/{vmode}/sched{smode}/B{B_cap}"
+    log(f"[parity] {label}: R={spec.R} gamma={spec.gamma} V={spec.V} r={spec.r} dtype={spec.dtype}")
+    if inp is None:
+        inp = synth.generate(spec)
+    dev, sps = upload(inp, spec)
+    B = spec.budgets[0] if B_cap is None else B_cap
+    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B, verify_mode=MODES[vmode],
+                  sched_mode=smode, K_fixed=K_fixed, seed=seed, step=step)
+    ch.run(gather=True)
+    torch.cuda.synchronize()
+    res = ch.results()
+    reqs = np.arange(spec.R) if sample is None else sample_requests(spec.R, sample)
+    flips = check_draft(res, inp, seed, step, reqs, label)
+    check_confidence(res, inp, reqs, label)
+    ref_s = check_schedule(res, sps, B, smode, K_fixed, label)
+    full = vmode in ("static", "cap_accept")
+    check_pack(res, inp, None if full else ref_s["win_len"], spec.tiers, ch.M_cap, label)
+    rows = PackedView(inp["target"], res["cu_seqlens"])
+    flips += check_verify(res, inp, rows, MODES[vmode], res["win_len"], seed, step, reqs, label)
+    log(f"[parity] {label}: ok, K={int(res['K'][0])} M={res['totals'].tolist()} "
+        f"mean A={res['accept_len'].mean():.2f} excused flips={flips}")
+    return res, ch
+
+
+# ---------------------------------------------------------------------------
+# diagnostic: the matrix-core logits tile against the oracle's logits
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,V,r,R", [("f32", 1000, 32, 20), ("bf16", 3000, 64, 20),
+                                          ("bf16", 2950, 256, 33), ("bf16", 517, 100, 5),
+                                          ("f32", 640, 128, 16)])
+def test_markov_logits_tile(dv, dtype, V, r, R):
+    import torch
+    log(f"[logits] dtype={dtype} V={V} r={r} R={R}")
+    sp = synth.small_spec(R=R, gamma=2, V=V, r=r, d=8, dtype=dtype, W_std=0.3)
+    inp = synth.generate(sp)
+    dev, _ = upload(inp, sp)
+    W2p = dv.prepack_w2(dev["W2"])
+    x_prev = to_dev(inp["anchor"])
+    z = dv.markov_logits(dev["U"], sp.gamma * V, dev["W1"], W2p, x_prev, R=R, V=V, r=r)
+    torch.cuda.synchronize()
+    ref = oracle.markov_logits(inp["U"][:, 0], inp["W1"], inp["W2"], inp["anchor"])
+    np.testing.assert_allclose(z.cpu().numpy(), ref, rtol=0, atol=2e-5)
+
+
+# ---------------------------------------------------------------------------
+# small workloads: every stage, every mode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("vmode", ["static", "compact", "cap_accept"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_chain(dv, vmode, dtype):
+    sp = synth.small_spec(R=20, gamma=5, V=3000, r=64, d=96, dtype=dtype)
+    run_and_check(dv, sp, vmode)
+
+
+@pytest.mark.parametrize("smode", [oracle.SCHED_GREEDY, oracle.SCHED_FIXED])
+def test_small_chain_sched_modes(dv, smode):
+    sp = synth.small_spec(R=37, gamma=4, V=1777, r=48, d=40, dtype="bf16", seed=5)
+    run_and_check(dv, sp, "compact", smode=smode, K_fixed=50)
+
+
+def test_small_chain_ragged_rank_and_vocab(dv):
+    # rank not a multiple of 8 (scalar staging), vocabulary not a multiple of 8
+    sp = synth.small_spec(R=18, gamma=3, V=997, r=45, d=33, dtype="bf16", seed=9)
+    run_and_check(dv, sp, "compact")
+
+
+def test_cap_accept_commits_match_compact(dv):
+    sp = synth.small_spec(R=40, gamma=6, V=2048, r=32, d=64, dtype="bf16", seed=21)
+    inp = synth.generate(sp)
+    comp, _ = run_and_check(dv, sp, "compact", inp=inp)
+    cap, _ = run_and_check(dv, sp, "cap_accept", inp=inp)
+    assert np.array_equal(comp["tokens"], cap["tokens"])
+    assert np.array_equal(comp["win_len"], cap["win_len"])
+    assert np.array_equal(comp["accept_len"], cap["accept_len"])
+    assert np.array_equal(comp["out_tokens"], cap["out_tokens"])
+    assert np.all(cap["ceiling_len"] >= cap["accept_len"])
+
+
+def test_determinism(dv):
+    import torch
+    sp = synth.small_spec(R=24, gamma=5, V=3000, r=64, d=32, dtype="bf16", seed=3)
+    inp = synth.generate(sp)
+    dev, _ = upload(inp, sp)
+    outs = []
+    for _ in range(2):
+        ch = dv.Chain(dev, b=float(inp["b"]), tiers=sp.tiers, B_cap=sp.R * sp.gamma, verify_mode=1)
+        ch.run()
+        torch.cuda.synchronize()
+        outs.append(ch.results())
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_step_and_seed_change_draws(dv):
+    sp = synth.small_spec(R=16, gamma=4, V=1000, r=32, d=16, dtype="bf16", seed=4)
+    inp = synth.generate(sp)
+    a, _ = run_and_check(dv, sp, "static", inp=inp, seed=0, step=0)
+    b, _ = run_and_check(dv, sp, "static", inp=inp, seed=0, step=1)
+    c, _ = run_and_check(dv, sp, "static", inp=inp, seed=7, step=0)
+    assert not np.array_equal(a["tokens"], b["tokens"])
+    assert not np.array_equal(a["tokens"], c["tokens"])
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_tiny_all_modes(dv):
+    sp = synth.CONFIGS["tiny"]
+    inp = synth.generate(sp)
+    for vmode in ("static", "compact", "cap_accept"):
+        for smode in (oracle.SCHED_ARGMAX, oracle.SCHED_GREEDY, oracle.SCHED_FIXED):
+            if vmode != "compact" and smode != oracle.SCHED_ARGMAX:
+                continue
+            run_and_check(dv, sp, vmode, smode=smode, K_fixed=6, inp=inp)
+
+
+@pytest.mark.parametrize("vmode", ["static", "compact"])
+def test_qwen3(dv, vmode):
+    run_and_check(dv, synth.CONFIGS["qwen3"], vmode, sample=12)
+
+
+def test_dsv4_compact(dv):
+    run_and_check(dv, synth.CONFIGS["dsv4"], "compact", sample=12)
+
+
+@pytest.mark.parametrize("vmode", ["cap_accept", "compact"])
+def test_mixed(dv, vmode):
+    run_and_check(dv, synth.CONFIGS["mixed"], vmode, sample=12)
+
+
+def test_long_budget_sweep(dv):
+    sp = synth.CONFIGS["long"]
+    inp = synth.generate(sp)
+    for B in sp.budgets:
+        run_and_check(dv, sp, "compact", B_cap=B, sample=8, inp=inp)
