@@ -281,4 +281,130 @@ __device__ __forceinline__ void tile_logits(const f32x4 acc[4], const float u16[
 }
 
 
+
+// ---------------------------------------------------------------------------
+// block-wide inverse-CDF tile search
+// ---------------------------------------------------------------------------
+//
+// One workgroup per request. Thread p owns tiles [p c, (p+1) c) of the n_t
+// per-tile weights w_t = wfn(t) (c = ceil(n_t / threads)). The workgroup
+// forms S = sum_t w_t (thread-local sums in tile order, then a fixed-order
+// scan over threads) and T = u S, finds the first thread whose inclusive
+// prefix exceeds T, and that thread walks its tiles to the first one where the
+// cumulative weight crosses T. Result: the crossing tile and the cumulative
+// weight before it (pb). When rounding leaves no crossing, the result is the
+// last tile with positive weight and pb = -inf, which makes the in-tile search
+// end at its last positive entry.
+
+struct TileSearchShared {
+  float wsum[16];
+  int wfirst[16];
+  int wlast[16];
+  int tstar;
+  float pb, S, T;
+};
+
+template <typename WFn>
+__device__ __forceinline__ void block_tile_search(int n_t, float u, WFn wfn, TileSearchShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nw = blockDim.x / kWave;
+  const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
+  float ls = 0.0f;
+  int last = -1;
+  for (int t = t0; t < t1; ++t) {
+    const float w = wfn(t);
+    if (w > 0.0f) last = t;
+    ls += w;
+  }
+  float incl = wave_inclusive_scan(ls, lane);
+  int wl = last;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wl = max(wl, __shfl_xor(wl, o, kWave));
+  if (lane == kWave - 1) sh.wsum[wave] = incl;
+  if (lane == 0) sh.wlast[wave] = wl;
+  __syncthreads();
+  float off = 0.0f;
+  for (int w = 0; w < wave; ++w) off += sh.wsum[w];
+  int glast = -1;
+  for (int w = 0; w < nw; ++w) glast = max(glast, sh.wlast[w]);
+  float S = 0.0f;  // same order as the offsets: the last thread's prefix is S
+  for (int w = 0; w < nw; ++w) S += sh.wsum[w];
+  const float T = u * S;
+  const float prev_in_wave = __shfl_up(incl, 1, kWave);
+  incl += off;
+  const float prev = (lane == 0) ? off : prev_in_wave + off;
+  const unsigned long long pm = __ballot(incl > T);
+  if (lane == 0) sh.wfirst[wave] = pm ? wave * kWave + __ffsll((long long)pm) - 1 : 0x7fffffff;
+  __syncthreads();
+  int pstar = 0x7fffffff;
+  for (int w = 0; w < nw; ++w) pstar = min(pstar, sh.wfirst[w]);
+  if (tid == 0) {
+    sh.S = S;
+    sh.T = T;
+    if (pstar == 0x7fffffff) {
+      sh.tstar = glast;
+      sh.pb = -INFINITY;
+    }
+  }
+  if (tid == pstar) {
+    float cum = prev;
+    int found = -1, lastpos = -1;
+    float pbv = -INFINITY;
+    for (int t = t0; t < t1; ++t) {
+      const float w = wfn(t);
+      if (w > 0.0f) lastpos = t;
+      const float cn = cum + w;
+      if (cn > T) {
+        found = t;
+        pbv = cum;
+        break;
+      }
+      cum = cn;
+    }
+    sh.tstar = found >= 0 ? found : (lastpos >= 0 ? lastpos : glast);
+    sh.pb = found >= 0 ? pbv : -INFINITY;
+  }
+  __syncthreads();
+}
+
+// Largest value of v over the workgroup (fixed order).
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  v = wave_max(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+// Sum over the workgroup (fixed order).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+  for (int w = 0; w < nw; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// In-tile inverse-CDF search by one wave: lane i holds weight e_i of entry
+// v = 64 t + i (0 outside the vocabulary). Returns the lane of the first entry
+// whose cumulative weight pb + sum_{j <= i} e_j exceeds T, else the last lane
+// with positive weight.
+__device__ __forceinline__ int tile_pick(float e, bool valid, float pb, float T, int lane) {
+  const float sc = wave_inclusive_scan(e, lane);
+  const bool cross = valid && (pb + sc > T);
+  const unsigned long long cm = __ballot(cross);
+  if (cm) return __ffsll((long long)cm) - 1;
+  const unsigned long long pm = __ballot(e > 0.0f);
+  return pm ? 63 - __clzll((long long)pm) : 0;
+}
+
 }  // namespace dspark

@@ -114,15 +114,6 @@ __global__ __launch_bounds__(512) void markov_partials_kernel(
 // pass B: per-request draw
 // ---------------------------------------------------------------------------
 
-struct SelectShared {
-  float m[16][16];     // [part][request]
-  float s[16][16];
-  float off[17][16];
-  int last[16][16];
-  float mrow[16], S[16], T[16], pb[16];
-  int tstar[16];
-};
-
 template <bool BF16, int KC>
 __global__ __launch_bounds__(256) void markov_select_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
@@ -135,129 +126,65 @@ __global__ __launch_bounds__(256) void markov_select_kernel(
   constexpr int kpad = KC * kChunkK;
   constexpr int ldw = kpad + kLdsPad;
   __shared__ __align__(16) T w1s[16 * ldw];
-  __shared__ SelectShared sh;
+  __shared__ TileSearchShared ts;
+  __shared__ float red[16];
 
   const int tid = threadIdx.x;
-  const int nb0 = blockIdx.x * kTileN;
+  const int n = blockIdx.x;              // this workgroup's request
+  const int nb0 = n & ~(kTileN - 1);     // its 16-request matrix-core block
+  const int q = n - nb0;
   const int count = min(kTileN, R - nb0);
   stage_rows<BF16>(W1, xprev + (size_t)nb0 * xstride, xstride, count, 16, r, V, kpad, ldw, w1s);
 
-  // ---- phase 1: merge partials, find the crossing tile ----
-  const int q = tid & 15, p = tid >> 4;
-  const int n = nb0 + q;
-  const bool active = q < count;
-  const int c = (n_t + 15) / 16;
-  const int t0 = min(n_t, p * c), t1 = min(n_t, t0 + c);
+  // merge the per-tile partials: m = max_t m_t, w_t = s_t exp(m_t - m)
+  const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
   float lm = -INFINITY;
-  if (active)
-    for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[(size_t)t * ldp + n].x);
-  sh.m[p][q] = lm;
-  __syncthreads();
-  float m = -INFINITY;
-#pragma unroll
-  for (int pp = 0; pp < 16; ++pp) m = fmaxf(m, sh.m[pp][q]);
-  float ls = 0.0f;
-  int last = -1;
-  if (active && m != -INFINITY) {
-    for (int t = t0; t < t1; ++t) {
-      const float2 pv = part[(size_t)t * ldp + n];
-      const float w = pv.y * __expf(pv.x - m);
-      if (w > 0.0f) last = t;
-      ls += w;
-    }
-  }
-  sh.s[p][q] = ls;
-  sh.last[p][q] = last;
-  __syncthreads();
-  if (p == 0) {
-    float off = 0.0f;
-    int lst = -1;
-    for (int pp = 0; pp < 16; ++pp) {
-      sh.off[pp][q] = off;
-      off += sh.s[pp][q];
-      lst = max(lst, sh.last[pp][q]);
-    }
-    sh.off[16][q] = off;
-    sh.S[q] = off;
-    sh.mrow[q] = m;
-    float Tq = 0.0f;
-    if (active) Tq = slot_uniform(seed, step, req_ids[n], k, kPurposeDraft) * off;
-    sh.T[q] = Tq;
-    // fallback (no part owns T): last tile with mass, searched to its end
-    sh.tstar[q] = lst;
-    sh.pb[q] = -INFINITY;   // never crosses: the search ends at the last positive entry
-  }
-  __syncthreads();
-  if (active) {
-    const float Tq = sh.T[q], o0 = sh.off[p][q], o1 = sh.off[p + 1][q];
-    if (Tq >= o0 && Tq < o1) {
-      float lc = 0.0f;
-      for (int t = t0; t < t1; ++t) {
-        const float2 pv = part[(size_t)t * ldp + n];
-        const float lcn = lc + pv.y * __expf(pv.x - m);
-        if (o0 + lcn > Tq) {
-          sh.tstar[q] = t;
-          sh.pb[q] = o0 + lc;
-          break;
-        }
-        lc = lcn;
-      }
-    }
-  }
-  __syncthreads();
+  for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[(size_t)t * ldp + n].x);
+  const float m = block_max(lm, red);
+  const float u = slot_uniform(seed, step, req_ids[n], k, kPurposeDraft);
+  block_tile_search(n_t, u, [&](int t) {
+    const float2 pv = part[(size_t)t * ldp + n];
+    return pv.y * __expf(pv.x - m);
+  }, ts);
 
-  // ---- phase 2: recompute the crossing tile, finish the search ----
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  // wave 0 recomputes the crossing tile and finishes the search in it
+  if (tid >= kWave) return;  // no barrier below
+  const int lane = tid;
   const int g = lane >> 4, nl = lane & 15;
-  for (int it = 0; it < 4; ++it) {
-    const int qq = wave + 4 * it;
-    if (qq >= count) continue;  // wave-uniform
-    const int nn = nb0 + qq;
-    const int t = min(max(sh.tstar[qq], 0), n_t - 1);
-    ATile<BF16, KC> at;
-    load_a_tile<BF16, KC>(W2p, t, lane, at);
-    f32x4 acc[4];
-    tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
-    const int v0 = t * kTileV + 16 * g;
-    const int nvalid = min(16, V - v0);
-    float u16[16];
-    const bool mine = (nl == qq);
-    if (mine && nvalid > 0) {
-      load16<BF16>(U + (size_t)nn * ldU + v0, nvalid, vec, u16);
-    } else {
+  const int t = min(max(ts.tstar, 0), n_t - 1);
+  ATile<BF16, KC> at;
+  load_a_tile<BF16, KC>(W2p, t, lane, at);
+  f32x4 acc[4];
+  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+  const int v0 = t * kTileV + 16 * g;
+  const int nvalid = min(16, V - v0);
+  float u16[16];
+  if (nl == q && nvalid > 0) {
+    load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
+  } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
-    }
-    float z[16];
-    tile_logits<BF16>(acc, u16, nvalid, true, z);
-    // lane i of the wave takes entry v = 64 t + i from lane qq + 16 (i / 16)
-    const int src = qq + 16 * (lane >> 4);
-    float zi = -INFINITY;
+    for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
+  }
+  float z[16];
+  tile_logits<BF16>(acc, u16, nvalid, true, z);
+  // lane i takes entry v = 64 t + i from lane q + 16 (i / 16)
+  const int src = q + 16 * (lane >> 4);
+  float zi = -INFINITY;
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const float val = __shfl(z[idx], src, kWave);
-      if ((lane & 15) == idx) zi = val;
-    }
-    const int v = t * kTileV + lane;
-    const bool valid = v < V;
-    const float mrow = sh.mrow[qq], S = sh.S[qq], Tq = sh.T[qq], pb = sh.pb[qq];
-    const float e = valid ? __expf(zi - mrow) : 0.0f;
-    const float sc = wave_inclusive_scan(e, lane);
-    const bool cross = valid && (pb + sc > Tq);
-    const unsigned long long cm = __ballot(cross);
-    int sel;
-    if (cm) {
-      sel = __ffsll((long long)cm) - 1;
-    } else {
-      const unsigned long long pm = __ballot(e > 0.0f);
-      sel = pm ? 63 - __clzll((long long)pm) : 0;
-    }
-    const float esel = __shfl(e, sel, kWave);
-    if (lane == 0) {
-      tok_out[(size_t)nn * ostride] = t * kTileV + sel;
-      p_out[(size_t)nn * ostride] = esel / S;
-      lse_out[(size_t)nn * ostride] = mrow + __logf(S);
-    }
+  for (int idx = 0; idx < 16; ++idx) {
+    const float val = __shfl(z[idx], src, kWave);
+    if ((lane & 15) == idx) zi = val;
+  }
+  const int v = t * kTileV + lane;
+  const bool valid = v < V;
+  const float e = valid ? __expf(zi - m) : 0.0f;
+  const int sel = tile_pick(e, valid, ts.pb, ts.T, lane);
+  const float esel = __shfl(e, sel, kWave);
+  if (lane == 0) {
+    tok_out[(size_t)n * ostride] = t * kTileV + sel;
+    p_out[(size_t)n * ostride] = esel / ts.S;
+    lse_out[(size_t)n * ostride] = m + __logf(ts.S);
   }
 }
 
@@ -366,7 +293,7 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
     const T* Uk = Ub + (size_t)(k - 1) * V;
     int st = launch_partials<BF16, KC>(Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, part, s);
     if (st) return st;
-    hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(ceil_div(R, kTileN)), dim3(256), 0, s,
+    hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
                        Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, n_t, part, R, seed, step,
                        req_ids, k, tokens + (k - 1), p_draft + (k - 1), lse_draft + (k - 1), gamma);
     st = launch_status();
@@ -526,7 +453,7 @@ static int launch_select_api(const void* U, long long ldU, const void* W1, const
   typedef typename Elem<BF16>::T T;
   const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
                    (reinterpret_cast<uintptr_t>(U) % 16) == 0;
-  hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(ceil_div(R, kTileN)), dim3(256), 0, s,
+  hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
                      static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
                      static_cast<const T*>(W2p), x_prev, xstride, R, V, r, n_vtiles(V), part, R,
                      seed, step, req_ids, k, tok, p, lse, ostride);

@@ -305,16 +305,6 @@ __global__ __launch_bounds__(512) void residual_partials_kernel(
 // residual select
 // ---------------------------------------------------------------------------
 
-struct RSelShared {
-  float sq[16][16];  // [part][request]
-  float sp[16][16];
-  float off[17][16];
-  int lastq[16][16];
-  int lastp[16][16];
-  float S[16], T[16], pb[16];
-  int tstar[16], usept[16];
-};
-
 template <bool BF16, int KC>
 __global__ __launch_bounds__(256) void residual_select_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
@@ -325,119 +315,62 @@ __global__ __launch_bounds__(256) void residual_select_kernel(
   constexpr int kpad = KC * kChunkK;
   constexpr int ldw = kpad + kLdsPad;
   __shared__ __align__(16) T w1s[16 * ldw];
-  __shared__ RSelShared sh;
+  __shared__ TileSearchShared ts;
+  __shared__ float red[16];
   const int tid = threadIdx.x;
-  const int nb0 = blockIdx.x * kTileN;
+  const int n = blockIdx.x;
+  const int nb0 = n & ~(kTileN - 1);
+  const int q = n - nb0;
   const int count = min(kTileN, R - nb0);
   stage_rows<BF16>(W1, jobs.xprev + nb0, 1, count, 16, r, V, kpad, ldw, w1s);
 
-  const int q = tid & 15, p = tid >> 4;
-  const int n = nb0 + q;
-  const bool active = q < count;
-  const int c = (n_t + 15) / 16;
-  const int t0 = min(n_t, p * c), t1 = min(n_t, t0 + c);
-  float lq = 0.0f, lp = 0.0f;
-  int lastq = -1, lastp = -1;
-  if (active)
-    for (int t = t0; t < t1; ++t) {
-      const float2 pv = rpart[(size_t)t * ldp + n];
-      if (pv.x > 0.0f) lastq = t;
-      if (pv.y > 0.0f) lastp = t;
-      lq += pv.x;
-      lp += pv.y;
-    }
-  sh.sq[p][q] = lq;
-  sh.sp[p][q] = lp;
-  sh.lastq[p][q] = lastq;
-  sh.lastp[p][q] = lastp;
-  __syncthreads();
-  if (p == 0) {
-    float tq = 0.0f;
-    for (int pp = 0; pp < 16; ++pp) tq += sh.sq[pp][q];
-    const int use_pt = !(tq > 0.0f);  // no residual mass left: draw from p_t
-    float off = 0.0f;
-    int lst = -1;
-    for (int pp = 0; pp < 16; ++pp) {
-      sh.off[pp][q] = off;
-      off += use_pt ? sh.sp[pp][q] : sh.sq[pp][q];
-      lst = max(lst, use_pt ? sh.lastp[pp][q] : sh.lastq[pp][q]);
-    }
-    sh.off[16][q] = off;
-    sh.S[q] = off;
-    sh.usept[q] = use_pt;
-    sh.T[q] = active ? jobs.u[n] * off : 0.0f;
-    sh.tstar[q] = lst;
-    sh.pb[q] = -INFINITY;  // fallback never crosses: last positive entry
-  }
-  __syncthreads();
-  if (active) {
-    const float Tq = sh.T[q], o0 = sh.off[p][q], o1 = sh.off[p + 1][q];
-    const int use_pt = sh.usept[q];
-    if (Tq >= o0 && Tq < o1) {
-      float lc = 0.0f;
-      for (int t = t0; t < t1; ++t) {
-        const float2 pv = rpart[(size_t)t * ldp + n];
-        const float lcn = lc + (use_pt ? pv.y : pv.x);
-        if (o0 + lcn > Tq) {
-          sh.tstar[q] = t;
-          sh.pb[q] = o0 + lc;
-          break;
-        }
-        lc = lcn;
-      }
-    }
-  }
-  __syncthreads();
+  // residual mass left? (else draw from p_t)
+  const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
+  float lq = 0.0f;
+  for (int t = t0; t < t1; ++t) lq += rpart[(size_t)t * ldp + n].x;
+  const float tq = block_sum(lq, red);
+  const bool use_pt = !(tq > 0.0f);
+  block_tile_search(n_t, jobs.u[n], [&](int t) {
+    const float2 pv = rpart[(size_t)t * ldp + n];
+    return use_pt ? pv.y : pv.x;
+  }, ts);
 
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  if (tid >= kWave) return;  // wave 0 finishes; no barrier below
+  const int lane = tid;
   const int g = lane >> 4, nl = lane & 15;
-  for (int it = 0; it < 4; ++it) {
-    const int qq = wave + 4 * it;
-    if (qq >= count) continue;  // wave-uniform
-    const int nn = nb0 + qq;
-    const int t = min(max(sh.tstar[qq], 0), n_t - 1);
-    ATile<BF16, KC> at;
-    load_a_tile<BF16, KC>(W2p, t, lane, at);
-    f32x4 acc[4];
-    tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
-    const int v0 = t * kTileV + 16 * g;
-    const int nvalid = min(16, V - v0);
-    const bool residual = jobs.kind[nn] == 0;
-    const int trow = jobs.trow[nn], dslot = jobs.slot[nn] - 1;
-    const float lse_t = jobs.lse_t[nn], lse_d = jobs.lse_d[nn];
-    float zt16[16], u16[16];
-    const bool mine = nl == qq;
-    if (mine && nvalid > 0) {
-      load_corr_inputs<BF16>(target, U, V, gamma, vec, nn, v0, nvalid, trow, dslot, residual, zt16, u16);
-    } else {
+  const int t = min(max(ts.tstar, 0), n_t - 1);
+  ATile<BF16, KC> at;
+  load_a_tile<BF16, KC>(W2p, t, lane, at);
+  f32x4 acc[4];
+  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+  const int v0 = t * kTileV + 16 * g;
+  const int nvalid = min(16, V - v0);
+  const bool residual = jobs.kind[n] == 0;
+  const int trow = jobs.trow[n], dslot = jobs.slot[n] - 1;
+  const float lse_t = jobs.lse_t[n], lse_d = jobs.lse_d[n];
+  float zt16[16], u16[16];
+  const bool mine = nl == q;
+  if (mine && nvalid > 0) {
+    load_corr_inputs<BF16>(target, U, V, gamma, vec, n, v0, nvalid, trow, dslot, residual, zt16, u16);
+  } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) zt16[i] = u16[i] = 0.0f;
-    }
-    float qv[16], pv[16];
-    corr_tile_values<BF16>(acc, zt16, u16, (mine ? nvalid : 0), lse_t, lse_d, residual, qv, pv);
-    const int use_pt = sh.usept[qq];
-    const int src = qq + 16 * (lane >> 4);
-    float wi = 0.0f;
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const float val = __shfl(use_pt ? pv[idx] : qv[idx], src, kWave);
-      if ((lane & 15) == idx) wi = val;
-    }
-    const int v = t * kTileV + lane;
-    const bool valid = v < V;
-    if (!valid) wi = 0.0f;
-    const float sc = wave_inclusive_scan(wi, lane);
-    const bool cross = valid && (sh.pb[qq] + sc > sh.T[qq]);
-    const unsigned long long cm = __ballot(cross);
-    int sel;
-    if (cm) {
-      sel = __ffsll((long long)cm) - 1;
-    } else {
-      const unsigned long long pm = __ballot(wi > 0.0f);
-      sel = pm ? 63 - __clzll((long long)pm) : 0;
-    }
-    if (lane == 0) out_tokens[(size_t)nn * (gamma + 1) + jobs.slot[nn] - 1] = t * kTileV + sel;
+    for (int i = 0; i < 16; ++i) zt16[i] = u16[i] = 0.0f;
   }
+  float qv[16], pv[16];
+  corr_tile_values<BF16>(acc, zt16, u16, (mine ? nvalid : 0), lse_t, lse_d, residual, qv, pv);
+  const int src = q + 16 * (lane >> 4);
+  float wi = 0.0f;
+#pragma unroll
+  for (int idx = 0; idx < 16; ++idx) {
+    const float val = __shfl(use_pt ? pv[idx] : qv[idx], src, kWave);
+    if ((lane & 15) == idx) wi = val;
+  }
+  const int v = t * kTileV + lane;
+  const bool valid = v < V;
+  if (!valid) wi = 0.0f;
+  const int sel = tile_pick(wi, valid, ts.pb, ts.T, lane);
+  if (lane == 0) out_tokens[(size_t)n * (gamma + 1) + jobs.slot[n] - 1] = t * kTileV + sel;
 }
 
 // ---------------------------------------------------------------------------
@@ -527,7 +460,7 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
     st = launch_status();
     if (st) return st;
   }
-  hipLaunchKernelGGL((residual_select_kernel<BF16, KC>), dim3(ceil_div(R, kTileN)), dim3(256), 0, s,
+  hipLaunchKernelGGL((residual_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
                      tg, Ub, vec, W1b, W2b, ws.jobs, R, gamma, V, r, n_t, ws.rpart, R, out_tokens);
   return launch_status();
 }
