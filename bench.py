@@ -89,6 +89,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="steps of per-kernel event timing (default: --steps)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one 256 MiB device-to-device copy (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -207,6 +210,14 @@ def main() -> int:
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
     }
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(spec, inp, args.mode)

@@ -78,6 +78,126 @@ __device__ __forceinline__ void load16(const typename Elem<BF16>::T* __restrict_
   }
 }
 
+
+// 16 consecutive elements kept as raw 16-byte words (bf16: 2 words holding
+// 8 values each; f32: 4 words), so a prefetch costs 8 or 16 VGPRs.
+template <bool BF16>
+struct Raw16 {
+  u32x4 w[BF16 ? 2 : 4];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load16_raw(const typename Elem<BF16>::T* __restrict__ p, int n,
+                                           bool vec, Raw16<BF16>& r) {
+  constexpr int NW = BF16 ? 2 : 4;
+  if (vec && n >= 16) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) r.w[i] = __builtin_nontemporal_load(q + i);
+  } else {
+    uint32_t bits[4 * NW];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = (2 * i < n) ? p[2 * i] : 0u;
+        const uint32_t hi = (2 * i + 1 < n) ? p[2 * i + 1] : 0u;
+        bits[i] = lo | (hi << 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bits[i] = (i < n) ? __float_as_uint(p[i]) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      r.w[i] = u32x4{bits[4 * i], bits[4 * i + 1], bits[4 * i + 2], bits[4 * i + 3]};
+  }
+}
+
+// Branch-free load of 16 elements row[v0 .. v0+16) for the engine's
+// pipelined epilogues. Every address stays inside the row [0, V): with VEC
+// (16-byte aligned rows, V a multiple of the vector width) word i reads from
+// v0 + VEC * min(i, words_valid - 1), and a lane past the end reads from the
+// row start; without VEC each element is read from min(v0 + i, V - 1). Entries
+// at or beyond nvalid hold arbitrary row values and must be masked by the
+// caller.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load16_clamped(const typename Elem<BF16>::T* __restrict__ row,
+                                               int v0, int nvalid, int V, Raw16<BF16>& r) {
+  constexpr int W = BF16 ? 2 : 4;
+  constexpr int PER = Elem<BF16>::kVec;
+  if constexpr (VEC) {
+    const int base = nvalid > 0 ? v0 : 0;
+    const int nv = nvalid > 0 ? min(W, (nvalid + PER - 1) / PER) : 1;
+    const u32x4* q = reinterpret_cast<const u32x4*>(row + base);
+#pragma unroll
+    for (int i = 0; i < W; ++i) r.w[i] = __builtin_nontemporal_load(q + min(i, nv - 1));
+  } else {
+    uint32_t bits[4 * W];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = row[min(v0 + 2 * i, V - 1)];
+        const uint32_t hi = row[min(v0 + 2 * i + 1, V - 1)];
+        bits[i] = lo | (hi << 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bits[i] = __float_as_uint(row[min(v0 + i, V - 1)]);
+    }
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+      r.w[i] = u32x4{bits[4 * i], bits[4 * i + 1], bits[4 * i + 2], bits[4 * i + 3]};
+  }
+}
+
+// Softmax partial of 16 masked logits (-inf = masked) merged over the four
+// lanes holding one request's 64 entries, without branches.
+__device__ __forceinline__ void softmax16_merge4(const float z[16], float& m_out, float& s_out) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, z[i]);
+  const float mref = (m == -INFINITY) ? 0.0f : m;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += __expf(z[i] - mref);
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+    const float mm = fmaxf(m, m2);
+    const float mr = (mm == -INFINITY) ? 0.0f : mm;
+    const float sa = (m == -INFINITY) ? 0.0f : s * __expf(m - mr);
+    const float sb = (m2 == -INFINITY) ? 0.0f : s2 * __expf(m2 - mr);
+    s = sa + sb;
+    m = mm;
+  }
+  m_out = m;
+  s_out = s;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack16(const Raw16<BF16>& r, float out[16]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[8 * h + 2 * i] = __uint_as_float(r.w[h][i] << 16);
+        out[8 * h + 2 * i + 1] = __uint_as_float(r.w[h][i] & 0xFFFF0000u);
+      }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[4 * h + i] = __uint_as_float(r.w[h][i]);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void zero16(Raw16<BF16>& r) {
+#pragma unroll
+  for (int i = 0; i < (BF16 ? 2 : 4); ++i) r.w[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x64-10
 // ---------------------------------------------------------------------------
@@ -265,6 +385,63 @@ __device__ __forceinline__ void stage_rows(const typename Elem<BF16>::T* __restr
   }
 }
 
+// The same staging split in two: load the W1 rows of up to 16 requests into
+// registers (each thread at most 4 vectors of 16 bytes), later store them into
+// LDS, so the loads overlap other work. Needs r a multiple of the vector width
+// and (16 * (KC * 32 / VEC)) <= 4 * blockDim.x.
+template <bool BF16, int KC>
+struct W1Stage {
+  u32x4 v[4];
+};
+
+template <bool BF16, int KC>
+__device__ __forceinline__ void w1_stage_load(const typename Elem<BF16>::T* __restrict__ W1,
+                                              const int* __restrict__ xprev, int xstride, int count,
+                                              int r, int V, W1Stage<BF16, KC>& st) {
+  constexpr int VEC = Elem<BF16>::kVec;
+  constexpr int per_row = KC * kChunkK / VEC;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * (int)blockDim.x + (int)threadIdx.x;
+    const int n = idx / per_row, c = idx - n * per_row;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (n < count && c * VEC < r) {
+      const int tok = clamp_token(xprev[(size_t)n * xstride], V);
+      val = *reinterpret_cast<const u32x4*>(W1 + (size_t)tok * r + c * VEC);
+    }
+    st.v[i] = val;
+  }
+}
+
+template <bool BF16, int KC>
+__device__ __forceinline__ void w1_stage_store(const W1Stage<BF16, KC>& st, int ldw,
+                                               typename Elem<BF16>::T* lds) {
+  constexpr int VEC = Elem<BF16>::kVec;
+  constexpr int per_row = KC * kChunkK / VEC;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * (int)blockDim.x + (int)threadIdx.x;
+    const int n = idx / per_row, c = idx - n * per_row;
+    if (n < 16) *reinterpret_cast<u32x4*>(lds + n * ldw + c * VEC) = st.v[i];
+  }
+}
+
+// Stage `count` gathered rows (kpad elements each, contiguous, already zero
+// padded) into LDS rows of ldw elements; rows count..15 are zero.
+template <bool BF16>
+__device__ __forceinline__ void stage_gathered(const typename Elem<BF16>::T* __restrict__ rows_in,
+                                               int count, int kpad, int ldw,
+                                               typename Elem<BF16>::T* lds) {
+  constexpr int VEC = Elem<BF16>::kVec;
+  const int per_row = kpad / VEC;
+  for (int idx = threadIdx.x; idx < 16 * per_row; idx += blockDim.x) {
+    const int n = idx / per_row, c = idx - n * per_row;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (n < count) v = *reinterpret_cast<const u32x4*>(rows_in + (size_t)n * kpad + c * VEC);
+    *reinterpret_cast<u32x4*>(lds + n * ldw + c * VEC) = v;
+  }
+}
+
 // z values of one tile for the lane's request (lane & 15) and entries
 // v0 + [0, 16), v0 = 64 t + 16 (lane >> 4); invalid entries get -inf.
 template <bool BF16>
@@ -362,6 +539,73 @@ __device__ __forceinline__ void block_tile_search(int n_t, float u, WFn wfn, Til
       }
       cum = cn;
     }
+    sh.tstar = found >= 0 ? found : (lastpos >= 0 ? lastpos : glast);
+    sh.pb = found >= 0 ? pbv : -INFINITY;
+  }
+  __syncthreads();
+}
+
+// The same search over weights a thread already holds in registers: w[i] is
+// the weight of tile t0 + i for i < cnt (cnt <= CMAX). Sums run in the same
+// order as block_tile_search, so both give the same bits.
+template <int CMAX>
+__device__ __forceinline__ void block_tile_search_regs(const float (&w)[CMAX], int t0, int cnt,
+                                                       float u, TileSearchShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nw = blockDim.x / kWave;
+  float ls = 0.0f;
+  int last = -1;
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i)
+    if (i < cnt) {
+      if (w[i] > 0.0f) last = t0 + i;
+      ls += w[i];
+    }
+  float incl = wave_inclusive_scan(ls, lane);
+  int wl = last;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wl = max(wl, __shfl_xor(wl, o, kWave));
+  if (lane == kWave - 1) sh.wsum[wave] = incl;
+  if (lane == 0) sh.wlast[wave] = wl;
+  __syncthreads();
+  float off = 0.0f;
+  for (int q = 0; q < wave; ++q) off += sh.wsum[q];
+  int glast = -1;
+  for (int q = 0; q < nw; ++q) glast = max(glast, sh.wlast[q]);
+  float S = 0.0f;
+  for (int q = 0; q < nw; ++q) S += sh.wsum[q];
+  const float T = u * S;
+  const float prev_in_wave = __shfl_up(incl, 1, kWave);
+  incl += off;
+  const float prev = (lane == 0) ? off : prev_in_wave + off;
+  const unsigned long long pm = __ballot(incl > T);
+  if (lane == 0) sh.wfirst[wave] = pm ? wave * kWave + __ffsll((long long)pm) - 1 : 0x7fffffff;
+  __syncthreads();
+  int pstar = 0x7fffffff;
+  for (int q = 0; q < nw; ++q) pstar = min(pstar, sh.wfirst[q]);
+  if (tid == 0) {
+    sh.S = S;
+    sh.T = T;
+    if (pstar == 0x7fffffff) {
+      sh.tstar = glast;
+      sh.pb = -INFINITY;
+    }
+  }
+  if (tid == pstar) {
+    float cum = prev;
+    int found = -1, lastpos = -1;
+    float pbv = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i)
+      if (i < cnt && found < 0) {
+        if (w[i] > 0.0f) lastpos = t0 + i;
+        const float cn = cum + w[i];
+        if (cn > T) {
+          found = t0 + i;
+          pbv = cum;
+        }
+        cum = cn;
+      }
     sh.tstar = found >= 0 ? found : (lastpos >= 0 ? lastpos : glast);
     sh.pb = found >= 0 ? pbv : -INFINITY;
   }

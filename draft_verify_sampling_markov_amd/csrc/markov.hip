@@ -23,6 +23,7 @@
 //                    finish the inverse-CDF search inside it.
 #include "dspark_device.hpp"
 #include "dspark_host.hpp"
+#include "tile_engine.hpp"
 
 #include <algorithm>
 
@@ -57,57 +58,58 @@ __global__ void prepack_w2_kernel(const T* __restrict__ W2, int r, int V, int KC
 // pass A: bias GEMM + U add + per-tile softmax partials
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int KC>
-__global__ __launch_bounds__(512) void markov_partials_kernel(
-    const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
+// Epilogue of the draft pass: z = bias + U_k, then the tile's softmax partial
+// (max, sum of exp(z - max)) per request, merged over the lane's four groups
+// in a fixed butterfly order. Lanes that must not write (other groups,
+// requests past R) store to a junk slot instead of branching.
+template <bool BF16, bool VEC>
+struct MarkovEpi {
+  typedef typename Elem<BF16>::T T;
+  typedef Raw16<BF16> Pre;
+  struct St {
+    const T* row;
+    int n;
+    bool active;
+  };
+  const T* U;
+  long long ldU;
+  int R, V;
+  float2* part;
+  int ldp;
+  float2* junk;
+
+  __device__ __forceinline__ St prepare(int n) const {
+    St s;
+    s.n = n;
+    s.active = n < R;
+    s.row = U + (size_t)min(n, R - 1) * ldU;
+    return s;
+  }
+  __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
+    load16_clamped<BF16, VEC>(s.row, v0, nvalid, V, p);
+  }
+  __device__ __forceinline__ void finish(const St& s, int v0, int nvalid, const f32x4 acc[4],
+                                         const Pre& p, int t, int lane) const {
+    float u16[16], z[16];
+    unpack16<BF16>(p, u16);
+    tile_logits<BF16>(acc, u16, nvalid, s.active, z);
+    float m, sm;
+    softmax16_merge4(z, m, sm);
+    float2* dst = ((lane >> 4) == 0 && s.active) ? part + (size_t)t * ldp + s.n : junk;
+    *dst = make_float2(m, sm);
+  }
+};
+
+template <bool BF16, int KC, int NW, int NB, bool VEC>
+__global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
+    const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
-    float2* __restrict__ part, int ldp) {
-  typedef typename Elem<BF16>::T T;
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* w1s = reinterpret_cast<T*>(smem);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
-  const int g = lane >> 4, nl = lane & 15;
-  constexpr int kpad = KC * kChunkK;
-  constexpr int ldw = kpad + kLdsPad;
-  const int rows = (R + 15) & ~15;
-
-  stage_rows<BF16>(W1, xprev, xstride, R, rows, r, V, kpad, ldw, w1s);
-  __syncthreads();
-
-  for (int t = blockIdx.x * nwaves + wave; t < n_t; t += gridDim.x * nwaves) {
-    ATile<BF16, KC> at;
-    load_a_tile<BF16, KC>(W2p, t, lane, at);
-    const int v0 = t * kTileV + 16 * g;
-    const int nvalid = min(16, V - v0);
-    for (int nb = 0; nb < rows; nb += kTileN) {
-      const int n = nb + nl;
-      const bool active = n < R;
-      float u16[16];
-      if (active && nvalid > 0) {
-        load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
-      }
-      f32x4 acc[4];
-      tile_mma<BF16, KC>(at, w1s + nb * ldw, ldw, lane, acc);
-      float z[16];
-      tile_logits<BF16>(acc, u16, nvalid, active, z);
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, z[i]);
-      float s = 0.0f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += __expf(z[i] - m);
-      }
-      softmax_merge(m, s, __shfl_xor(m, 16, kWave), __shfl_xor(s, 16, kWave));
-      softmax_merge(m, s, __shfl_xor(m, 32, kWave), __shfl_xor(s, 32, kWave));
-      if (g == 0 && active) part[(size_t)t * ldp + n] = make_float2(m, s);
-    }
-  }
+    float2* __restrict__ part, int ldp, float2* __restrict__ junk,
+    typename Elem<BF16>::T* __restrict__ w1g) {
+  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldp, junk};
+  run_tile_engine<BF16, KC, NW, NB>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; }, R, V,
+                                    r, n_t, epi, w1g, kTileOrder);
 }
 
 // ---------------------------------------------------------------------------
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(256) void markov_select_kernel(
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
     const float2* __restrict__ part, int ldp, uint64_t seed, uint64_t step,
     const uint32_t* __restrict__ req_ids, int k, int* __restrict__ tok_out,
-    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride) {
+    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride,
+    const typename Elem<BF16>::T* __restrict__ w1g) {
   typedef typename Elem<BF16>::T T;
   constexpr int kpad = KC * kChunkK;
   constexpr int ldw = kpad + kLdsPad;
@@ -134,29 +137,45 @@ __global__ __launch_bounds__(256) void markov_select_kernel(
   const int nb0 = n & ~(kTileN - 1);     // its 16-request matrix-core block
   const int q = n - nb0;
   const int count = min(kTileN, R - nb0);
-  stage_rows<BF16>(W1, xprev + (size_t)nb0 * xstride, xstride, count, 16, r, V, kpad, ldw, w1s);
+  // W1 rows of the 16-request block, as gathered (zero padded) by the GEMM
+  // pass of this slot when it exported them, else gathered here
+  if (w1g != nullptr) stage_gathered<BF16>(w1g + (size_t)nb0 * kpad, count, kpad, ldw, w1s);
+  else stage_rows<BF16>(W1, xprev + (size_t)nb0 * xstride, xstride, count, 16, r, V, kpad, ldw, w1s);
 
   // merge the per-tile partials: m = max_t m_t, w_t = s_t exp(m_t - m)
   const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
   const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
-  float lm = -INFINITY;
-  for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[(size_t)t * ldp + n].x);
-  const float m = block_max(lm, red);
   const float u = slot_uniform(seed, step, req_ids[n], k, kPurposeDraft);
-  block_tile_search(n_t, u, [&](int t) {
-    const float2 pv = part[(size_t)t * ldp + n];
-    return pv.y * __expf(pv.x - m);
-  }, ts);
+  float m;
+  constexpr int CMAX = 16;
+  if (c <= CMAX) {  // each thread's partials stay in registers
+    float2 pv[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i)
+      pv[i] = (t0 + i < t1) ? part[(size_t)(t0 + i) * ldp + n] : make_float2(-INFINITY, 0.0f);
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) lm = fmaxf(lm, pv[i].x);
+    m = block_max(lm, red);
+    float w[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) w[i] = (t0 + i < t1) ? pv[i].y * __expf(pv[i].x - m) : 0.0f;
+    block_tile_search_regs<CMAX>(w, t0, t1 - t0, u, ts);
+  } else {
+    float lm = -INFINITY;
+    for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[(size_t)t * ldp + n].x);
+    m = block_max(lm, red);
+    block_tile_search(n_t, u, [&](int t) {
+      const float2 pv = part[(size_t)t * ldp + n];
+      return pv.y * __expf(pv.x - m);
+    }, ts);
+  }
 
   // wave 0 recomputes the crossing tile and finishes the search in it
   if (tid >= kWave) return;  // no barrier below
   const int lane = tid;
   const int g = lane >> 4, nl = lane & 15;
   const int t = min(max(ts.tstar, 0), n_t - 1);
-  ATile<BF16, KC> at;
-  load_a_tile<BF16, KC>(W2p, t, lane, at);
-  f32x4 acc[4];
-  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
   const int v0 = t * kTileV + 16 * g;
   const int nvalid = min(16, V - v0);
   float u16[16];
@@ -166,6 +185,10 @@ __global__ __launch_bounds__(256) void markov_select_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
   }
+  ATile<BF16, KC> at;
+  load_a_tile<BF16, KC>(W2p, t, lane, at);
+  f32x4 acc[4];
+  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
   float z[16];
   tile_logits<BF16>(acc, u16, nvalid, true, z);
   // lane i takes entry v = 64 t + i from lane q + 16 (i / 16)
@@ -241,35 +264,61 @@ int device_cu_count() {
   return cache[dev];
 }
 
-size_t markov_ws_bytes(int R, int V) { return align_up((size_t)n_vtiles(V) * R * sizeof(float2), 256); }
+// Draft workspace: tile partials [ceil(V/64), R] (float2), one junk slot that
+// masked lanes write to, then the gathered W1 rows of the current slot's
+// previous tokens [R, 256] (room for 4-byte elements and the largest rank).
+static size_t markov_junk_offset(int R, int V) { return (size_t)n_vtiles(V) * R * sizeof(float2); }
+static size_t markov_w1g_offset(int R, int V) {
+  return align_up(markov_junk_offset(R, V) + 256, 256);
+}
+size_t markov_ws_bytes(int R, int V) {
+  return markov_w1g_offset(R, V) + align_up((size_t)R * kMaxRankBf16 * 4, 256);
+}
+
+template <bool BF16, int KC, int NW, int NB>
+static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
+                               const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
+                               const int32_t* xprev, int xstride, int Rg, int V, int r,
+                               float2* part, int ldp, float2* junk, typename Elem<BF16>::T* w1g,
+                               hipStream_t s) {
+  typedef EngineGeom<BF16, KC, NW> G;
+  const int n_t = n_vtiles(V);
+  const int per_cu = NW == 4 ? 2 : 1;
+  const int grid = std::max(1, std::min(n_t, device_cu_count() * per_cu));
+  if (vec)
+    hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
+                       G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, part, ldp,
+                       junk, w1g);
+  else
+    hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
+                       dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
+                       n_t, part, ldp, junk, w1g);
+  return launch_status();
+}
 
 template <bool BF16, int KC>
 static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                            const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                            const int32_t* xprev, int xstride, int R, int V, int r, float2* part,
-                           hipStream_t s) {
-  typedef typename Elem<BF16>::T T;
-  constexpr int ldw = KC * kChunkK + kLdsPad;
-  constexpr int threads = 512;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const size_t max_lds = (size_t)((kReqGroup + 15) & ~15) * ldw * sizeof(T);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_partials_kernel<BF16, KC>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds) != hipSuccess)
-      return DSPARK_EHIP;
-    attr_set = true;
-  }
-  const int n_t = n_vtiles(V);
-  const int ncu = device_cu_count();
+                           typename Elem<BF16>::T* w1g, hipStream_t s) {
+  constexpr int kpad = KC * kChunkK;
+  float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
   for (int g0 = 0; g0 < R; g0 += kReqGroup) {
     const int Rg = std::min(kReqGroup, R - g0);
-    const size_t lds = (size_t)((Rg + 15) & ~15) * ldw * sizeof(T);
-    const int per_cu = lds > 80 * 1024 ? 1 : 2;
-    const int grid = std::max(1, std::min(ceil_div(n_t, threads / kWave), ncu * per_cu));
-    hipLaunchKernelGGL((markov_partials_kernel<BF16, KC>), dim3(grid), dim3(threads), lds, s,
-                       Uk + (size_t)g0 * ldU, ldU, vec, W1, W2p, xprev + (size_t)g0 * xstride,
-                       xstride, Rg, V, r, n_t, part + g0, R);
-    const int st = launch_status();
+    const int blocks = ceil_div(Rg, kTileN);
+    const typename Elem<BF16>::T* Ug = Uk + (size_t)g0 * ldU;
+    const int32_t* xg = xprev + (size_t)g0 * xstride;
+    typename Elem<BF16>::T* wg = w1g ? w1g + (size_t)g0 * kpad : nullptr;
+    int st;
+    if (blocks <= 4)
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, part + g0,
+                                               R, junk, wg, s);
+    else if (blocks <= 8)
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, part + g0,
+                                               R, junk, wg, s);
+    else
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, part + g0,
+                                               R, junk, wg, s);
     if (st) return st;
   }
   return DSPARK_OK;
@@ -291,11 +340,13 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
     const int* xprev = (k == 1) ? anchor : tokens + (k - 2);
     const int xstride = (k == 1) ? 1 : gamma;
     const T* Uk = Ub + (size_t)(k - 1) * V;
-    int st = launch_partials<BF16, KC>(Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, part, s);
+    T* w1g = reinterpret_cast<T*>(reinterpret_cast<char*>(part) + markov_w1g_offset(R, V));
+    int st = launch_partials<BF16, KC>(Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, part, w1g, s);
     if (st) return st;
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
                        Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, n_t, part, R, seed, step,
-                       req_ids, k, tokens + (k - 1), p_draft + (k - 1), lse_draft + (k - 1), gamma);
+                       req_ids, k, tokens + (k - 1), p_draft + (k - 1), lse_draft + (k - 1), gamma,
+                       w1g);
     st = launch_status();
     if (st) return st;
   }
@@ -309,8 +360,9 @@ static int launch_partials_api(const void* U, long long ldU, const void* W1, con
   typedef typename Elem<BF16>::T T;
   const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
                    (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  T* w1g = reinterpret_cast<T*>(reinterpret_cast<char*>(part) + markov_w1g_offset(R, V));
   return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
-                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, s);
+                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, w1g, s);
 }
 
 template <bool BF16, int KC>
@@ -453,10 +505,12 @@ static int launch_select_api(const void* U, long long ldU, const void* W1, const
   typedef typename Elem<BF16>::T T;
   const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
                    (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  const T* w1g = reinterpret_cast<const T*>(reinterpret_cast<const char*>(part) +
+                                            markov_w1g_offset(R, V));
   hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
                      static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
                      static_cast<const T*>(W2p), x_prev, xstride, R, V, r, n_vtiles(V), part, R,
-                     seed, step, req_ids, k, tok, p, lse, ostride);
+                     seed, step, req_ids, k, tok, p, lse, ostride, w1g);
   return launch_status();
 }
 

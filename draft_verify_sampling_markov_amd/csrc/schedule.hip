@@ -15,9 +15,9 @@
 //
 // Everything is integer fixed point (survival quantised to 2^-20, Theta as a
 // uint64 product), so the result does not depend on the order in which the
-// workgroup's threads combine it. One workgroup: quantise, bitonic-sort the
-// R*gamma keys in LDS, integer prefix sums, Theta per K, reduction, window
-// counts.
+// workgroup's threads combine it. One workgroup: quantise, sort the R*gamma
+// keys in LDS (rank counting up to one key per thread, a bitonic network
+// beyond), integer prefix sums, Theta per K, reduction, window counts.
 //
 // Pack -- SGLang DSpark blog ("Ragged verify under full CUDA graphs"): windows
 // packed front to back into a cu_seqlens buffer, total rounded up to the
@@ -75,12 +75,45 @@ __device__ void bitonic_sort(unsigned long long* keys, int P) {
   }
 }
 
+// Sort the first N keys ascending. Keys are distinct (they carry their index).
+// Up to one key per thread: a key's position is the number of smaller keys,
+// counted in one pass over the array (LDS broadcast reads, eight in flight),
+// then a scatter through `scratch`. More keys: a bitonic network over the P
+// keys (padded with ~0).
+__device__ void sort_keys(unsigned long long* keys, unsigned long long* scratch, int N, int P) {
+  if (N <= (int)blockDim.x) {
+    const int i = threadIdx.x;
+    if (i < N) {
+      const unsigned long long mine = keys[i];
+      int rank = 0;
+      const int N8 = N & ~7;
+      for (int j = 0; j < N8; j += 8) {
+        unsigned long long kj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kj[u] = keys[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += kj[u] < mine;
+      }
+      for (int j = N8; j < N; ++j) rank += keys[j] < mine;
+      scratch[rank] = mine;
+    }
+    __syncthreads();
+    if (i < N) keys[i] = scratch[i];
+    __syncthreads();
+  } else {
+    bitonic_sort(keys, P);
+  }
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     const float* __restrict__ surv, const float* __restrict__ surv_budget,
     const uint32_t* __restrict__ sps, int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
     int* __restrict__ win_len, int* __restrict__ K_out) {
   __shared__ unsigned long long keys[kSchedMaxKeys];
-  __shared__ uint32_t pre[kSchedMaxKeys];  // inclusive prefix of sorted a_q; later window counts
+  __shared__ unsigned long long sort_scratch[kSchedMaxKeys];
+  // inclusive prefix of the sorted a_q, then window counts: reuses the sort
+  // scratch, which is dead once the sorted keys are back in `keys`
+  uint32_t* pre = reinterpret_cast<uint32_t*>(sort_scratch);
   __shared__ uint32_t wtot[kSchedThreads / kWave];
   __shared__ unsigned long long red_theta[kSchedThreads / kWave];
   __shared__ int red_k[kSchedThreads / kWave];
@@ -97,8 +130,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   if (mode == DSPARK_SCHED_FIXED) {
     K = min(max(K_fixed, 0), K_cap);
   } else {
+    // this thread's cost-table entries, fetched before the sort so the load
+    // overlaps it: sps[R + Kc] and sps[R + Kc + 1] for Kc = tid + i * threads
+    constexpr int kMaxPer = kSchedMaxKeys / kSchedThreads + 1;
+    uint32_t sp0[kMaxPer], sp1[kMaxPer];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int Kc = tid + i * (int)blockDim.x;
+      sp0[i] = Kc <= K_cap ? sps[R + Kc] : 0u;
+      sp1[i] = Kc < K_cap ? sps[R + Kc + 1] : 0u;
+    }
     build_keys(surv_budget ? surv_budget : surv, R, gamma, P, keys);
-    bitonic_sort(keys, P);
+    sort_keys(keys, sort_scratch, N, P);
     // inclusive prefix sums of the sorted a_q (each thread: 4 consecutive keys)
     const int per = (P + blockDim.x - 1) / blockDim.x;
     const int b0 = tid * per;
@@ -123,9 +166,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     // Theta_K = tau_K * sps[R + K], tau_K = R*2^20 + pre[K-1]
     unsigned long long best_t = 0;
     int best_k = 0x7fffffff;
-    for (int Kc = tid; Kc <= K_cap; Kc += blockDim.x) {
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int Kc = tid + i * (int)blockDim.x;
+      if (Kc > K_cap) continue;
       const unsigned long long tau = base + (Kc ? pre[Kc - 1] : 0u);
-      const unsigned long long th = tau * (unsigned long long)sps[R + Kc];
+      const unsigned long long th = tau * (unsigned long long)sp0[i];
       if (mode == DSPARK_SCHED_ARGMAX) {
         if (best_k == 0x7fffffff || th > best_t) {
           best_t = th;
@@ -133,7 +179,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
         }
       } else if (Kc < K_cap) {  // GREEDY: first K with Theta_{K+1} <= Theta_K
         const unsigned long long tau1 = base + pre[Kc];
-        const unsigned long long th1 = tau1 * (unsigned long long)sps[R + Kc + 1];
+        const unsigned long long th1 = tau1 * (unsigned long long)sp1[i];
         if (th1 <= th && Kc < best_k) best_k = Kc;
       }
     }
@@ -180,7 +226,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   // selection: the K best keys of the current survivals
   if (mode == DSPARK_SCHED_FIXED || surv_budget != nullptr) {
     build_keys(surv, R, gamma, P, keys);
-    bitonic_sort(keys, P);
+    sort_keys(keys, sort_scratch, N, P);
   }
   for (int i = tid; i < R; i += blockDim.x) pre[i] = 0u;
   __syncthreads();

@@ -1,0 +1,240 @@
+// Persistent, double-buffered engine for the Markov bias GEMM
+// [R, r] x [r, V] on the gfx950 matrix cores, shared by the draft pass and the
+// verify residual pass.
+//
+// Work split. A workgroup of NW waves walks a sequence of vocabulary tiles
+// (64 entries each): strided (blockIdx.x, + G, ..., G = gridDim.x) or a
+// contiguous range (make_tile_seq). The 16-request blocks
+// of its request group are dealt to the waves round-robin, NB per wave; a wave
+// keeps the gathered W1 rows of its blocks (the B operand) in registers for
+// the whole kernel. The pre-packed W2 tile (the A operand) is staged in LDS,
+// double buffered, and fetched two tiles ahead into two rotating register
+// sets; the epilogue's per-request rows (U, target) are also fetched two tiles
+// ahead. A workgroup thus keeps about two tiles of loads in flight while it
+// multiplies the current one. The steady-state loop is straight-line code:
+// prefetch addresses are clamped to valid tiles instead of guarded, so no
+// branch forces the compiler to drain the loads early. Every accumulator receives its rank chunks in increasing order,
+// exactly as tile_mma() in dspark_device.hpp does, so a later recompute of one
+// tile gives bit-identical logits.
+//
+// The epilogue policy supplies (all const, no branch around a load):
+//   struct St;                     // per-lane request state, set up once
+//   struct Pre;                    // prefetched per-lane rows of one tile
+//   St prepare(int n)              // request n of the lane (may be >= R)
+//   void load(const St&, int v0, int nvalid, Pre&)            // issue loads
+//   void finish(const St&, int v0, int nvalid, const f32x4 acc[4],
+//               const Pre&, int t, int lane)                  // consume, write
+#pragma once
+
+#include "dspark_device.hpp"
+
+namespace dspark {
+
+#ifndef DSPARK_TILE_ORDER
+#define DSPARK_TILE_ORDER 0
+#endif
+// 0: strided tile order; 1: contiguous ranges per workgroup
+constexpr int kTileOrder = DSPARK_TILE_ORDER;
+
+template <bool BF16, int KC, int NW>
+struct EngineGeom {
+  typedef typename Elem<BF16>::Frag Frag;
+  static constexpr int kTileFrags = KC * 4 * kWave;               // frags per W2 tile
+  static constexpr int kThreads = NW * kWave;
+  static constexpr int kPer = (kTileFrags + kThreads - 1) / kThreads;  // frags per thread
+  static constexpr size_t kLdsBytes = 2 * (size_t)kTileFrags * sizeof(Frag);
+  // fragment k of thread tid in a tile copy; when the tile has fewer
+  // fragments than threads, surplus threads repeat one (same value, same
+  // slot), which keeps the copy free of branches
+  static __device__ __forceinline__ int slot(int k, int tid) {
+    return (k * kThreads + tid) % kTileFrags;
+  }
+};
+
+// Gather the B operand (W1 rows of the wave's blocks) into registers.
+template <bool BF16, int KC, int NB, typename TokFn>
+__device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restrict__ W1, TokFn tok,
+                                         int R, int r, int V, int wave, int nw, int lane,
+                                         typename Elem<BF16>::Frag b[NB][KC]) {
+  typedef typename Elem<BF16>::T T;
+  typedef typename Elem<BF16>::Frag Frag;
+  constexpr int VEC = Elem<BF16>::kVec;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = (wave + nw * nb) * kTileN + (lane & 15);
+    const bool ok = n < R;
+    const T* row = W1 + (size_t)(ok ? clamp_token(tok(n), V) : 0) * r;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int k0 = kc * kChunkK + 8 * (lane >> 4);
+      Frag f;
+      if (ok && k0 + 8 <= r && (r % VEC) == 0) {
+        f = *reinterpret_cast<const Frag*>(row + k0);
+      } else {
+        T tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = (ok && k0 + e < r) ? row[k0 + e] : (T)0;
+        f = *reinterpret_cast<const Frag*>(tmp);
+      }
+      b[nb][kc] = f;
+    }
+  }
+}
+
+// The tiles a workgroup walks: tile(i) = base + i * step for i < count.
+struct TileSeq {
+  int base, step, count;
+  __device__ __forceinline__ int tile(int i) const { return base + min(i, count - 1) * step; }
+};
+
+// Strided (blockIdx.x, + G, + 2G, ...) when contig == 0; otherwise a
+// contiguous range of ceil or floor(n_t / G) tiles per workgroup.
+__device__ __forceinline__ TileSeq make_tile_seq(int n_t, int contig) {
+  const int G = gridDim.x, b = blockIdx.x;
+  TileSeq q;
+  if (!contig) {
+    q.base = b;
+    q.step = G;
+    q.count = b < n_t ? (n_t - 1 - b) / G + 1 : 0;
+  } else {
+    const int per = n_t / G, rem = n_t % G;
+    q.base = b * per + min(b, rem);
+    q.step = 1;
+    q.count = per + (b < rem ? 1 : 0);
+  }
+  return q;
+}
+
+// One step of the pipelined tile loop, straight-line code (no branch around
+// any load, so the compiler's in-order load counters let the prefetches stay
+// in flight): issue W2 of tile t2 into `w_issue`; multiply tile t out of `cur`;
+// hand the epilogue its rows for t (prefetched two steps ago into `u`); issue
+// the rows of t2 into `u`; store `w_ready` (W2 issued one step ago) into
+// `nxt`; barrier. t2 is the tile two steps ahead, clamped to the last one.
+template <bool BF16, int KC, int NW, int NB, class Epi>
+__device__ __forceinline__ void engine_step(
+    int t, int t2, int V, const typename Elem<BF16>::Frag* __restrict__ src,
+    const typename Elem<BF16>::Frag* cur, typename Elem<BF16>::Frag* nxt,
+    typename Elem<BF16>::Frag (&w_ready)[EngineGeom<BF16, KC, NW>::kPer],
+    typename Elem<BF16>::Frag (&w_issue)[EngineGeom<BF16, KC, NW>::kPer],
+    typename Epi::Pre (&u)[NB], const typename Elem<BF16>::Frag (&b)[NB][KC],
+    const typename Epi::St (&st)[NB], const Epi& epi) {
+  typedef EngineGeom<BF16, KC, NW> Geo;
+  typedef typename Elem<BF16>::Frag Frag;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int g = lane >> 4;
+  {
+    const Frag* s = src + (size_t)t2 * Geo::kTileFrags;
+#pragma unroll
+    for (int k = 0; k < Geo::kPer; ++k) w_issue[k] = s[Geo::slot(k, tid)];
+  }
+  f32x4 acc[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    Frag a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = cur[(kc * 4 + j) * kWave + lane];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma_step<BF16>(acc[nb][j], a[j], b[nb][kc]);
+  }
+  const int v0 = t * kTileV + 16 * g;
+  const int v0n = t2 * kTileV + 16 * g;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    epi.finish(st[nb], v0, min(16, V - v0), acc[nb], u[nb], t, lane);
+    epi.load(st[nb], v0n, min(16, V - v0n), u[nb]);
+  }
+#pragma unroll
+  for (int k = 0; k < Geo::kPer; ++k) nxt[Geo::slot(k, tid)] = w_ready[k];
+  __syncthreads();
+}
+
+// w1g_out (may be null): workgroup 0 writes the gathered W1 rows there, row n
+// at w1g_out + n * KC * 32 (zero padded), for a later kernel of the same step.
+template <bool BF16, int KC, int NW, int NB, class Epi, typename TokFn>
+__device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __restrict__ W1,
+                                                const typename Elem<BF16>::T* __restrict__ W2p,
+                                                TokFn tok, int R, int V, int r, int n_t,
+                                                const Epi& epi,
+                                                typename Elem<BF16>::T* __restrict__ w1g_out,
+                                                int contig) {
+  typedef EngineGeom<BF16, KC, NW> Geo;
+  typedef typename Elem<BF16>::Frag Frag;
+  extern __shared__ __align__(16) unsigned char smem[];
+  Frag* buf0 = reinterpret_cast<Frag*>(smem);
+  Frag* buf1 = buf0 + Geo::kTileFrags;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int g = lane >> 4, nl = lane & 15;
+  const Frag* src = reinterpret_cast<const Frag*>(W2p);
+  const TileSeq seq = make_tile_seq(n_t, contig);
+  if (seq.count <= 0) return;  // workgroup-uniform; no barrier passed yet
+
+  // prologue: tile 0 of the sequence into LDS, W2 of tile 1 and the rows of
+  // tiles 0 and 1 in flight; the first tile's loads go out before the
+  // (token -> W1 row) gather
+  Frag wA[Geo::kPer], wB[Geo::kPer];
+  typename Epi::Pre uA[NB], uB[NB];
+  const int t0 = seq.tile(0), t1 = seq.tile(1);
+  Frag first[Geo::kPer];
+  {
+    const Frag* s = src + (size_t)t0 * Geo::kTileFrags;
+#pragma unroll
+    for (int i = 0; i < Geo::kPer; ++i) first[i] = s[Geo::slot(i, tid)];
+  }
+  Frag b[NB][KC];
+  gather_b<BF16, KC, NB>(W1, tok, R, r, V, wave, NW, lane, b);
+  typename Epi::St st[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) st[nb] = epi.prepare((wave + NW * nb) * kTileN + nl);
+  if (w1g_out != nullptr && blockIdx.x == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = (wave + NW * nb) * kTileN + (lane & 15);
+      if (n < R) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          *reinterpret_cast<Frag*>(w1g_out + (size_t)n * (KC * kChunkK) + kc * kChunkK +
+                                   8 * (lane >> 4)) = b[nb][kc];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Geo::kPer; ++i) buf0[Geo::slot(i, tid)] = first[i];
+  {
+    const Frag* s = src + (size_t)t1 * Geo::kTileFrags;
+#pragma unroll
+    for (int i = 0; i < Geo::kPer; ++i) wA[i] = s[Geo::slot(i, tid)];
+  }
+  {
+    const int v0 = t0 * kTileV + 16 * g, v1 = t1 * kTileV + 16 * g;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      epi.load(st[nb], v0, min(16, V - v0), uA[nb]);
+      epi.load(st[nb], v1, min(16, V - v1), uB[nb]);
+    }
+  }
+  __syncthreads();
+
+  const int pairs = seq.count >> 1;
+  for (int p = 0; p < pairs; ++p) {
+    const int i = 2 * p;
+    engine_step<BF16, KC, NW, NB>(seq.tile(i), seq.tile(i + 2), V, src, buf0, buf1, wA, wB, uA, b,
+                                  st, epi);
+    engine_step<BF16, KC, NW, NB>(seq.tile(i + 1), seq.tile(i + 3), V, src, buf1, buf0, wB, wA, uB,
+                                  b, st, epi);
+  }
+  if (seq.count & 1) {
+    const int i = seq.count - 1;
+    engine_step<BF16, KC, NW, NB>(seq.tile(i), seq.tile(i), V, src, buf0, buf1, wA, wB, uA, b, st,
+                                  epi);
+  }
+}
+
+}  // namespace dspark

@@ -25,6 +25,7 @@
 //                     and finish the inverse-CDF search; write the token
 #include "dspark_device.hpp"
 #include "dspark_host.hpp"
+#include "tile_engine.hpp"
 
 #include <algorithm>
 
@@ -147,12 +148,24 @@ __global__ __launch_bounds__(256) void decide_kernel(
   bool acc = false;
   if (lane <= Lv) {
     const int row = c0 + lane;
-    float m = -INFINITY;
-    for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, part[(size_t)row * n_chunks + c].x);
-    float S = 0.0f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float2 pv = part[(size_t)row * n_chunks + c];
-      S += pv.y * __expf(pv.x - m);
+    float m = -INFINITY, S = 0.0f;
+    constexpr int CMAX = 32;
+    if (n_chunks <= CMAX) {  // all partials of the row in flight at once
+      float2 pv[CMAX];
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c)
+        pv[c] = c < n_chunks ? part[(size_t)row * n_chunks + c] : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c) m = fmaxf(m, pv[c].x);
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c)
+        if (c < n_chunks) S += pv[c].y * __expf(pv[c].x - m);
+    } else {
+      for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, part[(size_t)row * n_chunks + c].x);
+      for (int c = 0; c < n_chunks; ++c) {
+        const float2 pv = part[(size_t)row * n_chunks + c];
+        S += pv.y * __expf(pv.x - m);
+      }
     }
     lse = m + __logf(S);
     if (lane < Lv) {
@@ -239,66 +252,77 @@ __device__ __forceinline__ void load_corr_inputs(const typename Elem<BF16>::T* _
 // residual partials
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int KC>
-__global__ __launch_bounds__(512) void residual_partials_kernel(
-    const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
-    bool vec, const typename Elem<BF16>::T* __restrict__ W1,
-    const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int g0, int R, int gamma, int V,
-    int r, int n_t, float2* __restrict__ rpart, int ldp) {
+// Epilogue of the residual pass: per entry q = max(0, p_t - p_d) (or p_t for
+// a bonus job) and p_t, summed per tile and request. The job fields are read
+// once per kernel (prepare); a bonus job reads its target row in place of the
+// U row, so the loads need no branch.
+template <bool BF16, bool VEC>
+struct ResidualEpi {
   typedef typename Elem<BF16>::T T;
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* w1s = reinterpret_cast<T*>(smem);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
-  const int g = lane >> 4, nl = lane & 15;
-  constexpr int kpad = KC * kChunkK;
-  constexpr int ldw = kpad + kLdsPad;
-  const int rows = (R + 15) & ~15;
-  stage_rows<BF16>(W1, jobs.xprev + g0, 1, R, rows, r, V, kpad, ldw, w1s);
-  __syncthreads();
-  for (int t = blockIdx.x * nwaves + wave; t < n_t; t += gridDim.x * nwaves) {
-    ATile<BF16, KC> at;
-    load_a_tile<BF16, KC>(W2p, t, lane, at);
-    const int v0 = t * kTileV + 16 * g;
-    const int nvalid = min(16, V - v0);
-    for (int nb = 0; nb < rows; nb += kTileN) {
-      const int nloc = nb + nl;
-      const bool active = nloc < R;
-      const int n = g0 + nloc;
-      bool residual = false;
-      int trow = 0, dslot = 0;
-      float lse_t = 0.f, lse_d = 0.f;
-      float zt16[16], u16[16];
-      if (active) {
-        residual = jobs.kind[n] == 0;
-        trow = jobs.trow[n];
-        dslot = jobs.slot[n] - 1;
-        lse_t = jobs.lse_t[n];
-        lse_d = jobs.lse_d[n];
-      }
-      if (active && nvalid > 0) {
-        load_corr_inputs<BF16>(target, U, V, gamma, vec, n, v0, nvalid, trow, dslot, residual, zt16, u16);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) zt16[i] = u16[i] = 0.0f;
-      }
-      f32x4 acc[4];
-      tile_mma<BF16, KC>(at, w1s + nb * ldw, ldw, lane, acc);
-      float q[16], pt[16];
-      corr_tile_values<BF16>(acc, zt16, u16, (active ? nvalid : 0), lse_t, lse_d, residual, q, pt);
-      float sq = 0.0f, sp = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sq += q[i];
-        sp += pt[i];
-      }
-      sq += __shfl_xor(sq, 16, kWave);
-      sp += __shfl_xor(sp, 16, kWave);
-      sq += __shfl_xor(sq, 32, kWave);
-      sp += __shfl_xor(sp, 32, kWave);
-      if (g == 0 && active) rpart[(size_t)t * ldp + n] = make_float2(sq, sp);
-    }
+  struct Pre {
+    Raw16<BF16> zt, u;
+  };
+  struct St {
+    const T* trow;
+    const T* urow;
+    float lse_t, lse_d;
+    int ng;
+    bool residual, active;
+  };
+  const T* target;
+  const T* U;
+  int gamma, V, R, g0;
+  Jobs jobs;
+  float2* rpart;
+  int ldp;
+  float2* junk;
+
+  __device__ __forceinline__ St prepare(int n) const {
+    St s;
+    s.active = n < R;
+    s.ng = g0 + min(n, R - 1);
+    s.residual = jobs.kind[s.ng] == 0;
+    s.trow = target + (size_t)jobs.trow[s.ng] * V;
+    s.urow = s.residual ? U + ((size_t)s.ng * gamma + jobs.slot[s.ng] - 1) * V : s.trow;
+    s.lse_t = jobs.lse_t[s.ng];
+    s.lse_d = jobs.lse_d[s.ng];
+    return s;
   }
+  __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
+    load16_clamped<BF16, VEC>(s.trow, v0, nvalid, V, p.zt);
+    load16_clamped<BF16, VEC>(s.urow, v0, nvalid, V, p.u);
+  }
+  __device__ __forceinline__ void finish(const St& s, int v0, int nvalid, const f32x4 acc[4],
+                                         const Pre& p, int t, int lane) const {
+    float zt16[16], u16[16], q[16], pt[16];
+    unpack16<BF16>(p.zt, zt16);
+    unpack16<BF16>(p.u, u16);
+    corr_tile_values<BF16>(acc, zt16, u16, (s.active ? nvalid : 0), s.lse_t, s.lse_d, s.residual, q,
+                           pt);
+    float sq = 0.0f, sp = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sq += q[i];
+      sp += pt[i];
+    }
+    sq += __shfl_xor(sq, 16, kWave);
+    sp += __shfl_xor(sp, 16, kWave);
+    sq += __shfl_xor(sq, 32, kWave);
+    sp += __shfl_xor(sp, 32, kWave);
+    float2* dst = ((lane >> 4) == 0 && s.active) ? rpart + (size_t)t * ldp + s.ng : junk;
+    *dst = make_float2(sq, sp);
+  }
+};
+
+template <bool BF16, int KC, int NW, int NB, bool VEC>
+__global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
+    const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    Jobs jobs, int g0, int R, int gamma, int V, int r, int n_t, float2* __restrict__ rpart, int ldp,
+    float2* __restrict__ junk, typename Elem<BF16>::T* __restrict__ w1g) {
+  const ResidualEpi<BF16, VEC> epi{target, U, gamma, V, R, g0, jobs, rpart, ldp, junk};
+  run_tile_engine<BF16, KC, NW, NB>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V, r,
+                                    n_t, epi, w1g, kTileOrder);
 }
 
 // ---------------------------------------------------------------------------
@@ -310,7 +334,8 @@ __global__ __launch_bounds__(256) void residual_select_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     bool vec, const typename Elem<BF16>::T* __restrict__ W1,
     const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int R, int gamma, int V, int r,
-    int n_t, const float2* __restrict__ rpart, int ldp, int* __restrict__ out_tokens) {
+    int n_t, const float2* __restrict__ rpart, int ldp, int* __restrict__ out_tokens,
+    const typename Elem<BF16>::T* __restrict__ w1g) {
   typedef typename Elem<BF16>::T T;
   constexpr int kpad = KC * kChunkK;
   constexpr int ldw = kpad + kLdsPad;
@@ -322,19 +347,37 @@ __global__ __launch_bounds__(256) void residual_select_kernel(
   const int nb0 = n & ~(kTileN - 1);
   const int q = n - nb0;
   const int count = min(kTileN, R - nb0);
-  stage_rows<BF16>(W1, jobs.xprev + nb0, 1, count, 16, r, V, kpad, ldw, w1s);
+  // W1 rows of the jobs' previous tokens, as gathered by the residual pass
+  stage_gathered<BF16>(w1g + (size_t)nb0 * kpad, count, kpad, ldw, w1s);
 
   // residual mass left? (else draw from p_t)
   const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
   const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
-  float lq = 0.0f;
-  for (int t = t0; t < t1; ++t) lq += rpart[(size_t)t * ldp + n].x;
-  const float tq = block_sum(lq, red);
-  const bool use_pt = !(tq > 0.0f);
-  block_tile_search(n_t, jobs.u[n], [&](int t) {
-    const float2 pv = rpart[(size_t)t * ldp + n];
-    return use_pt ? pv.y : pv.x;
-  }, ts);
+  constexpr int CMAX = 16;
+  bool use_pt;
+  if (c <= CMAX) {  // each thread's partials stay in registers
+    float2 pv[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i)
+      pv[i] = (t0 + i < t1) ? rpart[(size_t)(t0 + i) * ldp + n] : make_float2(0.0f, 0.0f);
+    float lq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i)
+      if (t0 + i < t1) lq += pv[i].x;
+    use_pt = !(block_sum(lq, red) > 0.0f);
+    float w[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) w[i] = use_pt ? pv[i].y : pv[i].x;
+    block_tile_search_regs<CMAX>(w, t0, t1 - t0, jobs.u[n], ts);
+  } else {
+    float lq = 0.0f;
+    for (int t = t0; t < t1; ++t) lq += rpart[(size_t)t * ldp + n].x;
+    use_pt = !(block_sum(lq, red) > 0.0f);
+    block_tile_search(n_t, jobs.u[n], [&](int t) {
+      const float2 pv = rpart[(size_t)t * ldp + n];
+      return use_pt ? pv.y : pv.x;
+    }, ts);
+  }
 
   if (tid >= kWave) return;  // wave 0 finishes; no barrier below
   const int lane = tid;
@@ -380,6 +423,8 @@ __global__ __launch_bounds__(256) void residual_select_kernel(
 struct VerifyWs {
   float2* rowpart;
   float2* rpart;
+  float2* junk;  // write target of masked lanes
+  void* w1g;  // gathered W1 rows of the jobs' previous tokens [R, 256]
   Jobs jobs;
 };
 
@@ -394,12 +439,16 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
   };
   const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
   const size_t o_rp = take((size_t)n_vtiles(V) * R * sizeof(float2));
+  const size_t o_junk = take(256);
+  const size_t o_g = take((size_t)R * kMaxRankBf16 * 4);
   size_t o_j[7];
   for (int i = 0; i < 7; ++i) o_j[i] = take((size_t)R * 4);
   if (w && base) {
     char* b = static_cast<char*>(base);
     w->rowpart = reinterpret_cast<float2*>(b + o_row);
     w->rpart = reinterpret_cast<float2*>(b + o_rp);
+    w->junk = reinterpret_cast<float2*>(b + o_junk);
+    w->w1g = b + o_g;
     w->jobs.kind = reinterpret_cast<int*>(b + o_j[0]);
     w->jobs.slot = reinterpret_cast<int*>(b + o_j[1]);
     w->jobs.trow = reinterpret_cast<int*>(b + o_j[2]);
@@ -441,27 +490,34 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
                      req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
   st = launch_status();
   if (st) return st;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const size_t max_lds = (size_t)((kReqGroup + 15) & ~15) * ldw * sizeof(T);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&residual_partials_kernel<BF16, KC>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds) != hipSuccess)
-      return DSPARK_EHIP;
-    attr_set = true;
-  }
   const int ncu = device_cu_count();
   for (int g0 = 0; g0 < R; g0 += kReqGroup) {
     const int Rg = std::min(kReqGroup, R - g0);
-    const size_t lds = (size_t)((Rg + 15) & ~15) * ldw * sizeof(T);
-    const int per_cu = lds > 80 * 1024 ? 1 : 2;
-    const int grid = std::max(1, std::min(ceil_div(n_t, 8), ncu * per_cu));
-    hipLaunchKernelGGL((residual_partials_kernel<BF16, KC>), dim3(grid), dim3(512), lds, s, tg, Ub,
-                       vec, W1b, W2b, ws.jobs, g0, Rg, gamma, V, r, n_t, ws.rpart, R);
+    const int blocks = ceil_div(Rg, kTileN);
+    T* wg = static_cast<T*>(ws.w1g) + (size_t)g0 * kpad;
+#define DSPARK_RES_LAUNCH(NW_, NB_, PERCU)                                                         \
+    {                                                                                              \
+      typedef EngineGeom<BF16, KC, NW_> G;                                                         \
+      const dim3 grid(std::max(1, std::min(n_t, PERCU * ncu)));                                    \
+      if (vec)                                                                                     \
+        hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, true>), grid,             \
+                           dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
+                           gamma, V, r, n_t, ws.rpart, R, ws.junk, wg);                            \
+      else                                                                                         \
+        hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, false>), grid,            \
+                           dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
+                           gamma, V, r, n_t, ws.rpart, R, ws.junk, wg);                            \
+    }
+    if (blocks <= 4) DSPARK_RES_LAUNCH(4, 1, 2)
+    else if (blocks <= 8) DSPARK_RES_LAUNCH(8, 1, 1)
+    else DSPARK_RES_LAUNCH(8, 2, 1)
+#undef DSPARK_RES_LAUNCH
     st = launch_status();
     if (st) return st;
   }
   hipLaunchKernelGGL((residual_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
-                     tg, Ub, vec, W1b, W2b, ws.jobs, R, gamma, V, r, n_t, ws.rpart, R, out_tokens);
+                     tg, Ub, vec, W1b, W2b, ws.jobs, R, gamma, V, r, n_t, ws.rpart, R, out_tokens,
+                     static_cast<const T*>(ws.w1g));
   return launch_status();
 }
 
