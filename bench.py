@@ -48,6 +48,34 @@ def to_dev(arr):
     return torch.from_numpy(arr).cuda()
 
 
+PMC_SOURCES = ("draft_verify_sampling_markov_amd/csrc/markov.hip",
+               "draft_verify_sampling_markov_amd/csrc/tile_engine.hpp",
+               "draft_verify_sampling_markov_amd/csrc/dspark_device.hpp")
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per launch of the draft GEMM kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a 256 MiB copy), or
+    None when no summary exists for this workload or the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"markov_partials_{config_name}_static_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith(("|", "#", " ", "-")):
+            k, v = ln.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in PMC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(spec, inp, mode_name: str, budget_s: float = 12.0, n_req: int = 8):
     """The oracle as it stands, on the first n_req requests of the workload."""
     import numpy as np
@@ -189,7 +217,8 @@ def main() -> int:
     mfma_peak = MFMA_BF16_PEAK_TFS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFS
     roofline = {"kernel": "markov_partials_kernel (per-slot bias GEMM + U add + softmax partials)",
                 "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(spec.name),
                 "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(gemm_avg_ms * 1e3, 2),
                 "launches_timed": len(gemm_ms),
                 "mfma": {"achieved": round(achieved_tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
