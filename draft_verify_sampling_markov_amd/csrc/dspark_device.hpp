@@ -248,25 +248,80 @@ __device__ __forceinline__ float slot_uniform(uint64_t seed, uint64_t step, uint
 // wave reductions (fixed order, deterministic)
 // ---------------------------------------------------------------------------
 
+// Cross-lane steps use DPP row operations (gfx9-family encodings): the
+// quad permutes swap lanes 1 and 2 apart, the mirrors reverse a half-row / a
+// row, row_shr:n shifts within a 16-lane row, row_bcast:15 / :31 carry the
+// last lane of a row / of lanes 0-31 into the following rows, wave_shr:1
+// shifts the whole wave by one lane. Lanes a step does not write keep `old`.
+enum : int {
+  kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+  kDppRowShr1 = 0x111,
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppWaveShr1 = 0x138,
+  kDppRowMirror = 0x140,
+  kDppRowHalfMirror = 0x141,
+  kDppRowBcast15 = 0x142,
+  kDppRowBcast31 = 0x143,
+};
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Largest value over the 64 lanes, returned to every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v, v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast31, 0xC>(v, v));
+  return readlane_f(v, kWave - 1);
 }
+__device__ __forceinline__ int wave_max_int(int v) {
+  v = max(v, dpp_i<kDppXor1>(v, v));
+  v = max(v, dpp_i<kDppXor2>(v, v));
+  v = max(v, dpp_i<kDppRowHalfMirror>(v, v));
+  v = max(v, dpp_i<kDppRowMirror>(v, v));
+  v = max(v, dpp_i<kDppRowBcast15, 0xA>(v, v));
+  v = max(v, dpp_i<kDppRowBcast31, 0xC>(v, v));
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+// Sum over the 64 lanes in a fixed order, returned to every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v += dpp_f<kDppXor1>(0.0f, v);
+  v += dpp_f<kDppXor2>(0.0f, v);
+  v += dpp_f<kDppRowHalfMirror>(0.0f, v);
+  v += dpp_f<kDppRowMirror>(0.0f, v);
+  v += dpp_f<kDppRowBcast15, 0xA>(0.0f, v);
+  v += dpp_f<kDppRowBcast31, 0xC>(0.0f, v);
+  return readlane_f(v, kWave - 1);
+}
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele within rows, then the
+// row carries; fixed order).
+__device__ __forceinline__ float wave_inclusive_scan(float v, int /*lane*/) {
+  v += dpp_f<kDppRowShr1>(0.0f, v);
+  v += dpp_f<kDppRowShr2>(0.0f, v);
+  v += dpp_f<kDppRowShr4>(0.0f, v);
+  v += dpp_f<kDppRowShr8>(0.0f, v);
+  v += dpp_f<kDppRowBcast15, 0xA>(0.0f, v);
+  v += dpp_f<kDppRowBcast31, 0xC>(0.0f, v);
   return v;
 }
-// Inclusive prefix sum over the 64 lanes (Hillis-Steele; fixed order).
-__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
+// The value of the previous lane (0 for lane 0).
+__device__ __forceinline__ float wave_shift_up1(float v) { return dpp_f<kDppWaveShr1>(0.0f, v); }
 
 // Merge two (max, sum of exp(z - max)) softmax partials.
 __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
@@ -385,63 +440,6 @@ __device__ __forceinline__ void stage_rows(const typename Elem<BF16>::T* __restr
   }
 }
 
-// The same staging split in two: load the W1 rows of up to 16 requests into
-// registers (each thread at most 4 vectors of 16 bytes), later store them into
-// LDS, so the loads overlap other work. Needs r a multiple of the vector width
-// and (16 * (KC * 32 / VEC)) <= 4 * blockDim.x.
-template <bool BF16, int KC>
-struct W1Stage {
-  u32x4 v[4];
-};
-
-template <bool BF16, int KC>
-__device__ __forceinline__ void w1_stage_load(const typename Elem<BF16>::T* __restrict__ W1,
-                                              const int* __restrict__ xprev, int xstride, int count,
-                                              int r, int V, W1Stage<BF16, KC>& st) {
-  constexpr int VEC = Elem<BF16>::kVec;
-  constexpr int per_row = KC * kChunkK / VEC;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * (int)blockDim.x + (int)threadIdx.x;
-    const int n = idx / per_row, c = idx - n * per_row;
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (n < count && c * VEC < r) {
-      const int tok = clamp_token(xprev[(size_t)n * xstride], V);
-      val = *reinterpret_cast<const u32x4*>(W1 + (size_t)tok * r + c * VEC);
-    }
-    st.v[i] = val;
-  }
-}
-
-template <bool BF16, int KC>
-__device__ __forceinline__ void w1_stage_store(const W1Stage<BF16, KC>& st, int ldw,
-                                               typename Elem<BF16>::T* lds) {
-  constexpr int VEC = Elem<BF16>::kVec;
-  constexpr int per_row = KC * kChunkK / VEC;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * (int)blockDim.x + (int)threadIdx.x;
-    const int n = idx / per_row, c = idx - n * per_row;
-    if (n < 16) *reinterpret_cast<u32x4*>(lds + n * ldw + c * VEC) = st.v[i];
-  }
-}
-
-// Stage `count` gathered rows (kpad elements each, contiguous, already zero
-// padded) into LDS rows of ldw elements; rows count..15 are zero.
-template <bool BF16>
-__device__ __forceinline__ void stage_gathered(const typename Elem<BF16>::T* __restrict__ rows_in,
-                                               int count, int kpad, int ldw,
-                                               typename Elem<BF16>::T* lds) {
-  constexpr int VEC = Elem<BF16>::kVec;
-  const int per_row = kpad / VEC;
-  for (int idx = threadIdx.x; idx < 16 * per_row; idx += blockDim.x) {
-    const int n = idx / per_row, c = idx - n * per_row;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (n < count) v = *reinterpret_cast<const u32x4*>(rows_in + (size_t)n * kpad + c * VEC);
-    *reinterpret_cast<u32x4*>(lds + n * ldw + c * VEC) = v;
-  }
-}
-
 // z values of one tile for the lane's request (lane & 15) and entries
 // v0 + [0, 16), v0 = 64 t + 16 (lane >> 4); invalid entries get -inf.
 template <bool BF16>
@@ -460,183 +458,201 @@ __device__ __forceinline__ void tile_logits(const f32x4 acc[4], const float u16[
 
 
 // ---------------------------------------------------------------------------
-// block-wide inverse-CDF tile search
+// workgroup inverse-CDF tile search
 // ---------------------------------------------------------------------------
 //
-// One workgroup per request. Thread p owns tiles [p c, (p+1) c) of the n_t
-// per-tile weights w_t = wfn(t) (c = ceil(n_t / threads)). The workgroup
-// forms S = sum_t w_t (thread-local sums in tile order, then a fixed-order
-// scan over threads) and T = u S, finds the first thread whose inclusive
-// prefix exceeds T, and that thread walks its tiles to the first one where the
-// cumulative weight crosses T. Result: the crossing tile and the cumulative
-// weight before it (pb). When rounding leaves no crossing, the result is the
-// last tile with positive weight and pb = -inf, which makes the in-tile search
-// end at its last positive entry.
+// One workgroup of kSelThreads threads per request. Thread p owns the c
+// consecutive tiles [p c, p c + cnt) (cnt <= c; c = ceil(n_t / kSelThreads))
+// with weights w(i), i < cnt. The group forms S = sum of all weights (thread
+// sums in tile order, a fixed-order scan over the lanes of each wave, then the
+// wave totals in wave order) and T = u S, finds the first thread whose
+// inclusive prefix exceeds T, and that thread walks its tiles to the first one
+// where the running sum crosses T. Result (in every thread): the crossing
+// tile and the mass before it (pb). When rounding leaves no crossing, the
+// result is the last tile with positive weight and pb = -inf, which makes the
+// in-tile search end at that tile's last positive entry. CMAX > 0: the
+// weights sit in registers (w(i) is called with compile-time i < CMAX);
+// CMAX == 0: a rolled loop (weights re-read).
 
-struct TileSearchShared {
-  float wsum[16];
-  int wfirst[16];
-  int wlast[16];
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+struct WaveSearch {
   int tstar;
   float pb, S, T;
 };
 
-template <typename WFn>
-__device__ __forceinline__ void block_tile_search(int n_t, float u, WFn wfn, TileSearchShared& sh) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int nw = blockDim.x / kWave;
-  const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
-  float ls = 0.0f;
-  int last = -1;
-  for (int t = t0; t < t1; ++t) {
-    const float w = wfn(t);
-    if (w > 0.0f) last = t;
-    ls += w;
-  }
-  float incl = wave_inclusive_scan(ls, lane);
-  int wl = last;
+struct BlockSearchShared {
+  float red[kSelWaves];
+  float wsum[kSelWaves];
+  int wlast[kSelWaves];
+  int wfirst[kSelWaves];
+  int tstar;
+  float pb;
+};
+
+// Largest value over the workgroup (every thread gets it); one barrier.
+__device__ __forceinline__ float block_max(float v, BlockSearchShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  v = wave_max(v);
+  if (lane == 0) sh.red[wave] = v;
+  __syncthreads();
+  float m = sh.red[0];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wl = max(wl, __shfl_xor(wl, o, kWave));
-  if (lane == kWave - 1) sh.wsum[wave] = incl;
-  if (lane == 0) sh.wlast[wave] = wl;
-  __syncthreads();
-  float off = 0.0f;
-  for (int w = 0; w < wave; ++w) off += sh.wsum[w];
-  int glast = -1;
-  for (int w = 0; w < nw; ++w) glast = max(glast, sh.wlast[w]);
-  float S = 0.0f;  // same order as the offsets: the last thread's prefix is S
-  for (int w = 0; w < nw; ++w) S += sh.wsum[w];
-  const float T = u * S;
-  const float prev_in_wave = __shfl_up(incl, 1, kWave);
-  incl += off;
-  const float prev = (lane == 0) ? off : prev_in_wave + off;
-  const unsigned long long pm = __ballot(incl > T);
-  if (lane == 0) sh.wfirst[wave] = pm ? wave * kWave + __ffsll((long long)pm) - 1 : 0x7fffffff;
-  __syncthreads();
-  int pstar = 0x7fffffff;
-  for (int w = 0; w < nw; ++w) pstar = min(pstar, sh.wfirst[w]);
-  if (tid == 0) {
-    sh.S = S;
-    sh.T = T;
-    if (pstar == 0x7fffffff) {
-      sh.tstar = glast;
-      sh.pb = -INFINITY;
-    }
-  }
-  if (tid == pstar) {
-    float cum = prev;
-    int found = -1, lastpos = -1;
-    float pbv = -INFINITY;
-    for (int t = t0; t < t1; ++t) {
-      const float w = wfn(t);
-      if (w > 0.0f) lastpos = t;
-      const float cn = cum + w;
-      if (cn > T) {
-        found = t;
-        pbv = cum;
-        break;
-      }
-      cum = cn;
-    }
-    sh.tstar = found >= 0 ? found : (lastpos >= 0 ? lastpos : glast);
-    sh.pb = found >= 0 ? pbv : -INFINITY;
-  }
-  __syncthreads();
+  for (int q = 1; q < kSelWaves; ++q) m = fmaxf(m, sh.red[q]);
+  return m;
 }
 
-// The same search over weights a thread already holds in registers: w[i] is
-// the weight of tile t0 + i for i < cnt (cnt <= CMAX). Sums run in the same
-// order as block_tile_search, so both give the same bits.
-template <int CMAX>
-__device__ __forceinline__ void block_tile_search_regs(const float (&w)[CMAX], int t0, int cnt,
-                                                       float u, TileSearchShared& sh) {
+// Sum over the workgroup in a fixed order (every thread gets it); one barrier.
+__device__ __forceinline__ float block_sum(float v, BlockSearchShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  v = wave_sum(v);
+  if (lane == 0) sh.red[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kSelWaves; ++q) s += sh.red[q];
+  return s;
+}
+
+template <int CMAX, typename WFn>
+__device__ __forceinline__ WaveSearch block_tile_search(WFn w, int t0, int cnt, float u,
+                                                        BlockSearchShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int nw = blockDim.x / kWave;
   float ls = 0.0f;
   int last = -1;
+  if constexpr (CMAX > 0) {
 #pragma unroll
-  for (int i = 0; i < CMAX; ++i)
-    if (i < cnt) {
-      if (w[i] > 0.0f) last = t0 + i;
-      ls += w[i];
+    for (int i = 0; i < CMAX; ++i)
+      if (i < cnt) {
+        const float wi = w(i);
+        if (wi > 0.0f) last = t0 + i;
+        ls += wi;
+      }
+  } else {
+    for (int i = 0; i < cnt; ++i) {
+      const float wi = w(i);
+      if (wi > 0.0f) last = t0 + i;
+      ls += wi;
     }
+  }
   float incl = wave_inclusive_scan(ls, lane);
-  int wl = last;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wl = max(wl, __shfl_xor(wl, o, kWave));
+  const int wl = wave_max_int(last);
   if (lane == kWave - 1) sh.wsum[wave] = incl;
   if (lane == 0) sh.wlast[wave] = wl;
   __syncthreads();
-  float off = 0.0f;
-  for (int q = 0; q < wave; ++q) off += sh.wsum[q];
+  float off = 0.0f, S = 0.0f;
   int glast = -1;
-  for (int q = 0; q < nw; ++q) glast = max(glast, sh.wlast[q]);
-  float S = 0.0f;
-  for (int q = 0; q < nw; ++q) S += sh.wsum[q];
-  const float T = u * S;
-  const float prev_in_wave = __shfl_up(incl, 1, kWave);
+#pragma unroll
+  for (int q = 0; q < kSelWaves; ++q) {
+    if (q < wave) off += sh.wsum[q];
+    S += sh.wsum[q];
+    glast = max(glast, sh.wlast[q]);
+  }
+  WaveSearch r;
+  r.S = S;
+  r.T = u * S;
+  const float prev = wave_shift_up1(incl) + off;
   incl += off;
-  const float prev = (lane == 0) ? off : prev_in_wave + off;
-  const unsigned long long pm = __ballot(incl > T);
+  const unsigned long long pm = __ballot(incl > r.T);
   if (lane == 0) sh.wfirst[wave] = pm ? wave * kWave + __ffsll((long long)pm) - 1 : 0x7fffffff;
   __syncthreads();
   int pstar = 0x7fffffff;
-  for (int q = 0; q < nw; ++q) pstar = min(pstar, sh.wfirst[q]);
-  if (tid == 0) {
-    sh.S = S;
-    sh.T = T;
-    if (pstar == 0x7fffffff) {
-      sh.tstar = glast;
-      sh.pb = -INFINITY;
-    }
+#pragma unroll
+  for (int q = 0; q < kSelWaves; ++q) pstar = min(pstar, sh.wfirst[q]);
+  if (pstar == 0x7fffffff) {
+    r.tstar = glast;
+    r.pb = -INFINITY;
+    return r;  // uniform over the workgroup: no barrier follows on this path
   }
   if (tid == pstar) {
-    float cum = prev;
-    int found = -1, lastpos = -1;
-    float pbv = -INFINITY;
+    float cum = prev, pbv = -INFINITY;
+    int found = -1;
+    if constexpr (CMAX > 0) {
 #pragma unroll
-    for (int i = 0; i < CMAX; ++i)
-      if (i < cnt && found < 0) {
-        if (w[i] > 0.0f) lastpos = t0 + i;
-        const float cn = cum + w[i];
-        if (cn > T) {
+      for (int i = 0; i < CMAX; ++i)
+        if (i < cnt) {
+          const float cn = cum + w(i);
+          if (found < 0 && cn > r.T) {
+            found = t0 + i;
+            pbv = cum;
+          }
+          cum = cn;
+        }
+    } else {
+      for (int i = 0; i < cnt && found < 0; ++i) {
+        const float cn = cum + w(i);
+        if (cn > r.T) {
           found = t0 + i;
           pbv = cum;
         }
         cum = cn;
       }
-    sh.tstar = found >= 0 ? found : (lastpos >= 0 ? lastpos : glast);
+    }
+    sh.tstar = found >= 0 ? found : (last >= 0 ? last : glast);
     sh.pb = found >= 0 ? pbv : -INFINITY;
   }
   __syncthreads();
+  r.tstar = sh.tstar;
+  r.pb = sh.pb;
+  return r;
 }
 
-// Largest value of v over the workgroup (fixed order).
-__device__ __forceinline__ float block_max(float v, float* red) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  v = wave_max(v);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float m = red[0];
-  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
-  __syncthreads();
-  return m;
+// B operand of a tile product whose 16 columns all hold one W1 row: lane l
+// holds ranks kc*32 + 8 (l/16) .. +8 of `row` for every chunk kc (zero past r).
+// VW: row 16-byte aligned and r a multiple of 8 (one vector load per chunk).
+// Both paths are branch-free (clamped addresses, masked values), so the loads
+// of all chunks stay in flight together.
+template <bool BF16, int KC, bool VW>
+__device__ __forceinline__ void load_b_row(const typename Elem<BF16>::T* __restrict__ row, int r,
+                                           int lane, typename Elem<BF16>::Frag b[KC]) {
+  typedef typename Elem<BF16>::T T;
+  typedef typename Elem<BF16>::Frag Frag;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const int k0 = kc * kChunkK + 8 * (lane >> 4);
+    if constexpr (VW) {
+      const Frag f = *reinterpret_cast<const Frag*>(row + min(k0, r - 8));
+      b[kc] = k0 < r ? f : Frag{};
+    } else {
+      T tmp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const T v = row[min(k0 + e, r - 1)];
+        tmp[e] = (k0 + e < r) ? v : (T)0;
+      }
+      b[kc] = *reinterpret_cast<const Frag*>(tmp);
+    }
+  }
 }
 
-// Sum over the workgroup (fixed order).
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  v = wave_sum(v);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float s = 0.0f;
-  for (int w = 0; w < nw; ++w) s += red[w];
-  __syncthreads();
-  return s;
+// acc[j] = W2-tile x B over all rank chunks, B held in registers; the same
+// accumulation order as tile_mma() and the GEMM engine.
+template <bool BF16, int KC>
+__device__ __forceinline__ void tile_mma_regs(const ATile<BF16, KC>& at,
+                                              const typename Elem<BF16>::Frag (&b)[KC],
+                                              f32x4 acc[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mma_step<BF16>(acc[j], at.a[kc][j], b[kc]);
 }
+
+// Entry `idx` (0..15) of a lane's 16 values, without dynamic register indexing.
+__device__ __forceinline__ float pick16(const float v[16], int idx) {
+  float r = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) r = idx == i ? v[i] : r;
+  return r;
+}
+
+// Position of tile t's partial in a request's partial row, chunked for the
+// select workgroup: thread p's tiles [p c, p c + c) load as c coalesced
+// workgroup-wide reads, tile p c + i at i * kSelThreads + p. Rows hold
+// kSelThreads * c partials.
+__device__ __forceinline__ int part_pos(int t, int c) { return (t % c) * kSelThreads + t / c; }
 
 // In-tile inverse-CDF search by one wave: lane i holds weight e_i of entry
 // v = 64 t + i (0 outside the vocabulary). Returns the lane of the first entry

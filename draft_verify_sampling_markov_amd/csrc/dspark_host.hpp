@@ -14,7 +14,7 @@ constexpr int kMaxRows = 4096;      // R * (gamma + 1)
 constexpr int kMaxRankBf16 = 256;
 constexpr int kMaxRankF32 = 128;
 constexpr int kMaxTiers = 32;
-constexpr int kReqGroup = 256;      // requests whose W1 rows share one LDS stage
+constexpr int kReqGroup = 256;      // requests whose W1 rows one GEMM launch holds
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -26,6 +26,21 @@ inline int kc_instance(int r) {
   return kc <= 1 ? 1 : kc <= 2 ? 2 : kc <= 4 ? 4 : 8;
 }
 inline int n_vtiles(int V) { return ceil_div(V, 64); }
+// Request-major tile partial rows: c = ceil(n_t / 256) tiles per thread of the
+// 256-thread select workgroup, rows of 256 c partials (tile t at
+// part_pos(t, c), see dspark_device.hpp).
+constexpr int kSelThreadsHost = 256;
+inline int part_chunk(int V) { return ceil_div(n_vtiles(V), kSelThreadsHost); }
+inline int part_ld(int V) { return kSelThreadsHost * part_chunk(V); }
+
+// Vector paths: rows 16-byte aligned with V and the row stride multiples of
+// the vector width; W1 16-byte aligned with r a multiple of 8.
+inline bool rows_vec_ok(const void* p, long long ld, int V, int vec_elems) {
+  return (V % vec_elems) == 0 && (ld % vec_elems) == 0 && (reinterpret_cast<uintptr_t>(p) % 16) == 0;
+}
+inline bool w1_vec_ok(const void* W1, int r) {
+  return (r % 8) == 0 && (reinterpret_cast<uintptr_t>(W1) % 16) == 0;
+}
 
 inline bool dtype_ok(int dt) { return dt == DSPARK_F32 || dt == DSPARK_BF16; }
 inline size_t dtype_bytes(int dt) { return dt == DSPARK_BF16 ? 2 : 4; }

@@ -10,17 +10,17 @@
 // optimisation and zero-overhead scheduling") fuses this sampling path into
 // kernels; here it is two launches per slot:
 //
-//   markov_partials  the [R, r] x [r, V] bias GEMM on the matrix cores, with
-//                    W2 tiles streamed straight into registers (pre-packed
-//                    operand order) and the R gathered W1 rows staged in LDS;
-//                    each 64-entry vocabulary tile adds U_k and emits a softmax
-//                    partial (max, sum of exp) per request -- the [R, V]
-//                    logits never reach memory;
-//   markov_select    per request: merge the partials into (m, S), draw
-//                    u * S with the slot's Philox uniform, find the tile where
-//                    the cumulative mass crosses it, recompute that one tile
-//                    with the same matrix-core code (bit-identical logits) and
-//                    finish the inverse-CDF search inside it.
+//   markov_partials  the [R, r] x [r, V] bias GEMM on the matrix cores
+//                    (tile_engine.hpp: W2 tiles staged through LDS, the
+//                    gathered W1 rows held in registers); each 64-entry
+//                    vocabulary tile adds U_k and emits a softmax partial
+//                    (max, sum of exp) per request -- the [R, V] logits never
+//                    reach memory;
+//   markov_select    one workgroup per request: merge the partials into (m, S),
+//                    draw u * S with the slot's Philox uniform, find the tile
+//                    where the cumulative mass crosses it, recompute that one
+//                    tile with the same matrix-core code (bit-identical
+//                    logits) and finish the inverse-CDF search inside it.
 #include "dspark_device.hpp"
 #include "dspark_host.hpp"
 #include "tile_engine.hpp"
@@ -60,8 +60,9 @@ __global__ void prepack_w2_kernel(const T* __restrict__ W2, int r, int V, int KC
 
 // Epilogue of the draft pass: z = bias + U_k, then the tile's softmax partial
 // (max, sum of exp(z - max)) per request, merged over the lane's four groups
-// in a fixed butterfly order. Lanes that must not write (other groups,
-// requests past R) store to a junk slot instead of branching.
+// in a fixed butterfly order, stored at part[n * ldn + part_pos(t, c)]. Lanes
+// that must not write (other groups, requests past R) store to a junk slot
+// instead of branching.
 template <bool BF16, bool VEC>
 struct MarkovEpi {
   typedef typename Elem<BF16>::T T;
@@ -75,7 +76,7 @@ struct MarkovEpi {
   long long ldU;
   int R, V;
   float2* part;
-  int ldp;
+  int ldn, c;
   float2* junk;
 
   __device__ __forceinline__ St prepare(int n) const {
@@ -95,7 +96,7 @@ struct MarkovEpi {
     tile_logits<BF16>(acc, u16, nvalid, s.active, z);
     float m, sm;
     softmax16_merge4(z, m, sm);
-    float2* dst = ((lane >> 4) == 0 && s.active) ? part + (size_t)t * ldp + s.n : junk;
+    float2* dst = ((lane >> 4) == 0 && s.active) ? part + (size_t)s.n * ldn + part_pos(t, c) : junk;
     *dst = make_float2(m, sm);
   }
 };
@@ -105,109 +106,91 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
-    float2* __restrict__ part, int ldp, float2* __restrict__ junk,
-    typename Elem<BF16>::T* __restrict__ w1g) {
-  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldp, junk};
-  run_tile_engine<BF16, KC, NW, NB>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; }, R, V,
-                                    r, n_t, epi, w1g, kTileOrder);
+    float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk) {
+  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk};
+  run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
+                                         R, V, r, n_t, epi);
 }
 
 // ---------------------------------------------------------------------------
 // pass B: per-request draw
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int KC>
-__global__ __launch_bounds__(256) void markov_select_kernel(
+// One 256-thread workgroup per request. Thread p owns tiles [p c, p c + c) of
+// the request's partial row (CMAX >= c: held in registers; CMAX == 0:
+// re-read from memory). Wave 0 then recomputes the crossing tile with the W1
+// row it loaded at the start and finishes the draw.
+template <bool BF16, int KC, int CMAX, bool VW>
+__global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
-    const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
-    const float2* __restrict__ part, int ldp, uint64_t seed, uint64_t step,
+    const int* __restrict__ xprev, int xstride, int V, int r, int n_t,
+    const float2* __restrict__ part, int ldn, int c, uint64_t seed, uint64_t step,
     const uint32_t* __restrict__ req_ids, int k, int* __restrict__ tok_out,
-    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride,
-    const typename Elem<BF16>::T* __restrict__ w1g) {
-  typedef typename Elem<BF16>::T T;
-  constexpr int kpad = KC * kChunkK;
-  constexpr int ldw = kpad + kLdsPad;
-  __shared__ __align__(16) T w1s[16 * ldw];
-  __shared__ TileSearchShared ts;
-  __shared__ float red[16];
-
-  const int tid = threadIdx.x;
-  const int n = blockIdx.x;              // this workgroup's request
-  const int nb0 = n & ~(kTileN - 1);     // its 16-request matrix-core block
-  const int q = n - nb0;
-  const int count = min(kTileN, R - nb0);
-  // W1 rows of the 16-request block, as gathered (zero padded) by the GEMM
-  // pass of this slot when it exported them, else gathered here
-  if (w1g != nullptr) stage_gathered<BF16>(w1g + (size_t)nb0 * kpad, count, kpad, ldw, w1s);
-  else stage_rows<BF16>(W1, xprev + (size_t)nb0 * xstride, xstride, count, 16, r, V, kpad, ldw, w1s);
-
-  // merge the per-tile partials: m = max_t m_t, w_t = s_t exp(m_t - m)
-  const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
+    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride) {
+  typedef typename Elem<BF16>::Frag Frag;
+  __shared__ BlockSearchShared sh;
+  const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  const float2* prow = part + (size_t)n * ldn;
+  const int t0 = tid * c;
+  const int cnt = max(0, min(c, n_t - t0));
+  float2 pv[CMAX > 0 ? CMAX : 1];
+  if constexpr (CMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) pv[i] = prow[min(i, c - 1) * kSelThreads + tid];
+  }
+  // B operand (wave 0's): the W1 row of this request's previous token, in
+  // every column; every wave loads it, only wave 0 uses it
+  const int x = clamp_token(xprev[(size_t)n * xstride], V);
+  Frag b[KC];
+  load_b_row<BF16, KC, VW>(W1 + (size_t)x * r, r, lane, b);
+  // the Philox draw (scalar work) overlaps the loads in flight
   const float u = slot_uniform(seed, step, req_ids[n], k, kPurposeDraft);
   float m;
-  constexpr int CMAX = 16;
-  if (c <= CMAX) {  // each thread's partials stay in registers
-    float2 pv[CMAX];
-#pragma unroll
-    for (int i = 0; i < CMAX; ++i)
-      pv[i] = (t0 + i < t1) ? part[(size_t)(t0 + i) * ldp + n] : make_float2(-INFINITY, 0.0f);
+  WaveSearch ws;
+  if constexpr (CMAX > 0) {
     float lm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < CMAX; ++i) lm = fmaxf(lm, pv[i].x);
-    m = block_max(lm, red);
+    for (int i = 0; i < CMAX; ++i) lm = fmaxf(lm, i < cnt ? pv[i].x : -INFINITY);
+    m = block_max(lm, sh);
     float w[CMAX];
 #pragma unroll
-    for (int i = 0; i < CMAX; ++i) w[i] = (t0 + i < t1) ? pv[i].y * __expf(pv[i].x - m) : 0.0f;
-    block_tile_search_regs<CMAX>(w, t0, t1 - t0, u, ts);
+    for (int i = 0; i < CMAX; ++i) w[i] = i < cnt ? pv[i].y * __expf(pv[i].x - m) : 0.0f;
+    ws = block_tile_search<CMAX>([&](int i) { return w[i]; }, t0, cnt, u, sh);
   } else {
     float lm = -INFINITY;
-    for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[(size_t)t * ldp + n].x);
-    m = block_max(lm, red);
-    block_tile_search(n_t, u, [&](int t) {
-      const float2 pv = part[(size_t)t * ldp + n];
-      return pv.y * __expf(pv.x - m);
-    }, ts);
+    for (int i = 0; i < cnt; ++i) lm = fmaxf(lm, prow[i * kSelThreads + tid].x);
+    m = block_max(lm, sh);
+    ws = block_tile_search<0>([&](int i) {
+      const float2 q = prow[i * kSelThreads + tid];
+      return q.y * __expf(q.x - m);
+    }, t0, cnt, u, sh);
   }
+  if (tid >= kWave) return;  // wave 0 finishes; no barrier below
 
-  // wave 0 recomputes the crossing tile and finishes the search in it
-  if (tid >= kWave) return;  // no barrier below
-  const int lane = tid;
-  const int g = lane >> 4, nl = lane & 15;
-  const int t = min(max(ts.tstar, 0), n_t - 1);
+  // recompute the crossing tile; lane l gets entries 64 t + 16 (l/16) + [0, 16)
+  const int g = lane >> 4;
+  const int t = min(max(ws.tstar, 0), n_t - 1);
   const int v0 = t * kTileV + 16 * g;
   const int nvalid = min(16, V - v0);
-  float u16[16];
-  if (nl == q && nvalid > 0) {
-    load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
-  }
   ATile<BF16, KC> at;
   load_a_tile<BF16, KC>(W2p, t, lane, at);
+  float u16[16];
+  load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
   f32x4 acc[4];
-  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+  tile_mma_regs<BF16, KC>(at, b, acc);
   float z[16];
   tile_logits<BF16>(acc, u16, nvalid, true, z);
-  // lane i takes entry v = 64 t + i from lane q + 16 (i / 16)
-  const int src = q + 16 * (lane >> 4);
-  float zi = -INFINITY;
-#pragma unroll
-  for (int idx = 0; idx < 16; ++idx) {
-    const float val = __shfl(z[idx], src, kWave);
-    if ((lane & 15) == idx) zi = val;
-  }
-  const int v = t * kTileV + lane;
-  const bool valid = v < V;
+  // lane i takes tile entry i, which its own group holds at index i % 16
+  const float zi = pick16(z, lane & 15);
+  const bool valid = t * kTileV + lane < V;
   const float e = valid ? __expf(zi - m) : 0.0f;
-  const int sel = tile_pick(e, valid, ts.pb, ts.T, lane);
-  const float esel = __shfl(e, sel, kWave);
+  const int sel = tile_pick(e, valid, ws.pb, ws.T, lane);
+  const float esel = readlane_f(e, sel);
   if (lane == 0) {
     tok_out[(size_t)n * ostride] = t * kTileV + sel;
-    p_out[(size_t)n * ostride] = esel / ts.S;
-    lse_out[(size_t)n * ostride] = m + __logf(ts.S);
+    p_out[(size_t)n * ostride] = esel / ws.S;
+    lse_out[(size_t)n * ostride] = m + __logf(ws.S);
   }
 }
 
@@ -264,64 +247,91 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// Draft workspace: tile partials [ceil(V/64), R] (float2), one junk slot that
-// masked lanes write to, then the gathered W1 rows of the current slot's
-// previous tokens [R, 256] (room for 4-byte elements and the largest rank).
-static size_t markov_junk_offset(int R, int V) { return (size_t)n_vtiles(V) * R * sizeof(float2); }
-static size_t markov_w1g_offset(int R, int V) {
-  return align_up(markov_junk_offset(R, V) + 256, 256);
+// Draft workspace: the request-major tile partials [R, ldn] (float2,
+// ldn = 64 c, c = ceil(n_t / 64), tile t of request n at n * ldn +
+// part_pos(t, c)), then one junk slot that masked lanes write to.
+static size_t markov_junk_offset(int R, int V) {
+  return align_up((size_t)R * part_ld(V) * sizeof(float2), 256);
 }
-size_t markov_ws_bytes(int R, int V) {
-  return markov_w1g_offset(R, V) + align_up((size_t)R * kMaxRankBf16 * 4, 256);
+size_t markov_ws_bytes(int R, int V) { return markov_junk_offset(R, V) + 256; }
+
+template <bool BF16>
+static bool u_vec_ok(const void* U, long long ldU, int V) {
+  return rows_vec_ok(U, ldU, V, Elem<BF16>::kVec);
 }
 
 template <bool BF16, int KC, int NW, int NB>
 static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                                const int32_t* xprev, int xstride, int Rg, int V, int r,
-                               float2* part, int ldp, float2* junk, typename Elem<BF16>::T* w1g,
-                               hipStream_t s) {
+                               float2* part, float2* junk, hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
   const int per_cu = NW == 4 ? 2 : 1;
   const int grid = std::max(1, std::min(n_t, device_cu_count() * per_cu));
+  const int ldn = part_ld(V), c = part_chunk(V);
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
-                       G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, part, ldp,
-                       junk, w1g);
+                       G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, part, ldn,
+                       c, junk);
   else
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
                        dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
-                       n_t, part, ldp, junk, w1g);
+                       n_t, part, ldn, c, junk);
   return launch_status();
 }
 
+// One launch per group of up to 256 requests (the engine holds a group's W1
+// rows in registers).
 template <bool BF16, int KC>
 static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                            const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                            const int32_t* xprev, int xstride, int R, int V, int r, float2* part,
-                           typename Elem<BF16>::T* w1g, hipStream_t s) {
-  constexpr int kpad = KC * kChunkK;
+                           hipStream_t s) {
   float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
+  const int ldn = part_ld(V);
   for (int g0 = 0; g0 < R; g0 += kReqGroup) {
     const int Rg = std::min(kReqGroup, R - g0);
     const int blocks = ceil_div(Rg, kTileN);
     const typename Elem<BF16>::T* Ug = Uk + (size_t)g0 * ldU;
     const int32_t* xg = xprev + (size_t)g0 * xstride;
-    typename Elem<BF16>::T* wg = w1g ? w1g + (size_t)g0 * kpad : nullptr;
+    float2* pg = part + (size_t)g0 * ldn;
     int st;
     if (blocks <= 4)
-      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, part + g0,
-                                               R, junk, wg, s);
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
     else if (blocks <= 8)
-      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, part + g0,
-                                               R, junk, wg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
     else
-      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, part + g0,
-                                               R, junk, wg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
     if (st) return st;
   }
   return DSPARK_OK;
+}
+
+template <bool BF16, int KC>
+static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool vec, bool vec_w1,
+                         const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
+                         const int32_t* xprev, int xstride, int R, int V, int r,
+                         const float2* part, uint64_t seed, uint64_t step,
+                         const uint32_t* req_ids, int k, int32_t* tok, float* p, float* lse,
+                         int ostride, hipStream_t s) {
+  const int n_t = n_vtiles(V), c = part_chunk(V), ldn = part_ld(V);
+#define DSPARK_SELECT(CM)                                                                         \
+  if (vec_w1)                                                                                    \
+    hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, Uk, \
+                       ldU, vec, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed, step,    \
+                       req_ids, k, tok, p, lse, ostride);                                        \
+  else                                                                                           \
+    hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
+                       Uk, ldU, vec, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed,      \
+                       step, req_ids, k, tok, p, lse, ostride)
+  if (c <= 16) {
+    DSPARK_SELECT(16);
+  } else {
+    DSPARK_SELECT(0);
+  }
+#undef DSPARK_SELECT
+  return launch_status();
 }
 
 template <bool BF16, int KC>
@@ -333,21 +343,18 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
   const T* Ub = static_cast<const T*>(U);
   const T* W1b = static_cast<const T*>(W1);
   const T* W2b = static_cast<const T*>(W2p);
-  const int n_t = n_vtiles(V);
   const long long ldU = (long long)gamma * V;
-  const bool vec = (V % Elem<BF16>::kVec) == 0 && (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  const bool vec_u = u_vec_ok<BF16>(U, ldU, V), vec_w1 = w1_vec_ok(W1, r);
   for (int k = 1; k <= gamma; ++k) {
     const int* xprev = (k == 1) ? anchor : tokens + (k - 2);
     const int xstride = (k == 1) ? 1 : gamma;
     const T* Uk = Ub + (size_t)(k - 1) * V;
-    T* w1g = reinterpret_cast<T*>(reinterpret_cast<char*>(part) + markov_w1g_offset(R, V));
-    int st = launch_partials<BF16, KC>(Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, part, w1g, s);
+    int st = launch_partials<BF16, KC>(Uk, ldU, vec_u && vec_w1, W1b, W2b, xprev, xstride, R, V, r,
+                                       part, s);
     if (st) return st;
-    hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
-                       Uk, ldU, vec, W1b, W2b, xprev, xstride, R, V, r, n_t, part, R, seed, step,
-                       req_ids, k, tokens + (k - 1), p_draft + (k - 1), lse_draft + (k - 1), gamma,
-                       w1g);
-    st = launch_status();
+    st = launch_select<BF16, KC>(Uk, ldU, vec_u, vec_w1, W1b, W2b, xprev, xstride, R, V, r, part,
+                                 seed, step, req_ids, k, tokens + (k - 1), p_draft + (k - 1),
+                                 lse_draft + (k - 1), gamma, s);
     if (st) return st;
   }
   return DSPARK_OK;
@@ -358,11 +365,9 @@ static int launch_partials_api(const void* U, long long ldU, const void* W1, con
                                const int32_t* x_prev, int xstride, int R, int V, int r,
                                float2* part, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
-  const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
-                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
-  T* w1g = reinterpret_cast<T*>(reinterpret_cast<char*>(part) + markov_w1g_offset(R, V));
+  const bool vec = u_vec_ok<BF16>(U, ldU, V) && w1_vec_ok(W1, r);
   return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
-                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, w1g, s);
+                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, s);
 }
 
 template <bool BF16, int KC>
@@ -503,15 +508,10 @@ static int launch_select_api(const void* U, long long ldU, const void* W1, const
                              uint64_t step, const uint32_t* req_ids, int k, int R, int V, int r,
                              int32_t* tok, float* p, float* lse, int ostride, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
-  const bool vec = (V % Elem<BF16>::kVec) == 0 && (ldU % Elem<BF16>::kVec) == 0 &&
-                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
-  const T* w1g = reinterpret_cast<const T*>(reinterpret_cast<const char*>(part) +
-                                            markov_w1g_offset(R, V));
-  hipLaunchKernelGGL((markov_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
-                     static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
-                     static_cast<const T*>(W2p), x_prev, xstride, R, V, r, n_vtiles(V), part, R,
-                     seed, step, req_ids, k, tok, p, lse, ostride, w1g);
-  return launch_status();
+  return launch_select<BF16, KC>(static_cast<const T*>(U), ldU, u_vec_ok<BF16>(U, ldU, V),
+                                 w1_vec_ok(W1, r), static_cast<const T*>(W1),
+                                 static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, seed,
+                                 step, req_ids, k, tok, p, lse, ostride, s);
 }
 
 extern "C" int dspark_markov_select(const void* U_k, long long ldU, const void* W1,

@@ -2,20 +2,22 @@
 // [R, r] x [r, V] on the gfx950 matrix cores, shared by the draft pass and the
 // verify residual pass.
 //
-// Work split. A workgroup of NW waves walks a sequence of vocabulary tiles
-// (64 entries each): strided (blockIdx.x, + G, ..., G = gridDim.x) or a
-// contiguous range (make_tile_seq). The 16-request blocks
-// of its request group are dealt to the waves round-robin, NB per wave; a wave
-// keeps the gathered W1 rows of its blocks (the B operand) in registers for
-// the whole kernel. The pre-packed W2 tile (the A operand) is staged in LDS,
-// double buffered, and fetched two tiles ahead into two rotating register
-// sets; the epilogue's per-request rows (U, target) are also fetched two tiles
-// ahead. A workgroup thus keeps about two tiles of loads in flight while it
-// multiplies the current one. The steady-state loop is straight-line code:
-// prefetch addresses are clamped to valid tiles instead of guarded, so no
-// branch forces the compiler to drain the loads early. Every accumulator receives its rank chunks in increasing order,
-// exactly as tile_mma() in dspark_device.hpp does, so a later recompute of one
-// tile gives bit-identical logits.
+// Work split. A workgroup of NW waves walks a contiguous range of vocabulary
+// tiles (64 entries each). Ranges are laid out in XCD-major order: workgroup b
+// runs on XCD b % 8 (the dispatcher deals workgroups to the XCDs round-robin),
+// and the workgroups of one XCD take adjacent ranges, so each XCD's L2 sees
+// one contiguous stretch of the vocabulary and the per-request partial rows
+// are written mostly by one L2. The 16-request blocks of the request group
+// are dealt to the waves round-robin, NB per wave; a wave keeps the gathered
+// W1 rows of its blocks (the B operand) in registers for the whole kernel. The
+// pre-packed W2 tile (the A operand) is staged in LDS, double buffered, and
+// fetched two tiles ahead into two rotating register sets; the epilogue's
+// per-request rows (U, target) are also fetched two tiles ahead. The
+// steady-state loop is straight-line code: prefetch addresses are clamped to
+// valid tiles instead of guarded, so no branch forces the compiler to drain
+// the loads early. Every accumulator receives its rank chunks in increasing
+// order, exactly as tile_mma() / tile_mma_regs() in dspark_device.hpp do, so
+// a later recompute of one tile gives bit-identical logits.
 //
 // The epilogue policy supplies (all const, no branch around a load):
 //   struct St;                     // per-lane request state, set up once
@@ -30,11 +32,7 @@
 
 namespace dspark {
 
-#ifndef DSPARK_TILE_ORDER
-#define DSPARK_TILE_ORDER 0
-#endif
-// 0: strided tile order; 1: contiguous ranges per workgroup
-constexpr int kTileOrder = DSPARK_TILE_ORDER;
+constexpr int kNumXcd = 8;  // XCDs of an MI355X; only the tile order depends on it
 
 template <bool BF16, int KC, int NW>
 struct EngineGeom {
@@ -51,57 +49,53 @@ struct EngineGeom {
   }
 };
 
-// Gather the B operand (W1 rows of the wave's blocks) into registers.
-template <bool BF16, int KC, int NB, typename TokFn>
+// Gather the B operand (W1 rows of the wave's blocks) into registers. With
+// VEC (W1 16-byte aligned, r a multiple of 8) the loads are unconditional:
+// addresses are clamped into the row and out-of-range values zeroed after the
+// load, so the prologue has no branch that would drain the loads in flight.
+template <bool BF16, int KC, int NB, bool VEC, typename TokFn>
 __device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restrict__ W1, TokFn tok,
                                          int R, int r, int V, int wave, int nw, int lane,
                                          typename Elem<BF16>::Frag b[NB][KC]) {
   typedef typename Elem<BF16>::T T;
   typedef typename Elem<BF16>::Frag Frag;
-  constexpr int VEC = Elem<BF16>::kVec;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = (wave + nw * nb) * kTileN + (lane & 15);
     const bool ok = n < R;
-    const T* row = W1 + (size_t)(ok ? clamp_token(tok(n), V) : 0) * r;
+    const int x = clamp_token(tok(min(n, R - 1)), V);
+    const T* row = W1 + (size_t)x * r;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const int k0 = kc * kChunkK + 8 * (lane >> 4);
-      Frag f;
-      if (ok && k0 + 8 <= r && (r % VEC) == 0) {
-        f = *reinterpret_cast<const Frag*>(row + k0);
+      if constexpr (VEC) {
+        const Frag f = *reinterpret_cast<const Frag*>(row + min(k0, r - 8));
+        b[nb][kc] = (ok && k0 < r) ? f : Frag{};
       } else {
         T tmp[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) tmp[e] = (ok && k0 + e < r) ? row[k0 + e] : (T)0;
-        f = *reinterpret_cast<const Frag*>(tmp);
+        b[nb][kc] = *reinterpret_cast<const Frag*>(tmp);
       }
-      b[nb][kc] = f;
     }
   }
 }
 
-// The tiles a workgroup walks: tile(i) = base + i * step for i < count.
+// The tiles a workgroup walks: tile(i) = base + i for i < count.
 struct TileSeq {
-  int base, step, count;
-  __device__ __forceinline__ int tile(int i) const { return base + min(i, count - 1) * step; }
+  int base, count;
+  __device__ __forceinline__ int tile(int i) const { return base + min(i, count - 1); }
 };
 
-// Strided (blockIdx.x, + G, + 2G, ...) when contig == 0; otherwise a
-// contiguous range of ceil or floor(n_t / G) tiles per workgroup.
-__device__ __forceinline__ TileSeq make_tile_seq(int n_t, int contig) {
+// Workgroup b takes position p = (its XCD's first position) + b / 8 in
+// XCD-major order and the tiles [floor(p n_t / G), floor((p + 1) n_t / G)).
+__device__ __forceinline__ TileSeq make_tile_seq(int n_t) {
   const int G = gridDim.x, b = blockIdx.x;
+  const int x = b % kNumXcd, j = b / kNumXcd;
+  const int p = x * (G / kNumXcd) + min(x, G % kNumXcd) + j;
   TileSeq q;
-  if (!contig) {
-    q.base = b;
-    q.step = G;
-    q.count = b < n_t ? (n_t - 1 - b) / G + 1 : 0;
-  } else {
-    const int per = n_t / G, rem = n_t % G;
-    q.base = b * per + min(b, rem);
-    q.step = 1;
-    q.count = per + (b < rem ? 1 : 0);
-  }
+  q.base = (int)((long long)p * n_t / G);
+  q.count = (int)((long long)(p + 1) * n_t / G) - q.base;
   return q;
 }
 
@@ -155,15 +149,11 @@ __device__ __forceinline__ void engine_step(
   __syncthreads();
 }
 
-// w1g_out (may be null): workgroup 0 writes the gathered W1 rows there, row n
-// at w1g_out + n * KC * 32 (zero padded), for a later kernel of the same step.
-template <bool BF16, int KC, int NW, int NB, class Epi, typename TokFn>
+template <bool BF16, int KC, int NW, int NB, bool VEC, class Epi, typename TokFn>
 __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __restrict__ W1,
                                                 const typename Elem<BF16>::T* __restrict__ W2p,
                                                 TokFn tok, int R, int V, int r, int n_t,
-                                                const Epi& epi,
-                                                typename Elem<BF16>::T* __restrict__ w1g_out,
-                                                int contig) {
+                                                const Epi& epi) {
   typedef EngineGeom<BF16, KC, NW> Geo;
   typedef typename Elem<BF16>::Frag Frag;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -173,7 +163,7 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int g = lane >> 4, nl = lane & 15;
   const Frag* src = reinterpret_cast<const Frag*>(W2p);
-  const TileSeq seq = make_tile_seq(n_t, contig);
+  const TileSeq seq = make_tile_seq(n_t);
   if (seq.count <= 0) return;  // workgroup-uniform; no barrier passed yet
 
   // prologue: tile 0 of the sequence into LDS, W2 of tile 1 and the rows of
@@ -189,22 +179,10 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
     for (int i = 0; i < Geo::kPer; ++i) first[i] = s[Geo::slot(i, tid)];
   }
   Frag b[NB][KC];
-  gather_b<BF16, KC, NB>(W1, tok, R, r, V, wave, NW, lane, b);
+  gather_b<BF16, KC, NB, VEC>(W1, tok, R, r, V, wave, NW, lane, b);
   typename Epi::St st[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st[nb] = epi.prepare((wave + NW * nb) * kTileN + nl);
-  if (w1g_out != nullptr && blockIdx.x == 0) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = (wave + NW * nb) * kTileN + (lane & 15);
-      if (n < R) {
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          *reinterpret_cast<Frag*>(w1g_out + (size_t)n * (KC * kChunkK) + kc * kChunkK +
-                                   8 * (lane >> 4)) = b[nb][kc];
-      }
-    }
-  }
 #pragma unroll
   for (int i = 0; i < Geo::kPer; ++i) buf0[Geo::slot(i, tid)] = first[i];
   {

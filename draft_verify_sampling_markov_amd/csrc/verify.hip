@@ -20,9 +20,10 @@
 //                     of each request's job slot on the matrix cores, form
 //                     q = max(0, p_t - p_d) (or p_t for a bonus), and emit
 //                     per-tile sums of q and of p_t
-//   residual_select   per request: find the tile where the cumulative mass
-//                     crosses u * sum, recompute that tile with the same code
-//                     and finish the inverse-CDF search; write the token
+//   residual_select   one workgroup per request: find the tile where the
+//                     cumulative mass crosses u * sum, recompute that tile
+//                     with the same code and finish the inverse-CDF search;
+//                     write the token
 #include "dspark_device.hpp"
 #include "dspark_host.hpp"
 #include "tile_engine.hpp"
@@ -253,7 +254,8 @@ __device__ __forceinline__ void load_corr_inputs(const typename Elem<BF16>::T* _
 // ---------------------------------------------------------------------------
 
 // Epilogue of the residual pass: per entry q = max(0, p_t - p_d) (or p_t for
-// a bonus job) and p_t, summed per tile and request. The job fields are read
+// a bonus job) and p_t, summed per tile and request and stored at
+// rpart[n * ldn + part_pos(t, c)]. The job fields are read
 // once per kernel (prepare); a bonus job reads its target row in place of the
 // U row, so the loads need no branch.
 template <bool BF16, bool VEC>
@@ -274,7 +276,7 @@ struct ResidualEpi {
   int gamma, V, R, g0;
   Jobs jobs;
   float2* rpart;
-  int ldp;
+  int ldn, c;
   float2* junk;
 
   __device__ __forceinline__ St prepare(int n) const {
@@ -309,7 +311,8 @@ struct ResidualEpi {
     sp += __shfl_xor(sp, 16, kWave);
     sq += __shfl_xor(sq, 32, kWave);
     sp += __shfl_xor(sp, 32, kWave);
-    float2* dst = ((lane >> 4) == 0 && s.active) ? rpart + (size_t)t * ldp + s.ng : junk;
+    float2* dst =
+        ((lane >> 4) == 0 && s.active) ? rpart + (size_t)s.ng * ldn + part_pos(t, c) : junk;
     *dst = make_float2(sq, sp);
   }
 };
@@ -318,101 +321,86 @@ template <bool BF16, int KC, int NW, int NB, bool VEC>
 __global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
-    Jobs jobs, int g0, int R, int gamma, int V, int r, int n_t, float2* __restrict__ rpart, int ldp,
-    float2* __restrict__ junk, typename Elem<BF16>::T* __restrict__ w1g) {
-  const ResidualEpi<BF16, VEC> epi{target, U, gamma, V, R, g0, jobs, rpart, ldp, junk};
-  run_tile_engine<BF16, KC, NW, NB>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V, r,
-                                    n_t, epi, w1g, kTileOrder);
+    Jobs jobs, int g0, int R, int gamma, int V, int r, int n_t, float2* __restrict__ rpart, int ldn,
+    int c, float2* __restrict__ junk) {
+  const ResidualEpi<BF16, VEC> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c, junk};
+  run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
+                                         r, n_t, epi);
 }
 
 // ---------------------------------------------------------------------------
 // residual select
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int KC>
-__global__ __launch_bounds__(256) void residual_select_kernel(
+// One 256-thread workgroup per request, partials chunked as in the draft
+// select; wave 0 recomputes the crossing tile and writes the token.
+template <bool BF16, int KC, int CMAX, bool VW>
+__global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     bool vec, const typename Elem<BF16>::T* __restrict__ W1,
-    const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int R, int gamma, int V, int r,
-    int n_t, const float2* __restrict__ rpart, int ldp, int* __restrict__ out_tokens,
-    const typename Elem<BF16>::T* __restrict__ w1g) {
-  typedef typename Elem<BF16>::T T;
-  constexpr int kpad = KC * kChunkK;
-  constexpr int ldw = kpad + kLdsPad;
-  __shared__ __align__(16) T w1s[16 * ldw];
-  __shared__ TileSearchShared ts;
-  __shared__ float red[16];
-  const int tid = threadIdx.x;
-  const int n = blockIdx.x;
-  const int nb0 = n & ~(kTileN - 1);
-  const int q = n - nb0;
-  const int count = min(kTileN, R - nb0);
-  // W1 rows of the jobs' previous tokens, as gathered by the residual pass
-  stage_gathered<BF16>(w1g + (size_t)nb0 * kpad, count, kpad, ldw, w1s);
+    const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int gamma, int V, int r, int n_t,
+    const float2* __restrict__ rpart, int ldn, int c, int* __restrict__ out_tokens) {
+  typedef typename Elem<BF16>::Frag Frag;
+  __shared__ BlockSearchShared sh;
+  const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  const float2* prow = rpart + (size_t)n * ldn;
+  const int t0 = tid * c;
+  const int cnt = max(0, min(c, n_t - t0));
+  float2 pv[CMAX > 0 ? CMAX : 1];
+  if constexpr (CMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) pv[i] = prow[min(i, c - 1) * kSelThreads + tid];
+  }
+  const int x = clamp_token(jobs.xprev[n], V);
+  Frag b[KC];
+  load_b_row<BF16, KC, VW>(W1 + (size_t)x * r, r, lane, b);
+  const float u = jobs.u[n];
 
   // residual mass left? (else draw from p_t)
-  const int c = (n_t + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int t0 = min(n_t, tid * c), t1 = min(n_t, t0 + c);
-  constexpr int CMAX = 16;
   bool use_pt;
-  if (c <= CMAX) {  // each thread's partials stay in registers
-    float2 pv[CMAX];
-#pragma unroll
-    for (int i = 0; i < CMAX; ++i)
-      pv[i] = (t0 + i < t1) ? rpart[(size_t)(t0 + i) * ldp + n] : make_float2(0.0f, 0.0f);
+  WaveSearch ws;
+  if constexpr (CMAX > 0) {
     float lq = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CMAX; ++i)
-      if (t0 + i < t1) lq += pv[i].x;
-    use_pt = !(block_sum(lq, red) > 0.0f);
+    for (int i = 0; i < CMAX; ++i) lq += i < cnt ? pv[i].x : 0.0f;
+    use_pt = !(block_sum(lq, sh) > 0.0f);
     float w[CMAX];
 #pragma unroll
-    for (int i = 0; i < CMAX; ++i) w[i] = use_pt ? pv[i].y : pv[i].x;
-    block_tile_search_regs<CMAX>(w, t0, t1 - t0, jobs.u[n], ts);
+    for (int i = 0; i < CMAX; ++i) w[i] = i < cnt ? (use_pt ? pv[i].y : pv[i].x) : 0.0f;
+    ws = block_tile_search<CMAX>([&](int i) { return w[i]; }, t0, cnt, u, sh);
   } else {
     float lq = 0.0f;
-    for (int t = t0; t < t1; ++t) lq += rpart[(size_t)t * ldp + n].x;
-    use_pt = !(block_sum(lq, red) > 0.0f);
-    block_tile_search(n_t, jobs.u[n], [&](int t) {
-      const float2 pv = rpart[(size_t)t * ldp + n];
-      return use_pt ? pv.y : pv.x;
-    }, ts);
+    for (int i = 0; i < cnt; ++i) lq += prow[i * kSelThreads + tid].x;
+    use_pt = !(block_sum(lq, sh) > 0.0f);
+    ws = block_tile_search<0>([&](int i) {
+      const float2 q = prow[i * kSelThreads + tid];
+      return use_pt ? q.y : q.x;
+    }, t0, cnt, u, sh);
   }
-
   if (tid >= kWave) return;  // wave 0 finishes; no barrier below
-  const int lane = tid;
-  const int g = lane >> 4, nl = lane & 15;
-  const int t = min(max(ts.tstar, 0), n_t - 1);
-  ATile<BF16, KC> at;
-  load_a_tile<BF16, KC>(W2p, t, lane, at);
-  f32x4 acc[4];
-  tile_mma<BF16, KC>(at, w1s, ldw, lane, acc);
+
+  // recompute the crossing tile; lane l gets entries 64 t + 16 (l/16) + [0, 16)
+  const int g = lane >> 4;
+  const int t = min(max(ws.tstar, 0), n_t - 1);
   const int v0 = t * kTileV + 16 * g;
   const int nvalid = min(16, V - v0);
   const bool residual = jobs.kind[n] == 0;
   const int trow = jobs.trow[n], dslot = jobs.slot[n] - 1;
   const float lse_t = jobs.lse_t[n], lse_d = jobs.lse_d[n];
+  ATile<BF16, KC> at;
+  load_a_tile<BF16, KC>(W2p, t, lane, at);
   float zt16[16], u16[16];
-  const bool mine = nl == q;
-  if (mine && nvalid > 0) {
-    load_corr_inputs<BF16>(target, U, V, gamma, vec, n, v0, nvalid, trow, dslot, residual, zt16, u16);
-  } else {
+  load_corr_inputs<BF16>(target, U, V, gamma, vec, n, v0, nvalid, trow, dslot, residual, zt16, u16);
+  f32x4 acc[4];
+  tile_mma_regs<BF16, KC>(at, b, acc);
+  float qv[16], pt16[16];
+  corr_tile_values<BF16>(acc, zt16, u16, nvalid, lse_t, lse_d, residual, qv, pt16);
+  float w16[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) zt16[i] = u16[i] = 0.0f;
-  }
-  float qv[16], pv[16];
-  corr_tile_values<BF16>(acc, zt16, u16, (mine ? nvalid : 0), lse_t, lse_d, residual, qv, pv);
-  const int src = q + 16 * (lane >> 4);
-  float wi = 0.0f;
-#pragma unroll
-  for (int idx = 0; idx < 16; ++idx) {
-    const float val = __shfl(use_pt ? pv[idx] : qv[idx], src, kWave);
-    if ((lane & 15) == idx) wi = val;
-  }
-  const int v = t * kTileV + lane;
-  const bool valid = v < V;
-  if (!valid) wi = 0.0f;
-  const int sel = tile_pick(wi, valid, ts.pb, ts.T, lane);
+  for (int i = 0; i < 16; ++i) w16[i] = use_pt ? pt16[i] : qv[i];
+  const bool valid = t * kTileV + lane < V;
+  const float wi = valid ? pick16(w16, lane & 15) : 0.0f;
+  const int sel = tile_pick(wi, valid, ws.pb, ws.T, lane);
   if (lane == 0) out_tokens[(size_t)n * (gamma + 1) + jobs.slot[n] - 1] = t * kTileV + sel;
 }
 
@@ -422,9 +410,8 @@ __global__ __launch_bounds__(256) void residual_select_kernel(
 
 struct VerifyWs {
   float2* rowpart;
-  float2* rpart;
-  float2* junk;  // write target of masked lanes
-  void* w1g;  // gathered W1 rows of the jobs' previous tokens [R, 256]
+  float2* rpart;  // request-major residual tile partials [R, part_ld(V)]
+  float2* junk;   // write target of masked lanes
   Jobs jobs;
 };
 
@@ -438,9 +425,8 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
     return o;
   };
   const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
-  const size_t o_rp = take((size_t)n_vtiles(V) * R * sizeof(float2));
+  const size_t o_rp = take((size_t)R * part_ld(V) * sizeof(float2));
   const size_t o_junk = take(256);
-  const size_t o_g = take((size_t)R * kMaxRankBf16 * 4);
   size_t o_j[7];
   for (int i = 0; i < 7; ++i) o_j[i] = take((size_t)R * 4);
   if (w && base) {
@@ -448,7 +434,6 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
     w->rowpart = reinterpret_cast<float2*>(b + o_row);
     w->rpart = reinterpret_cast<float2*>(b + o_rp);
     w->junk = reinterpret_cast<float2*>(b + o_junk);
-    w->w1g = b + o_g;
     w->jobs.kind = reinterpret_cast<int*>(b + o_j[0]);
     w->jobs.slot = reinterpret_cast<int*>(b + o_j[1]);
     w->jobs.trow = reinterpret_cast<int*>(b + o_j[2]);
@@ -470,15 +455,16 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
                          int gamma, int V, int r, int32_t* accept_len, int32_t* out_tokens,
                          int32_t* n_out, int32_t* ceiling, const VerifyWs& ws, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
-  constexpr int kpad = KC * kChunkK;
-  constexpr int ldw = kpad + kLdsPad;
   const T* tg = static_cast<const T*>(target);
   const T* Ub = static_cast<const T*>(U);
   const T* W1b = static_cast<const T*>(W1);
   const T* W2b = static_cast<const T*>(W2p);
   const int nch = n_row_chunks(V), n_t = n_vtiles(V);
-  const bool vec = (V % Elem<BF16>::kVec) == 0 && (reinterpret_cast<uintptr_t>(target) % 16) == 0 &&
-                   (reinterpret_cast<uintptr_t>(U) % 16) == 0;
+  const bool vec = rows_vec_ok(target, V, V, Elem<BF16>::kVec) &&
+                   rows_vec_ok(U, V, V, Elem<BF16>::kVec);
+  const bool vec_w1 = w1_vec_ok(W1, r);
+  const bool vec_engine = vec && vec_w1;
+  const int ldn = part_ld(V), c = part_chunk(V);
   const int rows_ws = R * (gamma + 1);
   (void)M_cap;
   hipLaunchKernelGGL((row_partials_kernel<BF16>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s, tg, V,
@@ -494,19 +480,18 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
   for (int g0 = 0; g0 < R; g0 += kReqGroup) {
     const int Rg = std::min(kReqGroup, R - g0);
     const int blocks = ceil_div(Rg, kTileN);
-    T* wg = static_cast<T*>(ws.w1g) + (size_t)g0 * kpad;
 #define DSPARK_RES_LAUNCH(NW_, NB_, PERCU)                                                         \
     {                                                                                              \
       typedef EngineGeom<BF16, KC, NW_> G;                                                         \
       const dim3 grid(std::max(1, std::min(n_t, PERCU * ncu)));                                    \
-      if (vec)                                                                                     \
+      if (vec_engine)                                                                              \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, true>), grid,             \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           gamma, V, r, n_t, ws.rpart, R, ws.junk, wg);                            \
+                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk);                           \
       else                                                                                         \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, false>), grid,            \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           gamma, V, r, n_t, ws.rpart, R, ws.junk, wg);                            \
+                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk);                           \
     }
     if (blocks <= 4) DSPARK_RES_LAUNCH(4, 1, 2)
     else if (blocks <= 8) DSPARK_RES_LAUNCH(8, 1, 1)
@@ -515,9 +500,21 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
     st = launch_status();
     if (st) return st;
   }
-  hipLaunchKernelGGL((residual_select_kernel<BF16, KC>), dim3(R), dim3(256), 0, s,
-                     tg, Ub, vec, W1b, W2b, ws.jobs, R, gamma, V, r, n_t, ws.rpart, R, out_tokens,
-                     static_cast<const T*>(ws.w1g));
+#define DSPARK_RES_SELECT(CM)                                                                     \
+  if (vec_w1)                                                                                    \
+    hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, \
+                       tg, Ub, vec, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,        \
+                       out_tokens);                                                              \
+  else                                                                                           \
+    hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
+                       tg, Ub, vec, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,        \
+                       out_tokens)
+  if (c <= 16) {
+    DSPARK_RES_SELECT(16);
+  } else {
+    DSPARK_RES_SELECT(0);
+  }
+#undef DSPARK_RES_SELECT
   return launch_status();
 }
 

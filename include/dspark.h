@@ -238,9 +238,12 @@ int dspark_verify(const void* target_packed, int M_cap, const int32_t* cu_seqlen
 /* The first of the two passes dspark_markov_draft runs for every slot, as a
  * call of its own (for callers that time or fuse it): the bias GEMM
  * W1[x_prev] W2 on the matrix cores plus U_k, reduced per 64-entry vocabulary
- * tile t to a softmax partial part[t * R + n] = (max_v z, sum_v exp(z - max))
- * of request n (two floats). U_k rows are ldU elements apart; x_prev[n *
- * xstride] is the previous token of request n. part must hold
+ * tile t to a softmax partial (max_v z, sum_v exp(z - max)) of request n (two
+ * floats). The partials are request-major: with n_t = ceil(V / 64) tiles and
+ * c = ceil(n_t / 256), request n's row starts at part + n * 256 c (float2
+ * units) and tile t sits at (t % c) * 256 + t / c in it -- the order in which
+ * the 256 threads of dspark_markov_select read them. U_k rows are ldU elements
+ * apart; x_prev[n * xstride] is the previous token of request n. part must hold
  * dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, R, 1, V, r) bytes. */
 int dspark_markov_partials(const void* U_k, long long ldU, const void* W1, const void* W2p,
                            const int32_t* x_prev, int xstride, int R, int V, int r, int dtype,
