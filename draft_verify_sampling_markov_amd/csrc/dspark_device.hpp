@@ -640,11 +640,18 @@ __device__ __forceinline__ void tile_mma_regs(const ATile<BF16, KC>& at,
     for (int j = 0; j < 4; ++j) mma_step<BF16>(acc[j], at.a[kc][j], b[kc]);
 }
 
-// Entry `idx` (0..15) of a lane's 16 values, without dynamic register indexing.
-__device__ __forceinline__ float pick16(const float v[16], int idx) {
-  float r = v[0];
+// The product entry lane l of a one-row tile product needs for tile entry l,
+// acc[(l / 4) % 4][l % 4] (layout above), taken with exact 0/1 weights rather
+// than an indexed read: the compiler turns indexed picks out of small arrays
+// into LDS arrays addressed through the dispatch packet, a read of host memory.
+// Exact for finite products (adds of zero).
+__device__ __forceinline__ float own_entry(const f32x4 acc[4], int lane) {
+  const int j = (lane >> 2) & 3, i = lane & 3;
+  float r = 0.0f;
 #pragma unroll
-  for (int i = 1; i < 16; ++i) r = idx == i ? v[i] : r;
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) r = fmaf(acc[jj][ii], (jj == j && ii == i) ? 1.0f : 0.0f, r);
   return r;
 }
 

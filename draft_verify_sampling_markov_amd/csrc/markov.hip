@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
 // row it loaded at the start and finishes the draw.
 template <bool BF16, int KC, int CMAX, bool VW>
 __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
-    const typename Elem<BF16>::T* __restrict__ U, long long ldU, bool vec,
+    const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int V, int r, int n_t,
     const float2* __restrict__ part, int ldn, int c, uint64_t seed, uint64_t step,
@@ -168,23 +168,17 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
   }
   if (tid >= kWave) return;  // wave 0 finishes; no barrier below
 
-  // recompute the crossing tile; lane l gets entries 64 t + 16 (l/16) + [0, 16)
-  const int g = lane >> 4;
+  // recompute the crossing tile; lane l takes entry v = 64 t + l
   const int t = min(max(ws.tstar, 0), n_t - 1);
-  const int v0 = t * kTileV + 16 * g;
-  const int nvalid = min(16, V - v0);
   ATile<BF16, KC> at;
   load_a_tile<BF16, KC>(W2p, t, lane, at);
-  float u16[16];
-  load16<BF16>(U + (size_t)n * ldU + v0, nvalid, vec, u16);
+  const int v = t * kTileV + lane;
+  const bool valid = v < V;
+  const float uo = to_f32(U[(size_t)n * ldU + min(v, V - 1)]);
   f32x4 acc[4];
   tile_mma_regs<BF16, KC>(at, b, acc);
-  float z[16];
-  tile_logits<BF16>(acc, u16, nvalid, true, z);
-  // lane i takes tile entry i, which its own group holds at index i % 16
-  const float zi = pick16(z, lane & 15);
-  const bool valid = t * kTileV + lane < V;
-  const float e = valid ? __expf(zi - m) : 0.0f;
+  const float zo = own_entry(acc, lane) + uo;  // the same sum the GEMM pass formed
+  const float e = valid ? __expf(zo - m) : 0.0f;
   const int sel = tile_pick(e, valid, ws.pb, ws.T, lane);
   const float esel = readlane_f(e, sel);
   if (lane == 0) {
@@ -319,11 +313,11 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
 #define DSPARK_SELECT(CM)                                                                         \
   if (vec_w1)                                                                                    \
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, Uk, \
-                       ldU, vec, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed, step,    \
+                       ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed, step,         \
                        req_ids, k, tok, p, lse, ostride);                                        \
   else                                                                                           \
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
-                       Uk, ldU, vec, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed,      \
+                       Uk, ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed,           \
                        step, req_ids, k, tok, p, lse, ostride)
   if (c <= 16) {
     DSPARK_SELECT(16);

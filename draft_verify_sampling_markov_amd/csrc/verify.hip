@@ -234,21 +234,6 @@ __device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void load_corr_inputs(const typename Elem<BF16>::T* __restrict__ target,
-                                                 const typename Elem<BF16>::T* __restrict__ U,
-                                                 int V, int gamma, bool vec, int n, int v0,
-                                                 int nvalid, int trow, int dslot, bool residual,
-                                                 float zt16[16], float u16[16]) {
-  load16<BF16>(target + (size_t)trow * V + v0, nvalid, vec, zt16);
-  if (residual) {
-    load16<BF16>(U + ((size_t)n * gamma + dslot) * V + v0, nvalid, vec, u16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u16[i] = 0.0f;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // residual partials
 // ---------------------------------------------------------------------------
@@ -337,9 +322,9 @@ __global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
 template <bool BF16, int KC, int CMAX, bool VW>
 __global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
-    bool vec, const typename Elem<BF16>::T* __restrict__ W1,
-    const typename Elem<BF16>::T* __restrict__ W2p, Jobs jobs, int gamma, int V, int r, int n_t,
-    const float2* __restrict__ rpart, int ldn, int c, int* __restrict__ out_tokens) {
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    Jobs jobs, int gamma, int V, int r, int n_t, const float2* __restrict__ rpart, int ldn, int c,
+    int* __restrict__ out_tokens) {
   typedef typename Elem<BF16>::Frag Frag;
   __shared__ BlockSearchShared sh;
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -379,27 +364,24 @@ __global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
   }
   if (tid >= kWave) return;  // wave 0 finishes; no barrier below
 
-  // recompute the crossing tile; lane l gets entries 64 t + 16 (l/16) + [0, 16)
-  const int g = lane >> 4;
+  // recompute the crossing tile; lane l takes entry v = 64 t + l
   const int t = min(max(ws.tstar, 0), n_t - 1);
-  const int v0 = t * kTileV + 16 * g;
-  const int nvalid = min(16, V - v0);
   const bool residual = jobs.kind[n] == 0;
   const int trow = jobs.trow[n], dslot = jobs.slot[n] - 1;
   const float lse_t = jobs.lse_t[n], lse_d = jobs.lse_d[n];
   ATile<BF16, KC> at;
   load_a_tile<BF16, KC>(W2p, t, lane, at);
-  float zt16[16], u16[16];
-  load_corr_inputs<BF16>(target, U, V, gamma, vec, n, v0, nvalid, trow, dslot, residual, zt16, u16);
+  const int v = t * kTileV + lane;
+  const bool valid = v < V;
+  const int vc = min(v, V - 1);
+  const float zt = to_f32(target[(size_t)trow * V + vc]);
+  const float ud = residual ? to_f32(U[((size_t)n * gamma + dslot) * V + vc]) : 0.0f;
   f32x4 acc[4];
   tile_mma_regs<BF16, KC>(at, b, acc);
-  float qv[16], pt16[16];
-  corr_tile_values<BF16>(acc, zt16, u16, nvalid, lse_t, lse_d, residual, qv, pt16);
-  float w16[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) w16[i] = use_pt ? pt16[i] : qv[i];
-  const bool valid = t * kTileV + lane < V;
-  const float wi = valid ? pick16(w16, lane & 15) : 0.0f;
+  const float zd = own_entry(acc, lane) + ud;  // the same sum the residual pass formed
+  const float q = corr_weight(zt, zd, lse_t, lse_d, residual);
+  const float pt = __expf(zt - lse_t);
+  const float wi = valid ? (use_pt ? pt : q) : 0.0f;
   const int sel = tile_pick(wi, valid, ws.pb, ws.T, lane);
   if (lane == 0) out_tokens[(size_t)n * (gamma + 1) + jobs.slot[n] - 1] = t * kTileV + sel;
 }
@@ -503,11 +485,11 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
 #define DSPARK_RES_SELECT(CM)                                                                     \
   if (vec_w1)                                                                                    \
     hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, \
-                       tg, Ub, vec, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,        \
+                       tg, Ub, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,             \
                        out_tokens);                                                              \
   else                                                                                           \
     hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
-                       tg, Ub, vec, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,        \
+                       tg, Ub, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,             \
                        out_tokens)
   if (c <= 16) {
     DSPARK_RES_SELECT(16);
