@@ -323,6 +323,51 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int /*lane*/) {
 // The value of the previous lane (0 for lane 0).
 __device__ __forceinline__ float wave_shift_up1(float v) { return dpp_f<kDppWaveShr1>(0.0f, v); }
 
+// Integer versions (exact, so the order does not matter for the result).
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v) {
+  v += (uint32_t)dpp_i<kDppRowShr1>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowShr2>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowShr4>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowShr8>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowBcast15, 0xA>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowBcast31, 0xC>(0, (int)v);
+  return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+  v = min(v, dpp_i<kDppXor1>(v, v));
+  v = min(v, dpp_i<kDppXor2>(v, v));
+  v = min(v, dpp_i<kDppRowHalfMirror>(v, v));
+  v = min(v, dpp_i<kDppRowMirror>(v, v));
+  v = min(v, dpp_i<kDppRowBcast15, 0xA>(v, v));
+  v = min(v, dpp_i<kDppRowBcast31, 0xC>(v, v));
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// (largest th, then smallest k) over the 64 lanes, returned to every lane.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void argmax_step(unsigned long long& th, int& k) {
+  const int lo = (int)(uint32_t)th, hi = (int)(uint32_t)(th >> 32);
+  const uint32_t olo = (uint32_t)dpp_i<CTRL, ROW_MASK>(lo, lo);
+  const uint32_t ohi = (uint32_t)dpp_i<CTRL, ROW_MASK>(hi, hi);
+  const int ok = dpp_i<CTRL, ROW_MASK>(k, k);
+  const unsigned long long ot = ((unsigned long long)ohi << 32) | olo;
+  const bool better = ot > th || (ot == th && ok < k);
+  th = better ? ot : th;
+  k = better ? ok : k;
+}
+__device__ __forceinline__ void wave_argmax_u64(unsigned long long& th, int& k) {
+  argmax_step<kDppXor1>(th, k);
+  argmax_step<kDppXor2>(th, k);
+  argmax_step<kDppRowHalfMirror>(th, k);
+  argmax_step<kDppRowMirror>(th, k);
+  argmax_step<kDppRowBcast15, 0xA>(th, k);
+  argmax_step<kDppRowBcast31, 0xC>(th, k);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)th, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(th >> 32), kWave - 1);
+  th = ((unsigned long long)hi << 32) | lo;
+  k = __builtin_amdgcn_readlane(k, kWave - 1);
+}
+
 // Merge two (max, sum of exp(z - max)) softmax partials.
 __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
   const float mm = fmaxf(m, m2);

@@ -16,8 +16,10 @@
 // Everything is integer fixed point (survival quantised to 2^-20, Theta as a
 // uint64 product), so the result does not depend on the order in which the
 // workgroup's threads combine it. One workgroup: quantise, sort the R*gamma
-// keys in LDS (rank counting up to one key per thread, a bitonic network
-// beyond), integer prefix sums, Theta per K, reduction, window counts.
+// keys in LDS (a stable LSD radix sort over the 21-bit code 2^20 - a_q, three
+// passes of 7 bits: ties keep index order, which is the key order), integer
+// prefix sums, Theta per K, an argmax, and the window counts, read off the
+// K-th smallest key as a threshold.
 //
 // Pack -- SGLang DSpark blog ("Ragged verify under full CUDA graphs"): windows
 // packed front to back into a cu_seqlens buffer, total rounded up to the
@@ -31,8 +33,14 @@
 namespace dspark {
 
 constexpr int kSchedThreads = 1024;
+constexpr int kSchedWaves = kSchedThreads / kWave;
 constexpr int kSchedMaxKeys = 4096;
+constexpr int kSchedMaxRows = kSchedMaxKeys / kWave;  // rows of 64 keys
+constexpr int kRadixBits = 7;
+constexpr int kRadixBuckets = 1 << kRadixBits;
+constexpr int kRadixPasses = 3;                        // 21-bit codes
 constexpr uint32_t kQOne = 1u << 20;
+constexpr unsigned long long kPadCode = (1ull << (kRadixBits * kRadixPasses)) - 1;  // above any code
 
 __device__ __forceinline__ uint32_t quantize_survival(float a) {
   if (!(a == a)) return 0u;
@@ -40,8 +48,19 @@ __device__ __forceinline__ uint32_t quantize_survival(float a) {
   return (uint32_t)(a * 1048576.0f);  // exact scaling; truncation = floor for a >= 0
 }
 
-// keys[i] = ((2^20 - a_q) << 32) | i for i = r*gamma + j, padded to P with ~0.
-__device__ void build_keys(const float* __restrict__ a, int R, int gamma, int P,
+struct SchedShared {
+  unsigned long long orig[kSchedMaxKeys];  // keys in index order
+  unsigned long long a[kSchedMaxKeys];     // radix ping-pong buffers; result in a
+  unsigned long long b[kSchedMaxKeys];
+  uint32_t hist[kRadixBuckets * kSchedMaxRows];  // also the prefix sums afterwards
+  uint32_t wsum[kSchedWaves];
+  unsigned long long th[kSchedWaves];
+  int k[kSchedWaves];
+};
+
+// orig[i] = ((2^20 - a_q) << 32) | i for i = r*gamma + j (a_q the prefix-min
+// quantised survival of request r), padded to NP keys that sort last.
+__device__ void build_keys(const float* __restrict__ a, int R, int gamma, int NP,
                            unsigned long long* keys) {
   const int N = R * gamma;
   for (int req = threadIdx.x; req < R; req += blockDim.x) {
@@ -52,78 +71,102 @@ __device__ void build_keys(const float* __restrict__ a, int R, int gamma, int P,
       keys[i] = ((unsigned long long)(kQOne - run) << 32) | (unsigned long long)i;
     }
   }
-  for (int i = N + threadIdx.x; i < P; i += blockDim.x) keys[i] = ~0ull;
+  for (int i = N + threadIdx.x; i < NP; i += blockDim.x)
+    keys[i] = (kPadCode << 32) | (unsigned long long)i;
   __syncthreads();
 }
 
-__device__ void bitonic_sort(unsigned long long* keys, int P) {
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = keys[i], y = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+// In-place exclusive prefix sum of x[0..n) over the workgroup (n <= 8192).
+__device__ void block_exclusive_scan(uint32_t* x, int n, uint32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  constexpr int kE = kRadixBuckets * kSchedMaxRows / kSchedThreads;  // 8
+  const int e0 = tid * kE;
+  uint32_t v[kE];
+  uint32_t local = 0;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    v[e] = e0 + e < n ? x[e0 + e] : 0u;
+    local += v[e];
   }
+  const uint32_t incl = wave_inclusive_scan_u32(local);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t run = incl - local;
+#pragma unroll
+  for (int w = 0; w < kSchedWaves; ++w) run += w < wave ? wsum[w] : 0u;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    if (e0 + e < n) x[e0 + e] = run;
+    run += v[e];
+  }
+  __syncthreads();
 }
 
-// Sort the first N keys ascending. Keys are distinct (they carry their index).
-// Up to one key per thread: a key's position is the number of smaller keys,
-// counted in one pass over the array (LDS broadcast reads, eight in flight),
-// then a scatter through `scratch`. More keys: a bitonic network over the P
-// keys (padded with ~0).
-__device__ void sort_keys(unsigned long long* keys, unsigned long long* scratch, int N, int P) {
-  if (N <= (int)blockDim.x) {
-    const int i = threadIdx.x;
-    if (i < N) {
-      const unsigned long long mine = keys[i];
-      int rank = 0;
-      const int N8 = N & ~7;
-      for (int j = 0; j < N8; j += 8) {
-        unsigned long long kj[8];
+// One stable counting pass on digit (code >> shift) & 127 of NR rows of 64
+// keys: a key's place = keys of smaller digits + keys of its digit in earlier
+// rows (digit-major histogram scan) + earlier keys of its digit in its row
+// (ballot masks).
+__device__ void radix_pass(const unsigned long long* src, unsigned long long* dst, int NR,
+                           int shift, SchedShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  constexpr int kRowsPerWave = kSchedMaxRows / kSchedWaves;  // 4
+  unsigned long long kk[kRowsPerWave];
+  int dig[kRowsPerWave], rk[kRowsPerWave];
+  const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kj[u] = keys[j + u];
+  for (int u = 0; u < kRowsPerWave; ++u) {
+    const int row = wave + kSchedWaves * u;
+    kk[u] = 0ull;
+    dig[u] = 0;
+    rk[u] = 0;
+    if (row < NR) {  // wave-uniform
+      const unsigned long long key = src[row * kWave + lane];
+      const int d = (int)((key >> (32 + shift)) & (kRadixBuckets - 1));
+      unsigned long long B[kRadixBits];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) rank += kj[u] < mine;
+      for (int bt = 0; bt < kRadixBits; ++bt) B[bt] = __ballot((d >> bt) & 1);
+      unsigned long long m = ~0ull;
+#pragma unroll
+      for (int bt = 0; bt < kRadixBits; ++bt) m &= ((d >> bt) & 1) ? B[bt] : ~B[bt];
+      rk[u] = __popcll(m & below);
+#pragma unroll
+      for (int h = 0; h < kRadixBuckets / kWave; ++h) {
+        const int dd = lane + kWave * h;
+        unsigned long long mm = ~0ull;
+#pragma unroll
+        for (int bt = 0; bt < kRadixBits; ++bt) mm &= ((dd >> bt) & 1) ? B[bt] : ~B[bt];
+        sh.hist[dd * NR + row] = (uint32_t)__popcll(mm);
       }
-      for (int j = N8; j < N; ++j) rank += keys[j] < mine;
-      scratch[rank] = mine;
+      kk[u] = key;
+      dig[u] = d;
     }
-    __syncthreads();
-    if (i < N) keys[i] = scratch[i];
-    __syncthreads();
-  } else {
-    bitonic_sort(keys, P);
   }
+  __syncthreads();
+  block_exclusive_scan(sh.hist, kRadixBuckets * NR, sh.wsum);
+#pragma unroll
+  for (int u = 0; u < kRowsPerWave; ++u) {
+    const int row = wave + kSchedWaves * u;
+    if (row < NR) dst[sh.hist[dig[u] * NR + row] + rk[u]] = kk[u];
+  }
+  __syncthreads();
+}
+
+// Sort orig[0 .. 64 NR) ascending into sh.a (orig is kept).
+__device__ void radix_sort(int NR, SchedShared& sh) {
+  radix_pass(sh.orig, sh.a, NR, 0, sh);
+  radix_pass(sh.a, sh.b, NR, kRadixBits, sh);
+  radix_pass(sh.b, sh.a, NR, 2 * kRadixBits, sh);
 }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     const float* __restrict__ surv, const float* __restrict__ surv_budget,
     const uint32_t* __restrict__ sps, int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
     int* __restrict__ win_len, int* __restrict__ K_out) {
-  __shared__ unsigned long long keys[kSchedMaxKeys];
-  __shared__ unsigned long long sort_scratch[kSchedMaxKeys];
-  // inclusive prefix of the sorted a_q, then window counts: reuses the sort
-  // scratch, which is dead once the sorted keys are back in `keys`
-  uint32_t* pre = reinterpret_cast<uint32_t*>(sort_scratch);
-  __shared__ uint32_t wtot[kSchedThreads / kWave];
-  __shared__ unsigned long long red_theta[kSchedThreads / kWave];
-  __shared__ int red_k[kSchedThreads / kWave];
-  __shared__ int K_sh;
-
+  __shared__ SchedShared sh;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int nw = blockDim.x / kWave;
   const int N = R * gamma;
-  int P = 1;
-  while (P < N) P <<= 1;
+  const int NR = (N + kWave - 1) / kWave;
+  const int NP = NR * kWave;
   const int K_cap = max(0, min(min(B_cap, N), M_max - R));
 
   int K = 0;
@@ -136,106 +179,78 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     uint32_t sp0[kMaxPer], sp1[kMaxPer];
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
-      const int Kc = tid + i * (int)blockDim.x;
-      sp0[i] = Kc <= K_cap ? sps[R + Kc] : 0u;
-      sp1[i] = Kc < K_cap ? sps[R + Kc + 1] : 0u;
+      const int Kc = tid + i * kSchedThreads;
+      sp0[i] = sps[R + min(Kc, K_cap)];
+      sp1[i] = sps[R + min(Kc + 1, K_cap)];
     }
-    build_keys(surv_budget ? surv_budget : surv, R, gamma, P, keys);
-    sort_keys(keys, sort_scratch, N, P);
-    // inclusive prefix sums of the sorted a_q (each thread: 4 consecutive keys)
-    const int per = (P + blockDim.x - 1) / blockDim.x;
-    const int b0 = tid * per;
-    uint32_t local = 0;
-    for (int i = b0; i < min(b0 + per, N); ++i) local += kQOne - (uint32_t)(keys[i] >> 32);
-    uint32_t incl = local;
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += t;
-    }
-    if (lane == kWave - 1) wtot[wave] = incl;
+    build_keys(surv_budget ? surv_budget : surv, R, gamma, NP, sh.orig);
+    radix_sort(NR, sh);
+    // ex[K] = sum of the K largest a_q (exclusive prefix over the sorted keys)
+    for (int i = tid; i <= N; i += kSchedThreads)
+      sh.hist[i] = i < N ? kQOne - (uint32_t)(sh.a[i] >> 32) : 0u;
     __syncthreads();
-    uint32_t woff = 0;
-    for (int w = 0; w < wave; ++w) woff += wtot[w];
-    uint32_t run = woff + incl - local;
-    for (int i = b0; i < min(b0 + per, N); ++i) {
-      run += kQOne - (uint32_t)(keys[i] >> 32);
-      pre[i] = run;
-    }
-    __syncthreads();
+    block_exclusive_scan(sh.hist, N + 1, sh.wsum);
     const unsigned long long base = (unsigned long long)R * kQOne;
-    // Theta_K = tau_K * sps[R + K], tau_K = R*2^20 + pre[K-1]
+    // Theta_K = tau_K * sps[R + K], tau_K = R*2^20 + ex[K]
     unsigned long long best_t = 0;
     int best_k = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
-      const int Kc = tid + i * (int)blockDim.x;
+      const int Kc = tid + i * kSchedThreads;
       if (Kc > K_cap) continue;
-      const unsigned long long tau = base + (Kc ? pre[Kc - 1] : 0u);
-      const unsigned long long th = tau * (unsigned long long)sp0[i];
+      const unsigned long long th = (base + sh.hist[Kc]) * (unsigned long long)sp0[i];
       if (mode == DSPARK_SCHED_ARGMAX) {
         if (best_k == 0x7fffffff || th > best_t) {
           best_t = th;
           best_k = Kc;
         }
       } else if (Kc < K_cap) {  // GREEDY: first K with Theta_{K+1} <= Theta_K
-        const unsigned long long tau1 = base + pre[Kc];
-        const unsigned long long th1 = tau1 * (unsigned long long)sp1[i];
+        const unsigned long long th1 = (base + sh.hist[Kc + 1]) * (unsigned long long)sp1[i];
         if (th1 <= th && Kc < best_k) best_k = Kc;
       }
     }
-    // reduce: ARGMAX -> (largest Theta, then smallest K); GREEDY -> smallest K
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      const unsigned long long ot = __shfl_xor(best_t, o, kWave);
-      const int ok = __shfl_xor(best_k, o, kWave);
-      if (mode == DSPARK_SCHED_ARGMAX) {
-        if (ok != 0x7fffffff && (best_k == 0x7fffffff || ot > best_t || (ot == best_t && ok < best_k))) {
-          best_t = ot;
-          best_k = ok;
-        }
-      } else if (ok < best_k) {
-        best_k = ok;
-      }
+    // ARGMAX: largest Theta, then smallest K; GREEDY: smallest K
+    if (mode == DSPARK_SCHED_ARGMAX) {
+      wave_argmax_u64(best_t, best_k);
+    } else {
+      best_k = wave_min_int(best_k);
     }
     if (lane == 0) {
-      red_theta[wave] = best_t;
-      red_k[wave] = best_k;
+      sh.th[wave] = best_t;
+      sh.k[wave] = best_k;
     }
     __syncthreads();
-    if (tid == 0) {
-      unsigned long long bt = red_theta[0];
-      int bk = red_k[0];
-      for (int w = 1; w < nw; ++w) {
-        if (mode == DSPARK_SCHED_ARGMAX) {
-          if (red_k[w] != 0x7fffffff &&
-              (bk == 0x7fffffff || red_theta[w] > bt || (red_theta[w] == bt && red_k[w] < bk))) {
-            bt = red_theta[w];
-            bk = red_k[w];
-          }
-        } else if (red_k[w] < bk) {
-          bk = red_k[w];
+    unsigned long long bt = sh.th[0];
+    int bk = sh.k[0];
+    for (int w = 1; w < kSchedWaves; ++w) {
+      if (mode == DSPARK_SCHED_ARGMAX) {
+        if (sh.k[w] != 0x7fffffff &&
+            (bk == 0x7fffffff || sh.th[w] > bt || (sh.th[w] == bt && sh.k[w] < bk))) {
+          bt = sh.th[w];
+          bk = sh.k[w];
         }
+      } else {
+        bk = min(bk, sh.k[w]);
       }
-      if (mode == DSPARK_SCHED_GREEDY && bk == 0x7fffffff) bk = K_cap;
-      if (bk == 0x7fffffff) bk = 0;
-      K_sh = bk;
     }
-    __syncthreads();
-    K = K_sh;
+    if (mode == DSPARK_SCHED_GREEDY && bk == 0x7fffffff) bk = K_cap;
+    if (bk == 0x7fffffff) bk = 0;
+    K = bk;
   }
 
-  // selection: the K best keys of the current survivals
+  // selection: the K best keys of the current survivals; within a request
+  // they form a prefix, so its window is the count of its keys below the
+  // K-th smallest key
   if (mode == DSPARK_SCHED_FIXED || surv_budget != nullptr) {
-    build_keys(surv, R, gamma, P, keys);
-    sort_keys(keys, sort_scratch, N, P);
+    build_keys(surv, R, gamma, NP, sh.orig);
+    radix_sort(NR, sh);
   }
-  for (int i = tid; i < R; i += blockDim.x) pre[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < K; i += blockDim.x) {
-    const int idx = (int)(keys[i] & 0xffffffffull);
-    atomicAdd(&pre[idx / gamma], 1u);
+  const unsigned long long thr = K < N ? sh.a[K] : ~0ull;
+  for (int r = tid; r < R; r += kSchedThreads) {
+    int cnt = 0;
+    for (int j = 0; j < gamma; ++j) cnt += sh.orig[r * gamma + j] < thr;
+    win_len[r] = cnt;
   }
-  __syncthreads();
-  for (int i = tid; i < R; i += blockDim.x) win_len[i] = (int)pre[i];
   if (tid == 0) K_out[0] = K;
 }
 
