@@ -14,7 +14,10 @@ constexpr int kMaxRows = 4096;      // R * (gamma + 1)
 constexpr int kMaxRankBf16 = 256;
 constexpr int kMaxRankF32 = 128;
 constexpr int kMaxTiers = 32;
-constexpr int kReqGroup = 256;      // requests whose W1 rows one GEMM launch holds
+// Requests whose W1 rows one GEMM launch holds in registers: 16 blocks of 16
+// for bfloat16 (two per wave), 8 blocks for float32, whose 8-float operands
+// would not fit twice per wave.
+template <bool BF16> constexpr int req_group() { return BF16 ? 256 : 128; }
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

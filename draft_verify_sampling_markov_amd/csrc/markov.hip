@@ -284,8 +284,8 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
                            hipStream_t s) {
   float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
   const int ldn = part_ld(V);
-  for (int g0 = 0; g0 < R; g0 += kReqGroup) {
-    const int Rg = std::min(kReqGroup, R - g0);
+  for (int g0 = 0; g0 < R; g0 += req_group<BF16>()) {
+    const int Rg = std::min(req_group<BF16>(), R - g0);
     const int blocks = ceil_div(Rg, kTileN);
     const typename Elem<BF16>::T* Ug = Uk + (size_t)g0 * ldU;
     const int32_t* xg = xprev + (size_t)g0 * xstride;
@@ -295,8 +295,10 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
       st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
     else if (blocks <= 8)
       st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
-    else
+    else if constexpr (BF16)
       st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
+    else
+      st = DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
     if (st) return st;
   }
   return DSPARK_OK;

@@ -459,8 +459,8 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
   st = launch_status();
   if (st) return st;
   const int ncu = device_cu_count();
-  for (int g0 = 0; g0 < R; g0 += kReqGroup) {
-    const int Rg = std::min(kReqGroup, R - g0);
+  for (int g0 = 0; g0 < R; g0 += req_group<BF16>()) {
+    const int Rg = std::min(req_group<BF16>(), R - g0);
     const int blocks = ceil_div(Rg, kTileN);
 #define DSPARK_RES_LAUNCH(NW_, NB_, PERCU)                                                         \
     {                                                                                              \
@@ -477,7 +477,8 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
     }
     if (blocks <= 4) DSPARK_RES_LAUNCH(4, 1, 2)
     else if (blocks <= 8) DSPARK_RES_LAUNCH(8, 1, 1)
-    else DSPARK_RES_LAUNCH(8, 2, 1)
+    else if constexpr (BF16) DSPARK_RES_LAUNCH(8, 2, 1)
+    else return DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
 #undef DSPARK_RES_LAUNCH
     st = launch_status();
     if (st) return st;

@@ -89,6 +89,14 @@ def test_small_chain(dv, vmode, dtype):
     run_and_check(dv, sp, vmode)
 
 
+@pytest.mark.parametrize("dtype,R,r", [("bf16", 300, 32), ("f32", 150, 100)])
+def test_request_groups(dv, dtype, R, r):
+    # more requests than one GEMM launch holds (256 for bfloat16, 128 for
+    # float32): the draft and residual passes run one launch per group
+    sp = synth.small_spec(R=R, gamma=2, V=1200, r=r, d=24, dtype=dtype, seed=13)
+    run_and_check(dv, sp, "compact")
+
+
 @pytest.mark.parametrize("smode", [oracle.SCHED_GREEDY, oracle.SCHED_FIXED])
 def test_small_chain_sched_modes(dv, smode):
     sp = synth.small_spec(R=37, gamma=4, V=1777, r=48, d=40, dtype="bf16", seed=5)
