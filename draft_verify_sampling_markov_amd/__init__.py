@@ -34,6 +34,7 @@ _vp, _i, _u64, _sz, _f = _c.c_void_p, _c.c_int, _c.c_uint64, _c.c_size_t, _c.c_f
 _SIGNATURES = {
     "dspark_status_string": (_c.c_char_p, [_i]),
     "dspark_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "dspark_workspace_init": (_i, [_vp, _sz, _vp]),
     "dspark_prepacked_w2_bytes": (_sz, [_i, _i, _i]),
     "dspark_prepack_w2": (_i, [_vp, _i, _i, _i, _vp, _sz, _vp]),
     "dspark_cost_table_prepare": (_i, [_vp, _i, _vp, _i, _i, _vp]),
@@ -142,6 +143,20 @@ def workspace_bytes(call: int, R: int, gamma: int, V: int, r: int) -> int:
     return int(load_library().dspark_workspace_bytes(call, R, gamma, V, r))
 
 
+def workspace_init(ws, stream=None):
+    """Put a freshly allocated workspace (uint8 device tensor) in its initial state."""
+    _check(load_library().dspark_workspace_init(_dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                                _stream(stream)))
+    return ws
+
+
+def new_workspace(call: int, R: int, gamma: int, V: int, r: int, device, stream=None):
+    """Allocate and initialise the workspace of `call` for these sizes."""
+    torch = _torch()
+    need = workspace_bytes(call, R, gamma, V, r)
+    return workspace_init(_empty((max(need, 1),), torch.uint8, device), stream)
+
+
 def prepacked_w2_bytes(r: int, V: int, dtype: int) -> int:
     return int(load_library().dspark_prepacked_w2_bytes(r, V, dtype))
 
@@ -189,9 +204,8 @@ def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, re
     if out is None:
         out = (_empty((R, gamma), torch.int32, dev), _empty((R, gamma), torch.float32, dev),
                _empty((R, gamma), torch.float32, dev))
-    need = workspace_bytes(CALL_MARKOV_DRAFT, R, gamma, V, r)
     if ws is None:
-        ws = _empty((max(need, 1),), torch.uint8, dev)
+        ws = new_workspace(CALL_MARKOV_DRAFT, R, gamma, V, r, dev, stream)
     tokens, p, lse = out
     _check(load_library().dspark_markov_draft(
         _dev(U, "U"), _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
@@ -275,9 +289,8 @@ def verify(target_packed, cu_seqlens, anchor, tokens, p_draft, lse_draft, U, W1,
                "out_tokens": _empty((R, gamma + 1), torch.int32, dev),
                "n_out": _empty((R,), torch.int32, dev),
                "ceiling_len": _empty((R,), torch.int32, dev) if with_ceiling else None}
-    need = workspace_bytes(CALL_VERIFY, R, gamma, V, r)
     if ws is None:
-        ws = _empty((max(need, 1),), torch.uint8, dev)
+        ws = new_workspace(CALL_VERIFY, R, gamma, V, r, dev, stream)
     _check(load_library().dspark_verify(
         _dev(target_packed, "target_packed", U.dtype, (M_cap, V)), M_cap,
         _dev(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)), _dev(anchor, "anchor", torch.int32, (R,)),
@@ -329,7 +342,8 @@ def markov_logits(U_k, ldU: int, W1, W2p, x_prev, *, R: int, V: int, r: int, str
 from .chain import Chain  # noqa: E402  (needs the functions above)
 
 __all__ = [
-    "load_library", "status_string", "DsparkError", "workspace_bytes", "prepacked_w2_bytes",
+    "load_library", "status_string", "DsparkError", "workspace_bytes", "workspace_init",
+    "new_workspace", "prepacked_w2_bytes",
     "prepack_w2", "cost_table_prepare", "markov_draft", "confidence", "schedule_topb",
     "pack_ragged", "verify", "markov_logits", "markov_partials",
     "markov_select", "Chain", "EXPORTS", "F32", "BF16",

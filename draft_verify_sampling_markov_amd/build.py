@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     # keep the compiler from emitting packed-fp32 vector ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane atomics stay single atomics: the optimizer's wave-combined
+    # form reads the result back at once, which drains every load in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -15,7 +15,7 @@ from __future__ import annotations
 from typing import Dict, Optional, Sequence
 
 from . import (markov_draft, markov_partials, markov_select, confidence, schedule_topb,
-               pack_ragged, verify, prepack_w2, workspace_bytes, CALL_MARKOV_DRAFT, CALL_VERIFY,
+               pack_ragged, verify, prepack_w2, new_workspace, CALL_MARKOV_DRAFT, CALL_VERIFY,
                VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX)
 
 
@@ -57,8 +57,8 @@ class Chain:
                          "totals": e((2,), i32)}
         self.verify_out = {"accept_len": e((R,), i32), "out_tokens": e((R, g + 1), i32),
                            "n_out": e((R,), i32), "ceiling_len": e((R,), i32)}
-        self.ws_draft = e((max(1, workspace_bytes(CALL_MARKOV_DRAFT, R, g, V, r)),), u8)
-        self.ws_verify = e((max(1, workspace_bytes(CALL_VERIFY, R, g, V, r)),), u8)
+        self.ws_draft = new_workspace(CALL_MARKOV_DRAFT, R, g, V, r, dev)
+        self.ws_verify = new_workspace(CALL_VERIFY, R, g, V, r, dev)
         self.full_block = self.verify_mode in (VERIFY_STATIC, VERIFY_CAP_ACCEPT)
         self.target_packed = (inputs["target"].view(self.M_cap, V) if self.full_block
                               else e((self.M_cap, V), U.dtype))

@@ -1,5 +1,7 @@
-// C ABI utilities: status strings and workspace sizing.
+// C ABI utilities: status strings, workspace sizing and initialisation.
 #include "dspark_host.hpp"
+
+#include <algorithm>
 
 using namespace dspark;
 
@@ -24,4 +26,26 @@ extern "C" size_t dspark_workspace_bytes(int call, int R, int gamma, int V, int 
     case DSPARK_CALL_VERIFY: return verify_ws_bytes(R, gamma, V);
     default: return 0;
   }
+}
+
+// Zero-fill, 16 bytes per thread where the buffer allows (a kernel rather than
+// a memset, so the call may sit in a captured graph).
+__global__ void workspace_zero_kernel(unsigned char* __restrict__ p, size_t n) {
+  const size_t n16 = (reinterpret_cast<uintptr_t>(p) % 16) == 0 ? n / 16 : 0;
+  uint4* q = reinterpret_cast<uint4*>(p);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    q[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = n16 * 16 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = 0;
+}
+
+extern "C" int dspark_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return DSPARK_EINVAL;
+  if (ws_bytes == 0) return DSPARK_OK;
+  const size_t per_block = 256 * 16;
+  const int grid = (int)std::min<size_t>((ws_bytes + per_block - 1) / per_block, 4096);
+  hipLaunchKernelGGL(workspace_zero_kernel, dim3(grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<unsigned char*>(ws), ws_bytes);
+  return launch_status();
 }

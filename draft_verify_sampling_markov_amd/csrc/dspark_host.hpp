@@ -22,6 +22,10 @@ template <bool BF16> constexpr int req_group() { return BF16 ? 256 : 128; }
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Request groups a workspace keeps tile-queue counters for (enough for either
+// dtype).
+inline int queue_groups(int R) { return ceil_div(R, 128); }
+
 inline int rank_chunks(int r) { return ceil_div(r, 32); }
 // KC rounded up to the instantiated set {1, 2, 4, 8}.
 inline int kc_instance(int r) {

@@ -106,10 +106,11 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
-    float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk) {
+    float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk,
+    unsigned* __restrict__ queue) {
   const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
-                                         R, V, r, n_t, epi);
+                                         R, V, r, n_t, epi, queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -127,10 +128,14 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
     const int* __restrict__ xprev, int xstride, int V, int r, int n_t,
     const float2* __restrict__ part, int ldn, int c, uint64_t seed, uint64_t step,
     const uint32_t* __restrict__ req_ids, int k, int* __restrict__ tok_out,
-    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride) {
+    float* __restrict__ p_out, float* __restrict__ lse_out, int ostride,
+    unsigned* __restrict__ queue, int n_queue) {
   typedef typename Elem<BF16>::Frag Frag;
   __shared__ BlockSearchShared sh;
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  // the GEMM pass that wrote these partials has finished: put its tile-queue
+  // counters back to zero for the next one
+  if (n == 0 && tid < n_queue) queue[tid * kQueueStride] = 0u;
   const float2* prow = part + (size_t)n * ldn;
   const int t0 = tid * c;
   const int cnt = max(0, min(c, n_t - t0));
@@ -242,12 +247,20 @@ int device_cu_count() {
 }
 
 // Draft workspace: the request-major tile partials [R, ldn] (float2,
-// ldn = 64 c, c = ceil(n_t / 64), tile t of request n at n * ldn +
-// part_pos(t, c)), then one junk slot that masked lanes write to.
+// ldn = 256 c, c = ceil(n_t / 256), tile t of request n at n * ldn +
+// part_pos(t, c)), a 256-byte junk slot masked lanes write to, then the GEMM's
+// tile-queue counters (one block of kQueueWordsPerGroup words per request
+// group).
 static size_t markov_junk_offset(int R, int V) {
   return align_up((size_t)R * part_ld(V) * sizeof(float2), 256);
 }
-size_t markov_ws_bytes(int R, int V) { return markov_junk_offset(R, V) + 256; }
+static size_t markov_queue_offset(int R, int V) { return markov_junk_offset(R, V) + 256; }
+size_t markov_ws_bytes(int R, int V) {
+  return markov_queue_offset(R, V) + (size_t)queue_groups(R) * kQueueWordsPerGroup * 4;
+}
+static unsigned* markov_queue(float2* part, int R, int V) {
+  return reinterpret_cast<unsigned*>(reinterpret_cast<char*>(part) + markov_queue_offset(R, V));
+}
 
 template <bool BF16>
 static bool u_vec_ok(const void* U, long long ldU, int V) {
@@ -258,7 +271,7 @@ template <bool BF16, int KC, int NW, int NB>
 static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                                const int32_t* xprev, int xstride, int Rg, int V, int r,
-                               float2* part, float2* junk, hipStream_t s) {
+                               float2* part, float2* junk, unsigned* queue, hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
   const int per_cu = NW == 4 ? 2 : 1;
@@ -267,11 +280,11 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
                        G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, part, ldn,
-                       c, junk);
+                       c, junk, queue);
   else
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
                        dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
-                       n_t, part, ldn, c, junk);
+                       n_t, part, ldn, c, junk, queue);
   return launch_status();
 }
 
@@ -283,6 +296,7 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
                            const int32_t* xprev, int xstride, int R, int V, int r, float2* part,
                            hipStream_t s) {
   float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
+  unsigned* queue = markov_queue(part, R, V);
   const int ldn = part_ld(V);
   for (int g0 = 0; g0 < R; g0 += req_group<BF16>()) {
     const int Rg = std::min(req_group<BF16>(), R - g0);
@@ -290,13 +304,14 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
     const typename Elem<BF16>::T* Ug = Uk + (size_t)g0 * ldU;
     const int32_t* xg = xprev + (size_t)g0 * xstride;
     float2* pg = part + (size_t)g0 * ldn;
+    unsigned* qg = queue + (size_t)(g0 / req_group<BF16>()) * kQueueWordsPerGroup;
     int st;
     if (blocks <= 4)
-      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, s);
     else if (blocks <= 8)
-      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, s);
     else if constexpr (BF16)
-      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, s);
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, s);
     else
       st = DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
     if (st) return st;
@@ -312,15 +327,17 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
                          const uint32_t* req_ids, int k, int32_t* tok, float* p, float* lse,
                          int ostride, hipStream_t s) {
   const int n_t = n_vtiles(V), c = part_chunk(V), ldn = part_ld(V);
+  unsigned* queue = markov_queue(const_cast<float2*>(part), R, V);
+  const int n_queue = queue_groups(R) * kNumXcd;  // counters, kQueueStride words apart
 #define DSPARK_SELECT(CM)                                                                         \
   if (vec_w1)                                                                                    \
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, Uk, \
                        ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed, step,         \
-                       req_ids, k, tok, p, lse, ostride);                                        \
+                       req_ids, k, tok, p, lse, ostride, queue, n_queue);                        \
   else                                                                                           \
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
                        Uk, ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed,           \
-                       step, req_ids, k, tok, p, lse, ostride)
+                       step, req_ids, k, tok, p, lse, ostride, queue, n_queue)
   if (c <= 16) {
     DSPARK_SELECT(16);
   } else {

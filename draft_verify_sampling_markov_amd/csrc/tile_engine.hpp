@@ -2,12 +2,17 @@
 // [R, r] x [r, V] on the gfx950 matrix cores, shared by the draft pass and the
 // verify residual pass.
 //
-// Work split. A workgroup of NW waves walks a contiguous range of vocabulary
-// tiles (64 entries each). Ranges are laid out in XCD-major order: workgroup b
-// runs on XCD b % 8 (the dispatcher deals workgroups to the XCDs round-robin),
-// and the workgroups of one XCD take adjacent ranges, so each XCD's L2 sees
-// one contiguous stretch of the vocabulary and the per-request partial rows
-// are written mostly by one L2. The 16-request blocks of the request group
+// Work split. The vocabulary tiles (64 entries each) are cut into eight
+// contiguous ranges, one per XCD: workgroup b runs on XCD b % 8 (the
+// dispatcher deals workgroups to the XCDs round-robin), so each XCD's L2 sees
+// one contiguous stretch of the vocabulary and writes the partial rows of that
+// stretch. Inside its XCD's range, workgroup j takes tiles j, gx + j and
+// 2 gx + j (gx workgroups on the XCD), then claims further tiles one at a
+// time from the XCD's queue counter (an atomic add issued a step before the
+// tile's loads), so workgroups that run faster take more tiles and the
+// workgroups of a launch finish together. The counters sit 256 bytes apart
+// (atomics on one line serialise) and are put back to zero by the kernel that
+// consumes the partials, before it reads them. The 16-request blocks of the request group
 // are dealt to the waves round-robin, NB per wave; a wave keeps the gathered
 // W1 rows of its blocks (the B operand) in registers for the whole kernel. The
 // pre-packed W2 tile (the A operand) is staged in LDS, double buffered, and
@@ -81,22 +86,27 @@ __device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restric
   }
 }
 
-// The tiles a workgroup walks: tile(i) = base + i for i < count.
-struct TileSeq {
-  int base, count;
-  __device__ __forceinline__ int tile(int i) const { return base + min(i, count - 1); }
-};
+// Queue counters: one per XCD, kQueueStride words apart; a launch serving
+// request group g uses the counters at queue + g * kNumXcd * kQueueStride.
+constexpr int kQueueStride = 64;  // 256 bytes
+constexpr int kQueueWordsPerGroup = kNumXcd * kQueueStride;
+constexpr int kStaticTiles = 3;   // tiles per workgroup dealt before the queue
 
-// Workgroup b takes position p = (its XCD's first position) + b / 8 in
-// XCD-major order and the tiles [floor(p n_t / G), floor((p + 1) n_t / G)).
-__device__ __forceinline__ TileSeq make_tile_seq(int n_t) {
-  const int G = gridDim.x, b = blockIdx.x;
-  const int x = b % kNumXcd, j = b / kNumXcd;
-  const int p = x * (G / kNumXcd) + min(x, G % kNumXcd) + j;
-  TileSeq q;
-  q.base = (int)((long long)p * n_t / G);
-  q.count = (int)((long long)(p + 1) * n_t / G) - q.base;
-  return q;
+// Tile range [lo, hi) of this workgroup's XCD (split in proportion to the
+// workgroups each XCD runs), the XCD's workgroup count gx and this
+// workgroup's index j among them.
+struct XcdShare {
+  int lo, hi, gx, j;
+};
+__device__ __forceinline__ XcdShare xcd_share(int n_t) {
+  const int G = gridDim.x, x = blockIdx.x % kNumXcd;
+  const int first = x * (G / kNumXcd) + min(x, G % kNumXcd);
+  XcdShare s;
+  s.gx = G / kNumXcd + (x < G % kNumXcd ? 1 : 0);
+  s.j = blockIdx.x / kNumXcd;
+  s.lo = (int)((long long)n_t * first / G);
+  s.hi = (int)((long long)n_t * (first + s.gx) / G);
+  return s;
 }
 
 // One step of the pipelined tile loop, straight-line code (no branch around
@@ -104,7 +114,8 @@ __device__ __forceinline__ TileSeq make_tile_seq(int n_t) {
 // in flight): issue W2 of tile t2 into `w_issue`; multiply tile t out of `cur`;
 // hand the epilogue its rows for t (prefetched two steps ago into `u`); issue
 // the rows of t2 into `u`; store `w_ready` (W2 issued one step ago) into
-// `nxt`; barrier. t2 is the tile two steps ahead, clamped to the last one.
+// `nxt`. The caller ends the step with a barrier. t2 is the tile two steps
+// ahead, clamped into the range.
 template <bool BF16, int KC, int NW, int NB, class Epi>
 __device__ __forceinline__ void engine_step(
     int t, int t2, int V, const typename Elem<BF16>::Frag* __restrict__ src,
@@ -146,35 +157,38 @@ __device__ __forceinline__ void engine_step(
   }
 #pragma unroll
   for (int k = 0; k < Geo::kPer; ++k) nxt[Geo::slot(k, tid)] = w_ready[k];
-  __syncthreads();
 }
 
+// queue: this launch's kQueueWordsPerGroup counters (zero on entry).
 template <bool BF16, int KC, int NW, int NB, bool VEC, class Epi, typename TokFn>
 __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __restrict__ W1,
                                                 const typename Elem<BF16>::T* __restrict__ W2p,
                                                 TokFn tok, int R, int V, int r, int n_t,
-                                                const Epi& epi) {
+                                                const Epi& epi, unsigned* __restrict__ queue) {
   typedef EngineGeom<BF16, KC, NW> Geo;
   typedef typename Elem<BF16>::Frag Frag;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_grab[2];
   Frag* buf0 = reinterpret_cast<Frag*>(smem);
   Frag* buf1 = buf0 + Geo::kTileFrags;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int g = lane >> 4, nl = lane & 15;
   const Frag* src = reinterpret_cast<const Frag*>(W2p);
-  const TileSeq seq = make_tile_seq(n_t);
-  if (seq.count <= 0) return;  // workgroup-uniform; no barrier passed yet
+  const XcdShare xs = xcd_share(n_t);  // hi > lo: the grid has at most n_t workgroups
+  unsigned* counter = queue + (blockIdx.x % kNumXcd) * kQueueStride;
+  const int qbase = xs.lo + kStaticTiles * xs.gx;  // first tile the queue hands out
+  auto clampt = [&](int t) { return min(t, xs.hi - 1); };
+  int tc = xs.lo + xs.j, tn = tc + xs.gx, tnn = tn + xs.gx;  // current, next, next-but-one
+  if (tc >= xs.hi) return;  // workgroup-uniform; no barrier passed yet
 
-  // prologue: tile 0 of the sequence into LDS, W2 of tile 1 and the rows of
-  // tiles 0 and 1 in flight; the first tile's loads go out before the
-  // (token -> W1 row) gather
+  // prologue: tile tc into LDS, W2 of tn and the rows of tc and tn in flight;
+  // the first tile's loads go out before the (token -> W1 row) gather
   Frag wA[Geo::kPer], wB[Geo::kPer];
   typename Epi::Pre uA[NB], uB[NB];
-  const int t0 = seq.tile(0), t1 = seq.tile(1);
   Frag first[Geo::kPer];
   {
-    const Frag* s = src + (size_t)t0 * Geo::kTileFrags;
+    const Frag* s = src + (size_t)tc * Geo::kTileFrags;
 #pragma unroll
     for (int i = 0; i < Geo::kPer; ++i) first[i] = s[Geo::slot(i, tid)];
   }
@@ -186,12 +200,12 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
 #pragma unroll
   for (int i = 0; i < Geo::kPer; ++i) buf0[Geo::slot(i, tid)] = first[i];
   {
-    const Frag* s = src + (size_t)t1 * Geo::kTileFrags;
+    const Frag* s = src + (size_t)clampt(tn) * Geo::kTileFrags;
 #pragma unroll
     for (int i = 0; i < Geo::kPer; ++i) wA[i] = s[Geo::slot(i, tid)];
   }
   {
-    const int v0 = t0 * kTileV + 16 * g, v1 = t1 * kTileV + 16 * g;
+    const int v0 = tc * kTileV + 16 * g, v1 = clampt(tn) * kTileV + 16 * g;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       epi.load(st[nb], v0, min(16, V - v0), uA[nb]);
@@ -200,18 +214,27 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
   }
   __syncthreads();
 
-  const int pairs = seq.count >> 1;
-  for (int p = 0; p < pairs; ++p) {
-    const int i = 2 * p;
-    engine_step<BF16, KC, NW, NB>(seq.tile(i), seq.tile(i + 2), V, src, buf0, buf1, wA, wB, uA, b,
-                                  st, epi);
-    engine_step<BF16, KC, NW, NB>(seq.tile(i + 1), seq.tile(i + 3), V, src, buf1, buf0, wB, wA, uB,
-                                  b, st, epi);
-  }
-  if (seq.count & 1) {
-    const int i = seq.count - 1;
-    engine_step<BF16, KC, NW, NB>(seq.tile(i), seq.tile(i), V, src, buf0, buf1, wA, wB, uA, b, st,
-                                  epi);
+  // steady state: each step claims the tile three steps ahead (the atomic
+  // returns while the step multiplies) and publishes it before the barrier.
+  // A workgroup's tiles increase, so the first one past the range ends it.
+  for (;;) {
+    unsigned grab = 0;
+    if (tid == 0) grab = atomicAdd(counter, 1u);
+    engine_step<BF16, KC, NW, NB>(tc, clampt(tnn), V, src, buf0, buf1, wA, wB, uA, b, st, epi);
+    if (tid == 0) s_grab[0] = qbase + (int)grab;
+    __syncthreads();
+    tc = tn;
+    tn = tnn;
+    tnn = max(s_grab[0], tn + 1);
+    if (tc >= xs.hi) break;
+    if (tid == 0) grab = atomicAdd(counter, 1u);
+    engine_step<BF16, KC, NW, NB>(tc, clampt(tnn), V, src, buf1, buf0, wB, wA, uB, b, st, epi);
+    if (tid == 0) s_grab[1] = qbase + (int)grab;
+    __syncthreads();
+    tc = tn;
+    tn = tnn;
+    tnn = max(s_grab[1], tn + 1);
+    if (tc >= xs.hi) break;
   }
 }
 

@@ -307,10 +307,10 @@ __global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     Jobs jobs, int g0, int R, int gamma, int V, int r, int n_t, float2* __restrict__ rpart, int ldn,
-    int c, float2* __restrict__ junk) {
+    int c, float2* __restrict__ junk, unsigned* __restrict__ queue) {
   const ResidualEpi<BF16, VEC> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c, junk};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
-                                         r, n_t, epi);
+                                         r, n_t, epi, queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -324,10 +324,12 @@ __global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     Jobs jobs, int gamma, int V, int r, int n_t, const float2* __restrict__ rpart, int ldn, int c,
-    int* __restrict__ out_tokens) {
+    int* __restrict__ out_tokens, unsigned* __restrict__ queue, int n_queue) {
   typedef typename Elem<BF16>::Frag Frag;
   __shared__ BlockSearchShared sh;
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  // the residual GEMM has finished: put its tile-queue counters back to zero
+  if (n == 0 && tid < n_queue) queue[tid * kQueueStride] = 0u;
   const float2* prow = rpart + (size_t)n * ldn;
   const int t0 = tid * c;
   const int cnt = max(0, min(c, n_t - t0));
@@ -394,6 +396,7 @@ struct VerifyWs {
   float2* rowpart;
   float2* rpart;  // request-major residual tile partials [R, part_ld(V)]
   float2* junk;   // write target of masked lanes
+  unsigned* queue;  // tile-queue counters of the residual GEMM, per request group
   Jobs jobs;
 };
 
@@ -409,6 +412,7 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
   const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
   const size_t o_rp = take((size_t)R * part_ld(V) * sizeof(float2));
   const size_t o_junk = take(256);
+  const size_t o_q = take((size_t)queue_groups(R) * kQueueWordsPerGroup * 4);
   size_t o_j[7];
   for (int i = 0; i < 7; ++i) o_j[i] = take((size_t)R * 4);
   if (w && base) {
@@ -416,6 +420,7 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
     w->rowpart = reinterpret_cast<float2*>(b + o_row);
     w->rpart = reinterpret_cast<float2*>(b + o_rp);
     w->junk = reinterpret_cast<float2*>(b + o_junk);
+    w->queue = reinterpret_cast<unsigned*>(b + o_q);
     w->jobs.kind = reinterpret_cast<int*>(b + o_j[0]);
     w->jobs.slot = reinterpret_cast<int*>(b + o_j[1]);
     w->jobs.trow = reinterpret_cast<int*>(b + o_j[2]);
@@ -462,6 +467,7 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
   for (int g0 = 0; g0 < R; g0 += req_group<BF16>()) {
     const int Rg = std::min(req_group<BF16>(), R - g0);
     const int blocks = ceil_div(Rg, kTileN);
+    unsigned* qg = ws.queue + (size_t)(g0 / req_group<BF16>()) * kQueueWordsPerGroup;
 #define DSPARK_RES_LAUNCH(NW_, NB_, PERCU)                                                         \
     {                                                                                              \
       typedef EngineGeom<BF16, KC, NW_> G;                                                         \
@@ -469,11 +475,11 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
       if (vec_engine)                                                                              \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, true>), grid,             \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk);                           \
+                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk, qg);                       \
       else                                                                                         \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, false>), grid,            \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk);                           \
+                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk, qg);                       \
     }
     if (blocks <= 4) DSPARK_RES_LAUNCH(4, 1, 2)
     else if (blocks <= 8) DSPARK_RES_LAUNCH(8, 1, 1)
@@ -487,11 +493,11 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
   if (vec_w1)                                                                                    \
     hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, \
                        tg, Ub, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,             \
-                       out_tokens);                                                              \
+                       out_tokens, ws.queue, queue_groups(R) * kNumXcd);                         \
   else                                                                                           \
     hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
                        tg, Ub, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,             \
-                       out_tokens)
+                       out_tokens, ws.queue, queue_groups(R) * kNumXcd)
   if (c <= 16) {
     DSPARK_RES_SELECT(16);
   } else {

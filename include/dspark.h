@@ -11,7 +11,8 @@
  *   dspark_verify         lossless rejection-sampling verification
  *
  * plus host/device utilities (W2 pre-packing, cost-table preparation,
- * workspace sizing, status strings) and one diagnostic call.
+ * workspace sizing and initialisation, status strings) and one diagnostic
+ * call.
  *
  * Sources, cited by page title and section:
  *   [digest]  "DSpark: Confidence-Scheduled Speculative Decoding with
@@ -101,8 +102,18 @@ const char* dspark_status_string(int status);
 
 /* Bytes of workspace `call` needs for these sizes (0 for calls that need
  * none, and for invalid sizes). The verify workspace does not depend on M_cap:
- * a well-formed pack never has more than R * (gamma + 1) rows. */
+ * a well-formed pack never has more than R * (gamma + 1) rows.
+ *
+ * Workspaces hold the counters the GEMM passes deal vocabulary tiles from. A
+ * workspace must be initialised once, before its first use, with
+ * dspark_workspace_init (or be zero-filled by other means); every completed
+ * call leaves it initialised. A workspace serves one call at a time. */
 size_t dspark_workspace_bytes(int call, int R, int gamma, int V, int r);
+
+/* Zero-fill a workspace of ws_bytes bytes on `stream` (a kernel rather than a
+ * memset, so it may be captured in a graph). DSPARK_EINVAL for a null ws,
+ * DSPARK_EHIP if the launch fails. */
+int dspark_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of the pre-packed W2 buffer for rank r, vocabulary V and dtype. */
 size_t dspark_prepacked_w2_bytes(int r, int V, int dtype);
@@ -244,7 +255,10 @@ int dspark_verify(const void* target_packed, int M_cap, const int32_t* cu_seqlen
  * units) and tile t sits at (t % c) * 256 + t / c in it -- the order in which
  * the 256 threads of dspark_markov_select read them. U_k rows are ldU elements
  * apart; x_prev[n * xstride] is the previous token of request n. part must hold
- * dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, R, 1, V, r) bytes. */
+ * dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, R, 1, V, r) bytes and be an
+ * initialised workspace. The call uses up the workspace's tile queue; the
+ * dspark_markov_select call that consumes these partials restores it, so the
+ * two calls alternate on one workspace. */
 int dspark_markov_partials(const void* U_k, long long ldU, const void* W1, const void* W2p,
                            const int32_t* x_prev, int xstride, int R, int V, int r, int dtype,
                            void* part, size_t part_bytes, void* stream);

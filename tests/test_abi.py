@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -67,6 +67,7 @@ def test_host_validation_rejects_before_launch():
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 17, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 600, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 129, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_workspace_init(None, 256, None) == EINVAL
     assert lib.dspark_markov_draft(None, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == EINVAL
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, p, 8, None) == EWS
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, None, 1 << 30, None) == EWS
