@@ -127,7 +127,12 @@ __global__ __launch_bounds__(kRowThreads) void row_partials_kernel(
 // decide
 // ---------------------------------------------------------------------------
 
-template <bool BF16>
+// One wave per request, lane l for slot l + 1 (its packed row c0 + l). Every
+// load is issued up front from clamped addresses (no branch around a load);
+// one Philox block per lane gives that slot's accept, residual and bonus
+// uniforms, so the correction job's uniform is a lane pick once A is known.
+// CMAX > 0: the row's chunk partials (n_chunks <= CMAX) sit in registers.
+template <bool BF16, int CMAX>
 __global__ __launch_bounds__(256) void decide_kernel(
     const typename Elem<BF16>::T* __restrict__ target, int V, int n_chunks,
     const float2* __restrict__ part, const int* __restrict__ cu_seqlens,
@@ -145,62 +150,66 @@ __global__ __launch_bounds__(256) void decide_kernel(
   const int c0 = min(max(cu_seqlens[req], 0), rows_ws - 1);
   const int c1 = min(max(cu_seqlens[req + 1], c0 + 1), rows_ws);
   const int Lv = min(c1 - c0 - 1, gamma);
-  float lse = 0.0f;
-  bool acc = false;
-  if (lane <= Lv) {
-    const int row = c0 + lane;
-    float m = -INFINITY, S = 0.0f;
-    constexpr int CMAX = 32;
-    if (n_chunks <= CMAX) {  // all partials of the row in flight at once
-      float2 pv[CMAX];
+  const int jl = min(lane, gamma - 1);  // this lane's slot, clamped for the loads
+  const int tok = tokens[(size_t)req * gamma + jl];
+  const float pd = p_draft[(size_t)req * gamma + jl];
+  const float lsed = lse_draft[(size_t)req * gamma + jl];
+  const int anc = anchor[req];
+  const int wl = mode == DSPARK_VERIFY_CAP_ACCEPT ? win_len[req] : gamma;
+  const int row = c0 + min(lane, Lv);
+  const float zt = to_f32(target[(size_t)row * V + clamp_token(tok, V)]);
+  float m = -INFINITY, S = 0.0f;
+  if constexpr (CMAX > 0) {  // all partials of the row in flight at once
+    float2 pv[CMAX];
 #pragma unroll
-      for (int c = 0; c < CMAX; ++c)
-        pv[c] = c < n_chunks ? part[(size_t)row * n_chunks + c] : make_float2(-INFINITY, 0.0f);
+    for (int c = 0; c < CMAX; ++c) pv[c] = part[(size_t)row * n_chunks + min(c, n_chunks - 1)];
 #pragma unroll
-      for (int c = 0; c < CMAX; ++c) m = fmaxf(m, pv[c].x);
+    for (int c = 0; c < CMAX; ++c) m = fmaxf(m, c < n_chunks ? pv[c].x : -INFINITY);
 #pragma unroll
-      for (int c = 0; c < CMAX; ++c)
-        if (c < n_chunks) S += pv[c].y * __expf(pv[c].x - m);
-    } else {
-      for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, part[(size_t)row * n_chunks + c].x);
-      for (int c = 0; c < n_chunks; ++c) {
-        const float2 pv = part[(size_t)row * n_chunks + c];
-        S += pv.y * __expf(pv.x - m);
-      }
-    }
-    lse = m + __logf(S);
-    if (lane < Lv) {
-      const int x = clamp_token(tokens[(size_t)req * gamma + lane], V);
-      const float zt = to_f32(target[(size_t)row * V + x]);
-      const float pt = __expf(zt - lse);
-      const float ratio = pt / p_draft[(size_t)req * gamma + lane];
-      const float u1 = slot_uniform(seed, step, req_ids[req], lane + 1, kPurposeAccept);
-      acc = u1 < ratio;
+    for (int c = 0; c < CMAX; ++c) S += c < n_chunks ? pv[c].y * __expf(pv[c].x - m) : 0.0f;
+  } else {
+    for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, part[(size_t)row * n_chunks + c].x);
+    for (int c = 0; c < n_chunks; ++c) {
+      const float2 pv = part[(size_t)row * n_chunks + c];
+      S += pv.y * __expf(pv.x - m);
     }
   }
+  // this lane's Philox block (slot lane + 1): accept, residual and bonus words
+  const U64x4 blk = philox4x64_10((uint64_t)(lane + 1), (uint64_t)req_ids[req], step, 0ull, seed, 0ull);
+  const float to24 = 5.9604644775390625e-8f;  // 2^-24
+  const float u_acc = (float)(uint32_t)(blk.w[kPurposeAccept] >> 40) * to24;
+  const float u_res = (float)(uint32_t)(blk.w[kPurposeResidual] >> 40) * to24;
+  const float u_bon = (float)(uint32_t)(blk.w[kPurposeBonus] >> 40) * to24;
+  const float lse = m + __logf(S);
+  const float pt = __expf(zt - lse);
+  const float ratio = pt / pd;
+  const bool acc = lane < Lv && u_acc < ratio;
+
   const unsigned long long mask = __ballot(acc);
   const int A_full = min(__ffsll((long long)~mask) - 1, Lv);
-  int Lc = Lv;
-  if (mode == DSPARK_VERIFY_CAP_ACCEPT) Lc = min(min(max(win_len[req], 0), gamma), Lv);
+  const int Lc = mode == DSPARK_VERIFY_CAP_ACCEPT ? min(min(max(wl, 0), gamma), Lv) : Lv;
   const int A = min(A_full, Lc);
   const bool residual = A < Lc;
   const int slot = residual ? A + 1 : Lc + 1;
-  const int rel = slot - 1;  // packed row offset of the slot's target row
-  const float lse_t = __shfl(lse, rel, kWave);
+  const int rel = slot - 1;  // packed row offset of the slot's target row, a lane index
+  const float lse_t = readlane_f(lse, rel);
+  const float u_job = readlane_f(residual ? u_res : u_bon, rel);
+  const int xprev = A == 0 ? anc : __builtin_amdgcn_readlane(tok, A - 1);
+  const float lse_d = residual ? readlane_f(lsed, A) : 0.0f;
   if (lane == 0) {
     jobs.kind[req] = residual ? 0 : 1;
     jobs.slot[req] = slot;
     jobs.trow[req] = c0 + rel;
-    jobs.xprev[req] = A == 0 ? anchor[req] : tokens[(size_t)req * gamma + A - 1];
-    jobs.u[req] = slot_uniform(seed, step, req_ids[req], slot, residual ? kPurposeResidual : kPurposeBonus);
+    jobs.xprev[req] = xprev;
+    jobs.u[req] = u_job;
     jobs.lse_t[req] = lse_t;
-    jobs.lse_d[req] = residual ? lse_draft[(size_t)req * gamma + A] : 0.0f;
+    jobs.lse_d[req] = lse_d;
     accept_len[req] = A;
     n_out[req] = A + 1;
     if (ceiling) ceiling[req] = A_full;
   }
   if (lane <= gamma && lane != A)
-    out_tokens[(size_t)req * (gamma + 1) + lane] = lane < A ? tokens[(size_t)req * gamma + lane] : -1;
+    out_tokens[(size_t)req * (gamma + 1) + lane] = lane < A ? tok : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -458,9 +467,14 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
                      vec, nch, cu, R, rows_ws, ws.rowpart);
   int st = launch_status();
   if (st) return st;
-  hipLaunchKernelGGL((decide_kernel<BF16>), dim3(ceil_div(R, 4)), dim3(256), 0, s, tg, V, nch,
-                     ws.rowpart, cu, anchor, tokens, p_draft, lse_draft, win_len, mode, seed, step,
-                     req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
+  if (nch <= 32)
+    hipLaunchKernelGGL((decide_kernel<BF16, 32>), dim3(ceil_div(R, 4)), dim3(256), 0, s, tg, V, nch,
+                       ws.rowpart, cu, anchor, tokens, p_draft, lse_draft, win_len, mode, seed, step,
+                       req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
+  else
+    hipLaunchKernelGGL((decide_kernel<BF16, 0>), dim3(ceil_div(R, 4)), dim3(256), 0, s, tg, V, nch,
+                       ws.rowpart, cu, anchor, tokens, p_draft, lse_draft, win_len, mode, seed, step,
+                       req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
   st = launch_status();
   if (st) return st;
   const int ncu = device_cu_count();
