@@ -58,6 +58,17 @@ __global__ void prepack_w2_kernel(const T* __restrict__ W2, int r, int V, int KC
 // pass A: bias GEMM + U add + per-tile softmax partials
 // ---------------------------------------------------------------------------
 
+// The slot's Philox draws, taken by the GEMM pass so the select that follows
+// only loads them: in workgroup b, lane l of wave 0 draws for request
+// 64 b + l, in the prologue once its tile loads are out (the tile queue hands
+// these workgroups fewer tiles). u_out == nullptr: the select draws itself.
+struct DrawArgs {
+  uint64_t seed, step;
+  const uint32_t* req_ids;
+  int k;
+  float* u_out;
+};
+
 // Epilogue of the draft pass: z = bias + U_k, then the tile's softmax partial
 // (max, sum of exp(z - max)) per request, merged over the lane's four groups
 // in a fixed butterfly order, stored at part[n * ldn + part_pos(t, c)]. Lanes
@@ -78,6 +89,7 @@ struct MarkovEpi {
   float2* part;
   int ldn, c;
   float2* junk;
+  DrawArgs draw;
 
   __device__ __forceinline__ St prepare(int n) const {
     St s;
@@ -85,6 +97,12 @@ struct MarkovEpi {
     s.active = n < R;
     s.row = U + (size_t)min(n, R - 1) * ldU;
     return s;
+  }
+  // called once per workgroup in the engine's prologue
+  __device__ __forceinline__ void side_work() const {
+    const int q = (int)blockIdx.x * kWave + (int)threadIdx.x;
+    if (draw.u_out != nullptr && threadIdx.x < kWave && q < R)
+      draw.u_out[q] = slot_uniform(draw.seed, draw.step, draw.req_ids[q], draw.k, kPurposeDraft);
   }
   __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
     load16_clamped<BF16, VEC>(s.row, v0, nvalid, V, p);
@@ -107,8 +125,8 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
     float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk,
-    unsigned* __restrict__ queue) {
-  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk};
+    unsigned* __restrict__ queue, DrawArgs draw) {
+  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk, draw};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
                                          R, V, r, n_t, epi, queue);
 }
@@ -129,7 +147,7 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
     const float2* __restrict__ part, int ldn, int c, uint64_t seed, uint64_t step,
     const uint32_t* __restrict__ req_ids, int k, int* __restrict__ tok_out,
     float* __restrict__ p_out, float* __restrict__ lse_out, int ostride,
-    unsigned* __restrict__ queue, int n_queue) {
+    unsigned* __restrict__ queue, int n_queue, const float* __restrict__ u_pre) {
   typedef typename Elem<BF16>::Frag Frag;
   __shared__ BlockSearchShared sh;
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -149,8 +167,9 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
   const int x = clamp_token(xprev[(size_t)n * xstride], V);
   Frag b[KC];
   load_b_row<BF16, KC, VW>(W1 + (size_t)x * r, r, lane, b);
-  // the Philox draw (scalar work) overlaps the loads in flight
-  const float u = slot_uniform(seed, step, req_ids[n], k, kPurposeDraft);
+  // the draw was taken by the GEMM pass, or is taken here (scalar work that
+  // overlaps the loads in flight)
+  const float u = u_pre != nullptr ? u_pre[n] : slot_uniform(seed, step, req_ids[n], k, kPurposeDraft);
   float m;
   WaveSearch ws;
   if constexpr (CMAX > 0) {
@@ -255,8 +274,12 @@ static size_t markov_junk_offset(int R, int V) {
   return align_up((size_t)R * part_ld(V) * sizeof(float2), 256);
 }
 static size_t markov_queue_offset(int R, int V) { return markov_junk_offset(R, V) + 256; }
-size_t markov_ws_bytes(int R, int V) {
+static size_t markov_u_offset(int R, int V) {
   return markov_queue_offset(R, V) + (size_t)queue_groups(R) * kQueueWordsPerGroup * 4;
+}
+size_t markov_ws_bytes(int R, int V) { return markov_u_offset(R, V) + align_up((size_t)R * 4, 256); }
+static float* markov_u(float2* part, int R, int V) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(part) + markov_u_offset(R, V));
 }
 static unsigned* markov_queue(float2* part, int R, int V) {
   return reinterpret_cast<unsigned*>(reinterpret_cast<char*>(part) + markov_queue_offset(R, V));
@@ -271,7 +294,8 @@ template <bool BF16, int KC, int NW, int NB>
 static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                                const int32_t* xprev, int xstride, int Rg, int V, int r,
-                               float2* part, float2* junk, unsigned* queue, hipStream_t s) {
+                               float2* part, float2* junk, unsigned* queue, DrawArgs draw,
+                               hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
   const int per_cu = NW == 4 ? 2 : 1;
@@ -280,11 +304,11 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
                        G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, part, ldn,
-                       c, junk, queue);
+                       c, junk, queue, draw);
   else
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
                        dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
-                       n_t, part, ldn, c, junk, queue);
+                       n_t, part, ldn, c, junk, queue, draw);
   return launch_status();
 }
 
@@ -294,7 +318,7 @@ template <bool BF16, int KC>
 static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                            const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                            const int32_t* xprev, int xstride, int R, int V, int r, float2* part,
-                           hipStream_t s) {
+                           DrawArgs draw, hipStream_t s) {
   float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
   unsigned* queue = markov_queue(part, R, V);
   const int ldn = part_ld(V);
@@ -305,13 +329,18 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
     const int32_t* xg = xprev + (size_t)g0 * xstride;
     float2* pg = part + (size_t)g0 * ldn;
     unsigned* qg = queue + (size_t)(g0 / req_group<BF16>()) * kQueueWordsPerGroup;
+    DrawArgs dg = draw;
+    if (dg.u_out) {
+      dg.u_out += g0;
+      dg.req_ids += g0;
+    }
     int st;
     if (blocks <= 4)
-      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, s);
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, dg, s);
     else if (blocks <= 8)
-      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, dg, s);
     else if constexpr (BF16)
-      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, dg, s);
     else
       st = DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
     if (st) return st;
@@ -325,7 +354,7 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
                          const int32_t* xprev, int xstride, int R, int V, int r,
                          const float2* part, uint64_t seed, uint64_t step,
                          const uint32_t* req_ids, int k, int32_t* tok, float* p, float* lse,
-                         int ostride, hipStream_t s) {
+                         int ostride, const float* u_pre, hipStream_t s) {
   const int n_t = n_vtiles(V), c = part_chunk(V), ldn = part_ld(V);
   unsigned* queue = markov_queue(const_cast<float2*>(part), R, V);
   const int n_queue = queue_groups(R) * kNumXcd;  // counters, kQueueStride words apart
@@ -333,11 +362,11 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
   if (vec_w1)                                                                                    \
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, true>), dim3(R), dim3(kSelThreads), 0, s, Uk, \
                        ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed, step,         \
-                       req_ids, k, tok, p, lse, ostride, queue, n_queue);                        \
+                       req_ids, k, tok, p, lse, ostride, queue, n_queue, u_pre);                 \
   else                                                                                           \
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
                        Uk, ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed,           \
-                       step, req_ids, k, tok, p, lse, ostride, queue, n_queue)
+                       step, req_ids, k, tok, p, lse, ostride, queue, n_queue, u_pre)
   if (c <= 16) {
     DSPARK_SELECT(16);
   } else {
@@ -362,12 +391,13 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
     const int* xprev = (k == 1) ? anchor : tokens + (k - 2);
     const int xstride = (k == 1) ? 1 : gamma;
     const T* Uk = Ub + (size_t)(k - 1) * V;
+    const DrawArgs draw{seed, step, req_ids, k, markov_u(part, R, V)};
     int st = launch_partials<BF16, KC>(Uk, ldU, vec_u && vec_w1, W1b, W2b, xprev, xstride, R, V, r,
-                                       part, s);
+                                       part, draw, s);
     if (st) return st;
     st = launch_select<BF16, KC>(Uk, ldU, vec_u, vec_w1, W1b, W2b, xprev, xstride, R, V, r, part,
                                  seed, step, req_ids, k, tokens + (k - 1), p_draft + (k - 1),
-                                 lse_draft + (k - 1), gamma, s);
+                                 lse_draft + (k - 1), gamma, draw.u_out, s);
     if (st) return st;
   }
   return DSPARK_OK;
@@ -379,8 +409,10 @@ static int launch_partials_api(const void* U, long long ldU, const void* W1, con
                                float2* part, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
   const bool vec = u_vec_ok<BF16>(U, ldU, V) && w1_vec_ok(W1, r);
+  const DrawArgs none{0, 0, nullptr, 0, nullptr};
   return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
-                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, s);
+                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, none,
+                                   s);
 }
 
 template <bool BF16, int KC>
@@ -524,7 +556,7 @@ static int launch_select_api(const void* U, long long ldU, const void* W1, const
   return launch_select<BF16, KC>(static_cast<const T*>(U), ldU, u_vec_ok<BF16>(U, ldU, V),
                                  w1_vec_ok(W1, r), static_cast<const T*>(W1),
                                  static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, seed,
-                                 step, req_ids, k, tok, p, lse, ostride, s);
+                                 step, req_ids, k, tok, p, lse, ostride, nullptr, s);
 }
 
 extern "C" int dspark_markov_select(const void* U_k, long long ldU, const void* W1,

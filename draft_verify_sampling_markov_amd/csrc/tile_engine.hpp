@@ -31,6 +31,7 @@
 //   void load(const St&, int v0, int nvalid, Pre&)            // issue loads
 //   void finish(const St&, int v0, int nvalid, const f32x4 acc[4],
 //               const Pre&, int t, int lane)                  // consume, write
+//   void side_work()                // once, in the prologue, loads in flight
 #pragma once
 
 #include "dspark_device.hpp"
@@ -212,6 +213,7 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
       epi.load(st[nb], v1, min(16, V - v1), uB[nb]);
     }
   }
+  epi.side_work();
   __syncthreads();
 
   // steady state: each step claims the tile three steps ahead (the atomic

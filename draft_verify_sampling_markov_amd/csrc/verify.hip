@@ -284,6 +284,7 @@ struct ResidualEpi {
     s.lse_d = jobs.lse_d[s.ng];
     return s;
   }
+  __device__ __forceinline__ void side_work() const {}
   __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
     load16_clamped<BF16, VEC>(s.trow, v0, nvalid, V, p.zt);
     load16_clamped<BF16, VEC>(s.urow, v0, nvalid, V, p.u);
