@@ -106,6 +106,51 @@ def cpu_baseline(spec, inp, mode_name: str, budget_s: float = 12.0, n_req: int =
                       f"{dt:.1f} s (float64 numpy, BLAS threads={threads})"}
 
 
+def measure_decode(dv, dev, inp, spec, B_cap: int, steps: int, lag: int):
+    """The decode loop in compact mode: each step drafts from the token the
+    previous one committed, sizes its budget from the survivals of `lag` steps
+    before, and verifies the scheduled windows. Its target stand-in (a gather
+    of the windows' target rows, which a serving engine's target forward would
+    write) runs inside every step and is timed on its own as well. Times
+    `steps` steps run eagerly and as replays of one captured graph, from the
+    same state, and counts the tokens they commit with a recorded rerun."""
+    import numpy as np
+    import torch
+    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B_cap,
+                  verify_mode=dv.VERIFY_COMPACT, seed=1, step=1000)
+    ch.decode(lag + 3, lag=lag)                      # fills the history, loads every kernel
+    ch.decode(1, lag=lag, graph=True)                # captures the steady-state step
+    torch.cuda.synchronize()
+    st = ch.save_state()
+    out = {"lag": lag, "steps": steps, "verify": "compact"}
+    for name, graph in (("eager", False), ("graph", True)):
+        ch.load_state(st)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ch.decode(steps, lag=lag, graph=graph)
+        torch.cuda.synchronize()
+        out[f"{name}_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / steps, 4)
+    ch.load_state(st)
+    rec = ch.decode(steps, lag=lag, record=True)
+    torch.cuda.synchronize()
+    committed = float(np.mean([r["n_out"].sum() for r in rec]))
+    slots = float(np.mean([int(r["K"][0]) for r in rec]))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        ch.gather_target()
+    ev[1].record()
+    torch.cuda.synchronize()
+    out["target_standin_ms"] = round(ev[0].elapsed_time(ev[1]) / steps, 4)
+    out["committed_tokens_per_step"] = round(committed, 2)
+    out["verified_slots_per_step"] = round(slots, 1)
+    out["committed_tokens_per_s_graph"] = round(committed / (out["graph_ms_per_step"] * 1e-3), 1)
+    log(f"[bench] decode loop: eager {out['eager_ms_per_step']} ms/step, graph "
+        f"{out['graph_ms_per_step']} ms/step (target stand-in {out['target_standin_ms']} ms), "
+        f"{committed:.1f} tokens and {slots:.0f} verified slots per step")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +162,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="steps of per-kernel event timing (default: --steps)")
+    ap.add_argument("--decode-steps", type=int, default=20,
+                    help="steps of the multi-step decode loop (compact verify, budget from "
+                         "survivals --lag steps old) timed eagerly and as graph replays; 0 skips")
+    ap.add_argument("--lag", type=int, default=2)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one 256 MiB device-to-device copy (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -239,6 +288,8 @@ def main() -> int:
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
     }
+    if args.decode_steps > 0:
+        line["decode"] = measure_decode(dv, dev, inp, spec, B_cap, args.decode_steps, args.lag)
     if args.calibrate_copy:
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

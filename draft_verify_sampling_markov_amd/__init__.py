@@ -6,7 +6,7 @@ raises if the library is missing -- there is no fallback path.
 
 Calls (same names as the C ABI in include/dspark.h, without the prefix):
     prepack_w2, markov_draft, confidence, schedule_topb, pack_ragged, verify,
-    cost_table_prepare, workspace_bytes, markov_logits
+    advance, cost_table_prepare, workspace_bytes, markov_logits
 and ``Chain``, which holds preallocated buffers for repeated steps.
 """
 from __future__ import annotations
@@ -38,7 +38,7 @@ _SIGNATURES = {
     "dspark_prepacked_w2_bytes": (_sz, [_i, _i, _i]),
     "dspark_prepack_w2": (_i, [_vp, _i, _i, _i, _vp, _sz, _vp]),
     "dspark_cost_table_prepare": (_i, [_vp, _i, _vp, _i, _i, _vp]),
-    "dspark_markov_draft": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _i, _i, _i, _i, _i,
+    "dspark_markov_draft": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i, _i, _i,
                                  _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_confidence": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _vp]),
@@ -46,12 +46,13 @@ _SIGNATURES = {
     "dspark_pack_ragged": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
     "dspark_verify": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _u64,
-                           _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+                           _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dspark_advance": (_i, [_vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _vp]),
     "dspark_markov_logits": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "dspark_markov_partials": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz,
                                     _vp]),
-    "dspark_markov_select": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _vp, _u64, _u64, _vp, _i, _i,
-                                  _i, _i, _i, _vp, _vp, _vp, _i, _vp]),
+    "dspark_markov_select": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _vp, _u64, _u64, _vp, _vp,
+                                  _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -191,9 +192,10 @@ def cost_table_prepare(raw_step_time_s: Sequence[float], tiers: Sequence[int],
 # hot calls
 # ---------------------------------------------------------------------------
 
-def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, req_ids=None,
-                 out=None, ws=None, stream=None):
+def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, step_dev=None,
+                 req_ids=None, out=None, ws=None, stream=None):
     """U [R, gamma, V]; W1 [V, r]; W2p pre-packed; anchor [R] int32.
+    step_dev: optional int64 [1] device tensor holding the step (overrides step).
     Returns (tokens int32 [R, gamma], p_draft f32, lse_draft f32)."""
     torch = _torch()
     R, gamma, V = U.shape
@@ -209,7 +211,8 @@ def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, re
     tokens, p, lse = out
     _check(load_library().dspark_markov_draft(
         _dev(U, "U"), _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
-        _dev(anchor, "anchor", torch.int32, (R,)), seed, step, _dev(req_ids, "req_ids", None, (R,)),
+        _dev(anchor, "anchor", torch.int32, (R,)), seed, step,
+        _opt(step_dev, "step_dev", torch.int64, (1,)), _dev(req_ids, "req_ids", None, (R,)),
         R, gamma, V, r, dt, _dev(tokens, "tokens", torch.int32, (R, gamma)),
         _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
         _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
@@ -275,7 +278,7 @@ def pack_ragged(anchor, tokens, win_len, tiers: Sequence[int], M_cap: int, out=N
 
 
 def verify(target_packed, cu_seqlens, anchor, tokens, p_draft, lse_draft, U, W1, W2p, *, r: int,
-           mode: int, win_len=None, seed: int = 0, step: int = 0, req_ids=None,
+           mode: int, win_len=None, seed: int = 0, step: int = 0, step_dev=None, req_ids=None,
            with_ceiling: bool = True, out=None, ws=None, stream=None):
     """Returns dict: accept_len [R], out_tokens [R, gamma+1], n_out [R], ceiling_len [R] or None."""
     torch = _torch()
@@ -298,7 +301,8 @@ def verify(target_packed, cu_seqlens, anchor, tokens, p_draft, lse_draft, U, W1,
         _dev(lse_draft, "lse_draft", torch.float32, (R, gamma)), _dev(U, "U"),
         _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
         _opt(win_len, "win_len", torch.int32, (R,)), int(mode), seed, step,
-        _dev(req_ids, "req_ids", None, (R,)), R, gamma, V, r, _dtype_code(U),
+        _opt(step_dev, "step_dev", torch.int64, (1,)), _dev(req_ids, "req_ids", None, (R,)), R,
+        gamma, V, r, _dtype_code(U),
         _dev(out["accept_len"], "accept_len", torch.int32, (R,)),
         _dev(out["out_tokens"], "out_tokens", torch.int32, (R, gamma + 1)),
         _dev(out["n_out"], "n_out", torch.int32, (R,)),
@@ -318,12 +322,13 @@ def markov_partials(U_k, ldU: int, W1, W2p, x_prev, xstride: int, *, R: int, V: 
 
 def markov_select(U_k, ldU: int, W1, W2p, x_prev, xstride: int, part, *, k: int, R: int, V: int,
                   r: int, seed: int, step: int, req_ids, tok_out, p_out, lse_out, ostride: int,
-                  stream=None):
+                  step_dev=None, stream=None):
     """One slot's draw from the partials of markov_partials (pointer-level outputs:
     tok_out/p_out/lse_out may be strided views' base pointers given as tensors)."""
     _check(load_library().dspark_markov_select(
         U_k.data_ptr(), int(ldU), _dev(W1, "W1", U_k.dtype, (V, r)), _dev(W2p, "W2p", U_k.dtype),
-        x_prev.data_ptr(), int(xstride), _dev(part, "part"), seed, step, req_ids.data_ptr(), int(k),
+        x_prev.data_ptr(), int(xstride), _dev(part, "part"), seed, step,
+        _opt(step_dev, "step_dev", _torch().int64, (1,)), req_ids.data_ptr(), int(k),
         R, V, r, _dtype_code(U_k), tok_out.data_ptr(), p_out.data_ptr(), lse_out.data_ptr(),
         int(ostride), _stream(stream)))
 
@@ -339,6 +344,24 @@ def markov_logits(U_k, ldU: int, W1, W2p, x_prev, *, R: int, V: int, r: int, str
     return z
 
 
+def advance(anchor, accept_len, out_tokens, *, step_dev=None, surv_hist=None, surv=None,
+            stream=None):
+    """Carry a decode loop to its next step on the device: anchor <- the token
+    committed last (out_tokens[r, accept_len[r]]), step_dev += 1, and the
+    survival history surv_hist [n_hist, R, gamma] shifted by one level with
+    surv entering at level 0."""
+    torch = _torch()
+    R, g1 = out_tokens.shape
+    gamma = g1 - 1
+    n_hist = 0 if surv_hist is None else surv_hist.shape[0]
+    _check(load_library().dspark_advance(
+        _dev(anchor, "anchor", torch.int32, (R,)), _dev(accept_len, "accept_len", torch.int32, (R,)),
+        _dev(out_tokens, "out_tokens", torch.int32), R, gamma,
+        _opt(step_dev, "step_dev", torch.int64, (1,)),
+        _opt(surv_hist, "surv_hist", torch.float32, (n_hist, R, gamma)),
+        _opt(surv, "surv", torch.float32, (R, gamma)), n_hist, _stream(stream)))
+
+
 from .chain import Chain  # noqa: E402  (needs the functions above)
 
 __all__ = [
@@ -346,7 +369,7 @@ __all__ = [
     "new_workspace", "prepacked_w2_bytes",
     "prepack_w2", "cost_table_prepare", "markov_draft", "confidence", "schedule_topb",
     "pack_ragged", "verify", "markov_logits", "markov_partials",
-    "markov_select", "Chain", "EXPORTS", "F32", "BF16",
+    "markov_select", "advance", "Chain", "EXPORTS", "F32", "BF16",
     "VERIFY_STATIC", "VERIFY_COMPACT", "VERIFY_CAP_ACCEPT", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "VERIFY_MODES", "SCHED_MODES",
 ]

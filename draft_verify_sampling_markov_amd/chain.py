@@ -1,8 +1,14 @@
-"""One decode step of the DSpark chain over preallocated device buffers.
+"""Decode steps of the DSpark chain over preallocated device buffers.
 
 draft (dspark_markov_draft) -> confidence (dspark_confidence) -> schedule
 (dspark_schedule_topb) -> pack (dspark_pack_ragged) -> [target forward] ->
 verify (dspark_verify), all enqueued on one stream with no host read-back.
+``decode`` repeats the step, carrying x_0, the Philox step and a short
+survival history from one step to the next on the device (dspark_advance), so
+that the verify budget can come from confidences ``lag`` steps old (DSpark
+digest, "Infra": two steps back; vLLM adaptive verification page, "Execution
+pipeline": the previous step); the steady-state step can be captured once
+into a HIP graph and replayed.
 
 The target forward is outside this library. ``gather_target`` stands in for
 it: it copies the target logits of each packed row (request r, slot j) from a
@@ -15,8 +21,8 @@ from __future__ import annotations
 from typing import Dict, Optional, Sequence
 
 from . import (markov_draft, markov_partials, markov_select, confidence, schedule_topb,
-               pack_ragged, verify, prepack_w2, new_workspace, CALL_MARKOV_DRAFT, CALL_VERIFY,
-               VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX)
+               pack_ragged, verify, advance, prepack_w2, new_workspace, CALL_MARKOV_DRAFT,
+               CALL_VERIFY, VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX, SCHED_GREEDY)
 
 
 class Chain:
@@ -25,6 +31,8 @@ class Chain:
     inputs: dict of device tensors U [R, gamma, V], W1 [V, r], W2 [r, V],
     target [R, gamma+1, V] (same dtype), h [R, gamma, d], anchor [R] int32,
     w [d+r] f32, req_ids [R] int32, sps_milli [M_max+1] int32 (uint32 bits).
+    The chain keeps its own copy of the anchors (``self.anchor``), which
+    ``decode`` moves on from step to step.
     """
 
     def __init__(self, inputs: Dict[str, "object"], *, b: float, tiers: Sequence[int],
@@ -44,6 +52,13 @@ class Chain:
         self.K_fixed = int(K_fixed)
         self.seed, self.step = int(seed), int(step)
         dev = U.device
+        self.anchor = inputs["anchor"].clone()
+        self.step_dev = torch.tensor([self.step], dtype=torch.int64, device=dev)
+        self.surv_hist = None
+        self._graph = None
+        self._hist_steps = 0      # steps whose survivals the history holds (at most lag)
+        self._lag = None          # history depth the buffers and graph were made for
+        self._warm = False        # an eager decode step has run (every kernel loaded)
         R, g, V, r = self.R, self.gamma, self.V, self.r
         self.M_cap = R * (g + 1)
         self.W2p = W2p if W2p is not None else prepack_w2(inputs["W2"])
@@ -66,7 +81,7 @@ class Chain:
     # -- stages ------------------------------------------------------------
     def draft(self):
         i = self.inp
-        return markov_draft(i["U"], i["W1"], self.W2p, i["anchor"], r=self.r, seed=self.seed,
+        return markov_draft(i["U"], i["W1"], self.W2p, self.anchor, r=self.r, seed=self.seed,
                             step=self.step, req_ids=i["req_ids"], out=self.draft_out,
                             ws=self.ws_draft)
 
@@ -82,7 +97,7 @@ class Chain:
         Uf, tf, pf, lf = U.view(-1), tok.view(-1), p.view(-1), lse.view(-1)
         for k in range(1, g + 1):
             Uk = Uf[(k - 1) * V:]
-            x_prev, xs = (i["anchor"], 1) if k == 1 else (tf[k - 2:], g)
+            x_prev, xs = (self.anchor, 1) if k == 1 else (tf[k - 2:], g)
             if events is not None:
                 events[k - 1][0].record()
             markov_partials(Uk, g * V, W1, self.W2p, x_prev, xs, R=self.R, V=V, r=self.r,
@@ -95,7 +110,7 @@ class Chain:
 
     def confidence(self):
         i = self.inp
-        return confidence(i["h"], i["W1"], i["anchor"], self.draft_out[0], i["w"], self.b,
+        return confidence(i["h"], i["W1"], self.anchor, self.draft_out[0], i["w"], self.b,
                           out=self.conf_out)
 
     def schedule(self):
@@ -104,7 +119,7 @@ class Chain:
 
     def pack(self):
         win = None if self.full_block else self.sched_out[0]
-        return pack_ragged(self.inp["anchor"], self.draft_out[0], win, self.tiers, self.M_cap,
+        return pack_ragged(self.anchor, self.draft_out[0], win, self.tiers, self.M_cap,
                            out=self.pack_out)
 
     def gather_target(self):
@@ -122,7 +137,7 @@ class Chain:
     def verify(self):
         i = self.inp
         d = self.draft_out
-        return verify(self.target_packed, self.pack_out["cu_seqlens"], i["anchor"], d[0], d[1],
+        return verify(self.target_packed, self.pack_out["cu_seqlens"], self.anchor, d[0], d[1],
                       d[2], i["U"], i["W1"], self.W2p, r=self.r, mode=self.verify_mode,
                       win_len=self.sched_out[0], seed=self.seed, step=self.step,
                       req_ids=i["req_ids"], out=self.verify_out, ws=self.ws_verify)
@@ -144,3 +159,108 @@ class Chain:
         out = {"tokens": d[0], "p_draft": d[1], "lse_draft": d[2], "conf": c[0], "surv": c[1],
                "win_len": s[0], "K": s[1], **self.pack_out, **self.verify_out}
         return {k: v.cpu().numpy() for k, v in out.items()}
+
+    # -- decode loop -------------------------------------------------------
+    def _decode_step(self, budget, mode: int):
+        """One step of the loop, every launch on the current stream: the draft
+        and verify read the Philox step from ``step_dev``; dspark_advance then
+        moves x_0, the step and the survival history on."""
+        i, d = self.inp, self.draft_out
+        markov_draft(i["U"], i["W1"], self.W2p, self.anchor, r=self.r, seed=self.seed,
+                     step_dev=self.step_dev, req_ids=i["req_ids"], out=d, ws=self.ws_draft)
+        self.confidence()
+        schedule_topb(self.conf_out[1], i["sps_milli"], B_cap=self.B_cap, mode=mode,
+                      K_fixed=self.K_fixed, surv_budget=budget, out=self.sched_out)
+        self.pack()
+        if not self.full_block:
+            self.gather_target()
+        verify(self.target_packed, self.pack_out["cu_seqlens"], self.anchor, d[0], d[1], d[2],
+               i["U"], i["W1"], self.W2p, r=self.r, mode=self.verify_mode,
+               win_len=self.sched_out[0], seed=self.seed, step_dev=self.step_dev,
+               req_ids=i["req_ids"], out=self.verify_out, ws=self.ws_verify)
+        v = self.verify_out
+        advance(self.anchor, v["accept_len"], v["out_tokens"], step_dev=self.step_dev,
+                surv_hist=self.surv_hist,
+                surv=self.conf_out[1] if self.surv_hist is not None else None)
+
+    def reset(self, anchor=None, step: Optional[int] = None):
+        """Put x_0 (default: the inputs' anchors) and the Philox step (default:
+        the constructor's) back, and forget the survival history and graph."""
+        self.anchor.copy_(self.inp["anchor"] if anchor is None else anchor)
+        self.step_dev.fill_(self.step if step is None else int(step))
+        self.surv_hist = None
+        self._graph = None
+        self._hist_steps = 0
+        self._lag = None
+
+    def save_state(self):
+        """Device copies of the loop state (x_0, Philox step, survival history)."""
+        return {"anchor": self.anchor.clone(), "step": self.step_dev.clone(),
+                "hist": None if self.surv_hist is None else self.surv_hist.clone(),
+                "hist_steps": self._hist_steps, "lag": self._lag}
+
+    def load_state(self, st):
+        """Restore a save_state() snapshot in place (a captured graph stays valid)."""
+        if st["lag"] != self._lag:
+            raise ValueError("the snapshot was taken with another history depth")
+        self.anchor.copy_(st["anchor"])
+        self.step_dev.copy_(st["step"])
+        if st["hist"] is not None:
+            self.surv_hist.copy_(st["hist"])
+        self._hist_steps = st["hist_steps"]
+
+    def decode(self, steps: int, *, lag: int = 2, graph: bool = False, record: bool = False):
+        """Run ``steps`` decode steps from the current state.
+
+        Step t sizes its budget from the survivals of step t - lag (lag 0: its
+        own). The first ``lag`` steps have no survivals that old and, when the
+        mode is ARGMAX, run the greedy scheduler with its early stop instead.
+        graph=True captures the first step that uses the history into a HIP
+        graph and replays it for every later step (eager steps before it load
+        every kernel). record=True returns, per step, device copies of its
+        x_0, Philox step, budget array and every output (taken between steps,
+        outside any graph); otherwise returns None."""
+        torch = self.t
+        R, g = self.R, self.gamma
+        if lag < 0 or lag > 8:
+            raise ValueError("lag must be in [0, 8]")
+        if lag != self._lag:   # new history depth: new buffers, new graph
+            self.surv_hist = (torch.zeros((lag, R, g), dtype=torch.float32, device=self.anchor.device)
+                              if lag > 0 else None)
+            self._graph = None
+            self._hist_steps = 0
+            self._lag = lag
+        log = [] if record else None
+        for _ in range(steps):
+            steady = self._hist_steps >= lag
+            budget = self.surv_hist[lag - 1] if (lag > 0 and steady) else None
+            mode = self.sched_mode
+            if not steady and mode == SCHED_ARGMAX:
+                mode = SCHED_GREEDY
+            if record:
+                snap = {"anchor": self.anchor.clone(), "step": self.step_dev.clone(),
+                        "surv_budget": None if budget is None else budget.clone(),
+                        "sched_mode": mode}
+            if graph and steady and self._graph is not None:
+                self._graph.replay()
+            elif graph and steady and self._warm:
+                self._graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(self._graph):
+                    self._decode_step(budget, mode)
+                self._graph.replay()
+            else:
+                self._decode_step(budget, mode)
+                self._warm = True
+            self._hist_steps = min(self._hist_steps + 1, lag)
+            if record:
+                d, c, s, v = self.draft_out, self.conf_out, self.sched_out, self.verify_out
+                snap.update({"tokens": d[0].clone(), "p_draft": d[1].clone(),
+                             "lse_draft": d[2].clone(), "conf": c[0].clone(), "surv": c[1].clone(),
+                             "win_len": s[0].clone(), "K": s[1].clone(),
+                             **{k: t.clone() for k, t in self.pack_out.items()},
+                             **{k: t.clone() for k, t in v.items() if t is not None}})
+                log.append(snap)
+        if not record:
+            return None
+        return [{k: (x.cpu().numpy() if hasattr(x, "cpu") else x) for k, x in e.items()}
+                for e in log]

@@ -235,6 +235,15 @@ __device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_
 
 enum { kPurposeDraft = 0, kPurposeAccept = 1, kPurposeResidual = 2, kPurposeBonus = 3 };
 
+// The Philox step of a call: a launch argument, or, when dev is set, a word in
+// device memory read when the kernel runs, so that a launch recorded once (a
+// captured graph) follows a step counter the device advances.
+struct StepArg {
+  uint64_t value;
+  const uint64_t* dev;
+  __device__ __forceinline__ uint64_t get() const { return dev != nullptr ? *dev : value; }
+};
+
 // Uniform in [0, 1 - 2^-24] for slot k of request req_id: word `purpose` of the
 // Philox block with counter (k, req_id, step, 0) and key (seed, 0).
 __device__ __forceinline__ float slot_uniform(uint64_t seed, uint64_t step, uint32_t req_id, int k,

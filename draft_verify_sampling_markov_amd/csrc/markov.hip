@@ -63,7 +63,8 @@ __global__ void prepack_w2_kernel(const T* __restrict__ W2, int r, int V, int KC
 // 64 b + l, in the prologue once its tile loads are out (the tile queue hands
 // these workgroups fewer tiles). u_out == nullptr: the select draws itself.
 struct DrawArgs {
-  uint64_t seed, step;
+  uint64_t seed;
+  StepArg step;
   const uint32_t* req_ids;
   int k;
   float* u_out;
@@ -102,7 +103,7 @@ struct MarkovEpi {
   __device__ __forceinline__ void side_work() const {
     const int q = (int)blockIdx.x * kWave + (int)threadIdx.x;
     if (draw.u_out != nullptr && threadIdx.x < kWave && q < R)
-      draw.u_out[q] = slot_uniform(draw.seed, draw.step, draw.req_ids[q], draw.k, kPurposeDraft);
+      draw.u_out[q] = slot_uniform(draw.seed, draw.step.get(), draw.req_ids[q], draw.k, kPurposeDraft);
   }
   __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
     load16_clamped<BF16, VEC>(s.row, v0, nvalid, V, p);
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int V, int r, int n_t,
-    const float2* __restrict__ part, int ldn, int c, uint64_t seed, uint64_t step,
+    const float2* __restrict__ part, int ldn, int c, uint64_t seed, StepArg step,
     const uint32_t* __restrict__ req_ids, int k, int* __restrict__ tok_out,
     float* __restrict__ p_out, float* __restrict__ lse_out, int ostride,
     unsigned* __restrict__ queue, int n_queue, const float* __restrict__ u_pre) {
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
   load_b_row<BF16, KC, VW>(W1 + (size_t)x * r, r, lane, b);
   // the draw was taken by the GEMM pass, or is taken here (scalar work that
   // overlaps the loads in flight)
-  const float u = u_pre != nullptr ? u_pre[n] : slot_uniform(seed, step, req_ids[n], k, kPurposeDraft);
+  const float u = u_pre != nullptr ? u_pre[n] : slot_uniform(seed, step.get(), req_ids[n], k, kPurposeDraft);
   float m;
   WaveSearch ws;
   if constexpr (CMAX > 0) {
@@ -352,7 +353,7 @@ template <bool BF16, int KC>
 static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool vec, bool vec_w1,
                          const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                          const int32_t* xprev, int xstride, int R, int V, int r,
-                         const float2* part, uint64_t seed, uint64_t step,
+                         const float2* part, uint64_t seed, StepArg step,
                          const uint32_t* req_ids, int k, int32_t* tok, float* p, float* lse,
                          int ostride, const float* u_pre, hipStream_t s) {
   const int n_t = n_vtiles(V), c = part_chunk(V), ldn = part_ld(V);
@@ -378,7 +379,7 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
 
 template <bool BF16, int KC>
 static int launch_markov(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
-                         uint64_t seed, uint64_t step, const uint32_t* req_ids, int R, int gamma,
+                         uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                          int V, int r, int32_t* tokens, float* p_draft, float* lse_draft,
                          float2* part, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
@@ -409,7 +410,7 @@ static int launch_partials_api(const void* U, long long ldU, const void* W1, con
                                float2* part, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
   const bool vec = u_vec_ok<BF16>(U, ldU, V) && w1_vec_ok(W1, r);
-  const DrawArgs none{0, 0, nullptr, 0, nullptr};
+  const DrawArgs none{0, StepArg{0, nullptr}, nullptr, 0, nullptr};
   return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
                                    static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, none,
                                    s);
@@ -468,7 +469,7 @@ extern "C" int dspark_prepack_w2(const void* W2, int r, int V, int dtype, void* 
   }
 
 static int markov_dispatch(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
-                           uint64_t seed, uint64_t step, const uint32_t* req_ids, int R, int gamma,
+                           uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                            int V, int r, int dtype, int32_t* tokens, float* p, float* lse,
                            float2* part, hipStream_t s) {
   if (dtype == DSPARK_BF16) {
@@ -484,7 +485,7 @@ static int markov_dispatch(const void* U, const void* W1, const void* W2p, const
 
 extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2p,
                                    const int32_t* anchor, uint64_t seed, uint64_t step,
-                                   const uint32_t* req_ids, int R, int gamma, int V, int r,
+                                   const uint64_t* step_dev, const uint32_t* req_ids, int R, int gamma, int V, int r,
                                    int dtype, int32_t* tokens, float* p_draft, float* lse_draft,
                                    void* ws, size_t ws_bytes, void* stream) {
   int st = check_sizes(R, gamma, V, r, dtype);
@@ -492,8 +493,8 @@ extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2
   if (!U || !W1 || !W2p || !anchor || !req_ids || !tokens || !p_draft || !lse_draft)
     return DSPARK_EINVAL;
   if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
-  return markov_dispatch(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, dtype, tokens,
-                         p_draft, lse_draft, static_cast<float2*>(ws),
+  return markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
+                         r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws),
                          static_cast<hipStream_t>(stream));
 }
 
@@ -550,7 +551,7 @@ extern "C" int dspark_markov_partials(const void* U_k, long long ldU, const void
 template <bool BF16, int KC>
 static int launch_select_api(const void* U, long long ldU, const void* W1, const void* W2p,
                              const int32_t* x_prev, int xstride, const float2* part, uint64_t seed,
-                             uint64_t step, const uint32_t* req_ids, int k, int R, int V, int r,
+                             StepArg step, const uint32_t* req_ids, int k, int R, int V, int r,
                              int32_t* tok, float* p, float* lse, int ostride, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
   return launch_select<BF16, KC>(static_cast<const T*>(U), ldU, u_vec_ok<BF16>(U, ldU, V),
@@ -562,7 +563,7 @@ static int launch_select_api(const void* U, long long ldU, const void* W1, const
 extern "C" int dspark_markov_select(const void* U_k, long long ldU, const void* W1,
                                     const void* W2p, const int32_t* x_prev, int xstride,
                                     const void* part, uint64_t seed, uint64_t step,
-                                    const uint32_t* req_ids, int k, int R, int V, int r, int dtype,
+                                    const uint64_t* step_dev, const uint32_t* req_ids, int k, int R, int V, int r, int dtype,
                                     int32_t* tok_out, float* p_out, float* lse_out, int ostride,
                                     void* stream) {
   int st = check_sizes(R, 1, V, r, dtype);
@@ -572,7 +573,8 @@ extern "C" int dspark_markov_select(const void* U_k, long long ldU, const void* 
   if (ldU < V || xstride < 1 || ostride < 1 || k < 1 || k > kMaxGamma + 1) return DSPARK_ESIZE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float2* pt = static_cast<const float2*>(part);
-#define DSPARK_SEL_ARGS U_k, ldU, W1, W2p, x_prev, xstride, pt, seed, step, req_ids, k, R, V, r, \
+  const StepArg sa{step, step_dev};
+#define DSPARK_SEL_ARGS U_k, ldU, W1, W2p, x_prev, xstride, pt, seed, sa, req_ids, k, R, V, r, \
                         tok_out, p_out, lse_out, ostride, s
   if (dtype == DSPARK_BF16) {
     switch (kc_instance(r)) {

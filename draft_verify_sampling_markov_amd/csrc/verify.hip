@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void decide_kernel(
     const float2* __restrict__ part, const int* __restrict__ cu_seqlens,
     const int* __restrict__ anchor, const int* __restrict__ tokens,
     const float* __restrict__ p_draft, const float* __restrict__ lse_draft,
-    const int* __restrict__ win_len, int mode, uint64_t seed, uint64_t step,
+    const int* __restrict__ win_len, int mode, uint64_t seed, StepArg step,
     const uint32_t* __restrict__ req_ids, int R, int gamma, int rows_ws, Jobs jobs,
     int* __restrict__ accept_len,
     int* __restrict__ out_tokens, int* __restrict__ n_out, int* __restrict__ ceiling) {
@@ -155,6 +155,7 @@ __global__ __launch_bounds__(256) void decide_kernel(
   const float pd = p_draft[(size_t)req * gamma + jl];
   const float lsed = lse_draft[(size_t)req * gamma + jl];
   const int anc = anchor[req];
+  const uint64_t stp = step.get();
   const int wl = mode == DSPARK_VERIFY_CAP_ACCEPT ? win_len[req] : gamma;
   const int row = c0 + min(lane, Lv);
   const float zt = to_f32(target[(size_t)row * V + clamp_token(tok, V)]);
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256) void decide_kernel(
     }
   }
   // this lane's Philox block (slot lane + 1): accept, residual and bonus words
-  const U64x4 blk = philox4x64_10((uint64_t)(lane + 1), (uint64_t)req_ids[req], step, 0ull, seed, 0ull);
+  const U64x4 blk = philox4x64_10((uint64_t)(lane + 1), (uint64_t)req_ids[req], stp, 0ull, seed, 0ull);
   const float to24 = 5.9604644775390625e-8f;  // 2^-24
   const float u_acc = (float)(uint32_t)(blk.w[kPurposeAccept] >> 40) * to24;
   const float u_res = (float)(uint32_t)(blk.w[kPurposeResidual] >> 40) * to24;
@@ -448,7 +449,7 @@ template <bool BF16, int KC>
 static int launch_verify(const void* target, int M_cap, const int32_t* cu, const int32_t* anchor,
                          const int32_t* tokens, const float* p_draft, const float* lse_draft,
                          const void* U, const void* W1, const void* W2p, const int32_t* win_len,
-                         int mode, uint64_t seed, uint64_t step, const uint32_t* req_ids, int R,
+                         int mode, uint64_t seed, StepArg step, const uint32_t* req_ids, int R,
                          int gamma, int V, int r, int32_t* accept_len, int32_t* out_tokens,
                          int32_t* n_out, int32_t* ceiling, const VerifyWs& ws, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
@@ -530,10 +531,10 @@ extern "C" int dspark_verify(const void* target_packed, int M_cap, const int32_t
                              const int32_t* anchor, const int32_t* tokens, const float* p_draft,
                              const float* lse_draft, const void* U, const void* W1,
                              const void* W2p, const int32_t* win_len, int mode, uint64_t seed,
-                             uint64_t step, const uint32_t* req_ids, int R, int gamma, int V,
-                             int r, int dtype, int32_t* accept_len, int32_t* out_tokens,
-                             int32_t* n_out, int32_t* ceiling_len, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             uint64_t step, const uint64_t* step_dev, const uint32_t* req_ids,
+                             int R, int gamma, int V, int r, int dtype, int32_t* accept_len,
+                             int32_t* out_tokens, int32_t* n_out, int32_t* ceiling_len, void* ws,
+                             size_t ws_bytes, void* stream) {
   int st = check_sizes(R, gamma, V, r, dtype);
   if (st) return st;
   if (mode < DSPARK_VERIFY_STATIC || mode > DSPARK_VERIFY_CAP_ACCEPT) return DSPARK_EINVAL;
@@ -546,9 +547,10 @@ extern "C" int dspark_verify(const void* target_packed, int M_cap, const int32_t
   VerifyWs w;
   carve(&w, ws, R, gamma, V);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const StepArg sa{step, step_dev};
 #define DSPARK_VERIFY_ARGS                                                                        \
   target_packed, M_cap, cu_seqlens, anchor, tokens, p_draft, lse_draft, U, W1, W2p, win_len, mode, \
-      seed, step, req_ids, R, gamma, V, r, accept_len, out_tokens, n_out, ceiling_len, w, s
+      seed, sa, req_ids, R, gamma, V, r, accept_len, out_tokens, n_out, ceiling_len, w, s
   if (dtype == DSPARK_BF16) {
     switch (kc_instance(r)) {
       case 1: return launch_verify<true, 1>(DSPARK_VERIFY_ARGS);

@@ -10,7 +10,8 @@
  *   dspark_pack_ragged    cu_seqlens packing rounded up to a capture tier
  *   dspark_verify         lossless rejection-sampling verification
  *
- * plus host/device utilities (W2 pre-packing, cost-table preparation,
+ * a sixth, dspark_advance, that carries a decode loop from one step to the
+ * next on the device, plus host/device utilities (W2 pre-packing, cost-table preparation,
  * workspace sizing and initialisation, status strings) and one diagnostic
  * call.
  *
@@ -48,6 +49,10 @@
  *     test, the residual resample and the bonus sample at slot k. A word x
  *     becomes the uniform (x >> 40) * 2^-24. Outputs are a pure function of
  *     the inputs and (seed, step, req_ids).
+ *   - Calls that draw take the step as a value and, optionally, as a device
+ *     word `step_dev` (uint64). When step_dev is not NULL the kernels read the
+ *     step from it when they run and the value is ignored; a launch captured
+ *     once in a graph then follows a counter that dspark_advance moves on.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -161,7 +166,8 @@ int dspark_cost_table_prepare(const double* raw_step_time_s, int M_max, const in
  * Sampling: inverse CDF over ascending ids with a strict comparison,
  * x = min{v : C_v > u S}, on the draft uniform of slot k. */
 int dspark_markov_draft(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
-                        uint64_t seed, uint64_t step, const uint32_t* req_ids, int R, int gamma,
+                        uint64_t seed, uint64_t step, const uint64_t* step_dev,
+                        const uint32_t* req_ids, int R, int gamma,
                         int V, int r, int dtype, int32_t* tokens, float* p_draft,
                         float* lse_draft, void* ws, size_t ws_bytes, void* stream);
 
@@ -242,9 +248,29 @@ int dspark_verify(const void* target_packed, int M_cap, const int32_t* cu_seqlen
                   const int32_t* anchor, const int32_t* tokens, const float* p_draft,
                   const float* lse_draft, const void* U, const void* W1, const void* W2p,
                   const int32_t* win_len, int mode, uint64_t seed, uint64_t step,
-                  const uint32_t* req_ids, int R, int gamma, int V, int r, int dtype,
-                  int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                  const uint64_t* step_dev, const uint32_t* req_ids, int R, int gamma, int V,
+                  int r, int dtype, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
                   int32_t* ceiling_len, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode-loop advance ([digest] "Infra": the verify budget is sized from
+ * confidences two steps back, while candidates are ranked by the latest
+ * survivals; [vllm] "Execution pipeline": budget from the previous step's
+ * double-buffered confidences, slots assigned on the GPU without read-back).
+ * One launch, after a step's dspark_verify, that prepares the next step:
+ *   anchor[r] <- out_tokens[r, A] with A = accept_len[r] clamped to [0, gamma]
+ *               (the correction or bonus token, the next x_0)
+ *   *step_dev += 1                    (skipped if step_dev is NULL)
+ *   surv_hist [n_hist, R, gamma] f32: level h <- level h - 1 (h >= 1),
+ *               level 0 <- surv [R, gamma] (n_hist = 0: no history; surv_hist
+ *               and surv may then be NULL)
+ * After the call, level h holds the survivals of the step h + 1 steps before
+ * the next one; passing level lag - 1 as surv_budget to dspark_schedule_topb
+ * sizes the budget from confidences lag steps old. 0 <= n_hist <= 8.
+ * anchor, accept_len and out_tokens are the [R], [R] and [R, gamma + 1]
+ * buffers of the step just verified. */
+int dspark_advance(int32_t* anchor, const int32_t* accept_len, const int32_t* out_tokens, int R,
+                   int gamma, uint64_t* step_dev, float* surv_hist, const float* surv, int n_hist,
+                   void* stream);
 
 /* The first of the two passes dspark_markov_draft runs for every slot, as a
  * call of its own (for callers that time or fuse it): the bias GEMM
@@ -273,9 +299,9 @@ int dspark_markov_partials(const void* U_k, long long ldU, const void* W1, const
  * call, for k = 1..gamma. */
 int dspark_markov_select(const void* U_k, long long ldU, const void* W1, const void* W2p,
                          const int32_t* x_prev, int xstride, const void* part, uint64_t seed,
-                         uint64_t step, const uint32_t* req_ids, int k, int R, int V, int r,
-                         int dtype, int32_t* tok_out, float* p_out, float* lse_out, int ostride,
-                         void* stream);
+                         uint64_t step, const uint64_t* step_dev, const uint32_t* req_ids, int k,
+                         int R, int V, int r, int dtype, int32_t* tok_out, float* p_out,
+                         float* lse_out, int ostride, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostic                                                                */

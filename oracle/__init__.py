@@ -40,7 +40,7 @@ from .schedule import cost_table_prepare, quantize_survival, schedule_topb, \
     SCHED_ARGMAX, SCHED_GREEDY, SCHED_FIXED
 from .pack import pack_ragged
 from .verify import verify, VERIFY_STATIC, VERIFY_COMPACT, VERIFY_CAP_ACCEPT
-from .chain import chain
+from .chain import chain, decode
 
 __all__ = [
     "philox4x64_10", "uniform24", "uniforms", "PURPOSE_DRAFT", "PURPOSE_ACCEPT",
@@ -48,5 +48,5 @@ __all__ = [
     "markov_step", "markov_draft", "confidence", "cost_table_prepare",
     "quantize_survival", "schedule_topb", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "pack_ragged", "verify", "VERIFY_STATIC", "VERIFY_COMPACT",
-    "VERIFY_CAP_ACCEPT", "chain",
+    "VERIFY_CAP_ACCEPT", "chain", "decode",
 ]

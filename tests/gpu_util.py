@@ -99,8 +99,8 @@ def check_confidence(res, inp, reqs, label=""):
     assert np.all(np.diff(res["surv"], axis=1) <= 0), label
 
 
-def check_schedule(res, sps, B_cap, mode, K_fixed=0, label=""):
-    ref = oracle.schedule_topb(res["surv"], [int(x) for x in sps], B_cap, mode, K_fixed)
+def check_schedule(res, sps, B_cap, mode, K_fixed=0, label="", budget=None):
+    ref = oracle.schedule_topb(res["surv"], [int(x) for x in sps], B_cap, mode, K_fixed, budget)
     assert res["win_len"].tolist() == ref["win_len"], label
     assert int(res["K"][0]) == ref["K"], label
     return ref

@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -63,14 +63,14 @@ def test_host_validation_rejects_before_launch():
     EINVAL, EDTYPE, ETIER, ESIZE, EWS = -1, -2, -3, -4, -5
     p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
     # markov_draft: bad dtype, bad sizes, null pointers, missing workspace
-    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 5, p, p, p, p, 1 << 30, None) == EDTYPE
-    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 17, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
-    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 600, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
-    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 129, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 5, p, p, p, p, 1 << 30, None) == EDTYPE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 17, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 600, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 129, 0, p, p, p, p, 1 << 30, None) == ESIZE
     assert lib.dspark_workspace_init(None, 256, None) == EINVAL
-    assert lib.dspark_markov_draft(None, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == EINVAL
-    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, p, 8, None) == EWS
-    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, None, 1 << 30, None) == EWS
+    assert lib.dspark_markov_draft(None, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, p, p, 1 << 30, None) == EINVAL
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, p, p, 8, None) == EWS
+    assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, p, None, 1 << 30, None) == EWS
     # confidence
     assert lib.dspark_confidence(p, p, p, p, p, 0.0, None, 4, 7, 0, 1024, 32, 0, p, p, None) == ESIZE
     assert lib.dspark_confidence(p, None, p, p, p, 0.0, None, 4, 7, 64, 1024, 32, 0, p, p, None) == EINVAL
@@ -85,7 +85,7 @@ def test_host_validation_rejects_before_launch():
     assert lib.dspark_pack_ragged(p, p, None, 4, 7, tiers, 0, 32, p, p, p, p, p, None) == ETIER
     assert lib.dspark_pack_ragged(p, p, None, 4, 7, tiers, 3, 31, p, p, p, p, p, None) == ESIZE
     # verify
-    args = [p, 32, p, p, p, p, p, p, p, p, None, 2, 0, 0, p, 4, 7, 1024, 32, 0, p, p, p, None, p, 1 << 30, None]
+    args = [p, 32, p, p, p, p, p, p, p, p, None, 2, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, p, None, p, 1 << 30, None]
     assert lib.dspark_verify(*args) == EINVAL          # cap-accept needs win_len
     args[11] = 7
     assert lib.dspark_verify(*args) == EINVAL          # bad mode
@@ -95,6 +95,12 @@ def test_host_validation_rejects_before_launch():
     args[1] = 32
     args[-2] = 16
     assert lib.dspark_verify(*args) == EWS
+    # advance: sizes, history depth, missing buffers
+    assert lib.dspark_advance(p, p, p, 0, 7, None, None, None, 0, None) == ESIZE
+    assert lib.dspark_advance(p, p, p, 4, 17, None, None, None, 0, None) == ESIZE
+    assert lib.dspark_advance(p, p, p, 4, 7, None, p, p, 9, None) == ESIZE
+    assert lib.dspark_advance(p, None, p, 4, 7, None, None, None, 0, None) == EINVAL
+    assert lib.dspark_advance(p, p, p, 4, 7, None, None, p, 2, None) == EINVAL
     # prepack
     assert lib.dspark_prepack_w2(p, 32, 1024, 1, p, 10, None) == EWS
     assert lib.dspark_prepack_w2(p, 32, 1024, 3, p, 1 << 30, None) == EDTYPE
