@@ -41,6 +41,7 @@ from .schedule import cost_table_prepare, quantize_survival, schedule_topb, \
 from .pack import pack_ragged
 from .verify import verify, VERIFY_STATIC, VERIFY_COMPACT, VERIFY_CAP_ACCEPT
 from .chain import chain, decode
+from .observe import analytic_acceptance, new_stats, observe, ece, utilisation
 
 __all__ = [
     "philox4x64_10", "uniform24", "uniforms", "PURPOSE_DRAFT", "PURPOSE_ACCEPT",
@@ -48,5 +49,6 @@ __all__ = [
     "markov_step", "markov_draft", "confidence", "cost_table_prepare",
     "quantize_survival", "schedule_topb", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "pack_ragged", "verify", "VERIFY_STATIC", "VERIFY_COMPACT",
-    "VERIFY_CAP_ACCEPT", "chain", "decode",
+    "VERIFY_CAP_ACCEPT", "chain", "decode", "analytic_acceptance", "new_stats", "observe",
+    "ece", "utilisation",
 ]
