@@ -151,6 +151,48 @@ def measure_decode(dv, dev, inp, spec, B_cap: int, steps: int, lag: int):
     return out
 
 
+def measure_observability(dv, dev, inp, spec, B_cap: int, steps: int):
+    """The two observability calls on a cap-accept step of the workload (the
+    mode that verifies the whole block while committing the window): the
+    accumulator (dspark_observe) and the analytic acceptance pass
+    (dspark_analytic_accept), each timed with HIP events over `steps` calls on
+    the chain's stream. The analytic pass's algorithmic bytes are the packed
+    target rows once for their log-sum-exps, then the U row and target row of
+    every verified slot, and W2 once per group of rows the GEMM engine holds."""
+    import numpy as np
+    import torch
+    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B_cap,
+                  verify_mode=dv.VERIFY_CAP_ACCEPT, observe_bins=16, analytic=True)
+    ch.run(gather=False)
+    torch.cuda.synchronize()
+    res = ch.results()
+    out = {"mode": "cap_accept", "calls": steps}
+    for name, fn in (("analytic", ch.analytic_step), ("observe", ch.observe_step)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[f"{name}_us"] = round(ev[0].elapsed_time(ev[1]) * 1e3 / steps, 2)
+    b = 2 if spec.dtype == "bf16" else 4
+    R, g, V, r = spec.R, spec.gamma, spec.V, spec.r
+    M = int(res["totals"][0])
+    verified = int(np.isfinite(res["cstar"]).sum())
+    groups = -(-(R * (g + 1)) // (256 if spec.dtype == "bf16" else 128))
+    nbytes = M * V * b + 2 * verified * V * b + groups * r * V * b
+    out["analytic_bytes"] = nbytes
+    out["analytic_gbs"] = round(nbytes / (out["analytic_us"] * 1e-6) / 1e9, 1)
+    summ = ch.observe_summary()
+    out["mean_cstar"] = round(float(np.nanmean(res["cstar"])), 4)
+    out["mean_conf"] = round(float(res["conf"].mean()), 4)
+    out["utilisation"] = round(summ["utilisation"], 4)
+    out["ece_conditional"] = round(summ["ece_conditional"], 4)
+    log(f"[bench] observability: analytic c* pass {out['analytic_us']} us "
+        f"({out['analytic_gbs']} GB/s), accumulator {out['observe_us']} us")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +208,8 @@ def main() -> int:
                     help="steps of the multi-step decode loop (compact verify, budget from "
                          "survivals --lag steps old) timed eagerly and as graph replays; 0 skips")
     ap.add_argument("--lag", type=int, default=2)
+    ap.add_argument("--observe-calls", type=int, default=10,
+                    help="timed calls of each observability pass on a cap-accept step; 0 skips")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one 256 MiB device-to-device copy (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -290,6 +334,8 @@ def main() -> int:
     }
     if args.decode_steps > 0:
         line["decode"] = measure_decode(dv, dev, inp, spec, B_cap, args.decode_steps, args.lag)
+    if args.observe_calls > 0:
+        line["observability"] = measure_observability(dv, dev, inp, spec, B_cap, args.observe_calls)
     if args.calibrate_copy:
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -6,7 +6,7 @@ raises if the library is missing -- there is no fallback path.
 
 Calls (same names as the C ABI in include/dspark.h, without the prefix):
     prepack_w2, markov_draft, confidence, schedule_topb, pack_ragged, verify,
-    advance, cost_table_prepare, workspace_bytes, markov_logits
+    advance, observe, analytic_accept, cost_table_prepare, workspace_bytes, markov_logits
 and ``Chain``, which holds preallocated buffers for repeated steps.
 """
 from __future__ import annotations
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libdspark.so")
 F32, BF16 = 0, 1
 VERIFY_STATIC, VERIFY_COMPACT, VERIFY_CAP_ACCEPT = 0, 1, 2
 SCHED_ARGMAX, SCHED_GREEDY, SCHED_FIXED = 0, 1, 2
-CALL_MARKOV_DRAFT, CALL_VERIFY = 0, 1
+CALL_MARKOV_DRAFT, CALL_VERIFY, CALL_ANALYTIC_ACCEPT = 0, 1, 2
 
 VERIFY_MODES = {"static": VERIFY_STATIC, "compact": VERIFY_COMPACT, "cap_accept": VERIFY_CAP_ACCEPT}
 SCHED_MODES = {"argmax": SCHED_ARGMAX, "greedy": SCHED_GREEDY, "fixed": SCHED_FIXED}
@@ -48,6 +48,10 @@ _SIGNATURES = {
     "dspark_verify": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _u64,
                            _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_advance": (_i, [_vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _vp]),
+    "dspark_observe_words": (_sz, [_i, _i, _i]),
+    "dspark_observe": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
+    "dspark_analytic_accept": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                    _vp, _vp, _sz, _vp]),
     "dspark_markov_logits": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "dspark_markov_partials": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz,
                                     _vp]),
@@ -362,6 +366,87 @@ def advance(anchor, accept_len, out_tokens, *, step_dev=None, surv_hist=None, su
         _opt(surv, "surv", torch.float32, (R, gamma)), n_hist, _stream(stream)))
 
 
+def observe_words(R: int, gamma: int, n_bins: int) -> int:
+    return int(load_library().dspark_observe_words(R, gamma, n_bins))
+
+
+def new_observe_block(R: int, gamma: int, n_bins: int, device, stream=None):
+    """A zeroed observability block (int64 device tensor of observe_words words)."""
+    torch = _torch()
+    n = observe_words(R, gamma, n_bins)
+    if n == 0:
+        raise DsparkError("unsupported observability block sizes")
+    blk = _empty((n,), torch.int64, device)
+    workspace_init(blk.view(torch.uint8), stream)
+    return blk
+
+
+def observe(conf, surv, win_len, accept_len, ceiling_len, cu_seqlens, stats, *, n_bins: int,
+            stream=None):
+    """Add one step to the observability block ``stats`` (dspark_observe)."""
+    torch = _torch()
+    R, gamma = conf.shape
+    _check(load_library().dspark_observe(
+        _dev(conf, "conf", torch.float32, (R, gamma)), _dev(surv, "surv", torch.float32, (R, gamma)),
+        _dev(win_len, "win_len", torch.int32, (R,)), _dev(accept_len, "accept_len", torch.int32, (R,)),
+        _dev(ceiling_len, "ceiling_len", torch.int32, (R,)),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)), R, gamma, int(n_bins),
+        _dev(stats, "stats", torch.int64), stats.numel(), _stream(stream)))
+
+
+def parse_observe(block, R: int, gamma: int, n_bins: int) -> Dict[str, object]:
+    """Split a host copy of an observability block into its named counters
+    (layout of dspark_observe) and derive ECE and utilisation from them."""
+    b = np.asarray(block).view(np.uint64).astype(object)
+    g1 = gamma + 1
+    hist0, req0 = 8, 8 + 3 * g1
+    bins0 = req0 + 3 * R
+    out = {"steps": int(b[0]), "req_steps": int(b[1]), "committed": int(b[2]),
+           "accepted": int(b[3]), "ceiling": int(b[4]), "window": int(b[5]),
+           "verified": int(b[6]),
+           "hist_window": b[hist0:hist0 + g1], "hist_accept": b[hist0 + g1:hist0 + 2 * g1],
+           "hist_ceiling": b[hist0 + 2 * g1:hist0 + 3 * g1],
+           "req_accepted": b[req0:req0 + R], "req_ceiling": b[req0 + R:req0 + 2 * R],
+           "req_window": b[req0 + 2 * R:req0 + 3 * R],
+           "bins": b[bins0:bins0 + 6 * gamma * n_bins].reshape(2, gamma, n_bins, 3)}
+
+    def ece(cells):
+        cnt = cells[..., 0].sum(axis=0)
+        n = int(cnt.sum())
+        if n == 0:
+            return float("nan")
+        ps, hits = cells[..., 1].sum(axis=0), cells[..., 2].sum(axis=0)
+        return sum(abs(float(ps[i]) / 2.0 ** 32 - int(hits[i])) for i in range(n_bins)) / n
+
+    out["ece_conditional"] = ece(out["bins"][0])
+    out["ece_prefix"] = ece(out["bins"][1])
+    out["ece_prefix_per_position"] = [ece(out["bins"][1, k][None]) for k in range(gamma)]
+    out["utilisation"] = (out["accepted"] / out["ceiling"]) if out["ceiling"] else float("nan")
+    return out
+
+
+def analytic_accept(target_packed, cu_seqlens, anchor, tokens, lse_draft, U, W1, W2p, *, r: int,
+                    out=None, ws=None, stream=None):
+    """c*[R, gamma] f32 = 1 - 1/2 |p_d - p_t|_1 for every verified slot, NaN elsewhere."""
+    torch = _torch()
+    R, gamma, V = U.shape
+    M_cap = target_packed.shape[0]
+    dev = U.device
+    if out is None:
+        out = _empty((R, gamma), torch.float32, dev)
+    if ws is None:
+        ws = new_workspace(CALL_ANALYTIC_ACCEPT, R, gamma, V, r, dev, stream)
+    _check(load_library().dspark_analytic_accept(
+        _dev(target_packed, "target_packed", U.dtype, (M_cap, V)), M_cap,
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,)), _dev(anchor, "anchor", torch.int32, (R,)),
+        _dev(tokens, "tokens", torch.int32, (R, gamma)),
+        _dev(lse_draft, "lse_draft", torch.float32, (R, gamma)), _dev(U, "U"),
+        _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype), R, gamma, V, r, _dtype_code(U),
+        _dev(out, "cstar", torch.float32, (R, gamma)), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)))
+    return out
+
+
 from .chain import Chain  # noqa: E402  (needs the functions above)
 
 __all__ = [
@@ -369,7 +454,8 @@ __all__ = [
     "new_workspace", "prepacked_w2_bytes",
     "prepack_w2", "cost_table_prepare", "markov_draft", "confidence", "schedule_topb",
     "pack_ragged", "verify", "markov_logits", "markov_partials",
-    "markov_select", "advance", "Chain", "EXPORTS", "F32", "BF16",
+    "markov_select", "advance", "observe_words", "new_observe_block", "observe", "parse_observe",
+    "analytic_accept", "Chain", "EXPORTS", "F32", "BF16",
     "VERIFY_STATIC", "VERIFY_COMPACT", "VERIFY_CAP_ACCEPT", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "VERIFY_MODES", "SCHED_MODES",
 ]

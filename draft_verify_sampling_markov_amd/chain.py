@@ -21,8 +21,9 @@ from __future__ import annotations
 from typing import Dict, Optional, Sequence
 
 from . import (markov_draft, markov_partials, markov_select, confidence, schedule_topb,
-               pack_ragged, verify, advance, prepack_w2, new_workspace, CALL_MARKOV_DRAFT,
-               CALL_VERIFY, VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX, SCHED_GREEDY)
+               pack_ragged, verify, advance, observe, new_observe_block, parse_observe,
+               analytic_accept, prepack_w2, new_workspace, CALL_MARKOV_DRAFT, CALL_VERIFY,
+               CALL_ANALYTIC_ACCEPT, VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX, SCHED_GREEDY)
 
 
 class Chain:
@@ -33,11 +34,17 @@ class Chain:
     w [d+r] f32, req_ids [R] int32, sps_milli [M_max+1] int32 (uint32 bits).
     The chain keeps its own copy of the anchors (``self.anchor``), which
     ``decode`` moves on from step to step.
+
+    Optional observability, run after every verify when enabled:
+    observe_bins > 0 accumulates dspark_observe counts into ``obs_block``
+    (read with ``observe_summary``); analytic=True writes the analytic
+    acceptance c* of every verified slot into ``cstar``.
     """
 
     def __init__(self, inputs: Dict[str, "object"], *, b: float, tiers: Sequence[int],
                  B_cap: int, verify_mode: int, sched_mode: int = SCHED_ARGMAX, K_fixed: int = 0,
-                 seed: int = 0, step: int = 0, W2p=None):
+                 seed: int = 0, step: int = 0, W2p=None, observe_bins: int = 0,
+                 analytic: bool = False):
         import torch
         self.t = torch
         self.inp = inputs
@@ -74,6 +81,12 @@ class Chain:
                            "n_out": e((R,), i32), "ceiling_len": e((R,), i32)}
         self.ws_draft = new_workspace(CALL_MARKOV_DRAFT, R, g, V, r, dev)
         self.ws_verify = new_workspace(CALL_VERIFY, R, g, V, r, dev)
+        self.n_bins = int(observe_bins)
+        self.obs_block = new_observe_block(R, g, self.n_bins, dev) if self.n_bins else None
+        self.analytic = bool(analytic)
+        self.cstar = e((R, g), f32) if self.analytic else None
+        self.ws_accept = (new_workspace(CALL_ANALYTIC_ACCEPT, R, g, V, r, dev) if self.analytic
+                          else None)
         self.full_block = self.verify_mode in (VERIFY_STATIC, VERIFY_CAP_ACCEPT)
         self.target_packed = (inputs["target"].view(self.M_cap, V) if self.full_block
                               else e((self.M_cap, V), U.dtype))
@@ -142,6 +155,29 @@ class Chain:
                       win_len=self.sched_out[0], seed=self.seed, step=self.step,
                       req_ids=i["req_ids"], out=self.verify_out, ws=self.ws_verify)
 
+    def observe_step(self):
+        """Add the current step's outputs to ``obs_block``."""
+        v = self.verify_out
+        observe(self.conf_out[0], self.conf_out[1], self.sched_out[0], v["accept_len"],
+                v["ceiling_len"], self.pack_out["cu_seqlens"], self.obs_block, n_bins=self.n_bins)
+
+    def analytic_step(self):
+        """c* of the current step's verified slots into ``cstar``."""
+        i, d = self.inp, self.draft_out
+        return analytic_accept(self.target_packed, self.pack_out["cu_seqlens"], self.anchor, d[0],
+                               d[2], i["U"], i["W1"], self.W2p, r=self.r, out=self.cstar,
+                               ws=self.ws_accept)
+
+    def _extras(self):
+        if self.analytic:
+            self.analytic_step()
+        if self.obs_block is not None:
+            self.observe_step()
+
+    def observe_summary(self) -> Dict[str, object]:
+        """Host copy of ``obs_block``, split and summarised (synchronises)."""
+        return parse_observe(self.obs_block.cpu().numpy(), self.R, self.gamma, self.n_bins)
+
     def run(self, gather: bool = True):
         """One whole step; ``gather`` re-runs the target stand-in between pack
         and verify (needed whenever the windows may have changed)."""
@@ -152,12 +188,15 @@ class Chain:
         if gather:
             self.gather_target()
         self.verify()
+        self._extras()
 
     def results(self) -> Dict[str, "object"]:
         """Host copies of every stage output (synchronises)."""
         d, c, s = self.draft_out, self.conf_out, self.sched_out
         out = {"tokens": d[0], "p_draft": d[1], "lse_draft": d[2], "conf": c[0], "surv": c[1],
                "win_len": s[0], "K": s[1], **self.pack_out, **self.verify_out}
+        if self.analytic:
+            out["cstar"] = self.cstar
         return {k: v.cpu().numpy() for k, v in out.items()}
 
     # -- decode loop -------------------------------------------------------
@@ -178,6 +217,7 @@ class Chain:
                i["U"], i["W1"], self.W2p, r=self.r, mode=self.verify_mode,
                win_len=self.sched_out[0], seed=self.seed, step_dev=self.step_dev,
                req_ids=i["req_ids"], out=self.verify_out, ws=self.ws_verify)
+        self._extras()
         v = self.verify_out
         advance(self.anchor, v["accept_len"], v["out_tokens"], step_dev=self.step_dev,
                 surv_hist=self.surv_hist,
@@ -259,6 +299,8 @@ class Chain:
                              "win_len": s[0].clone(), "K": s[1].clone(),
                              **{k: t.clone() for k, t in self.pack_out.items()},
                              **{k: t.clone() for k, t in v.items() if t is not None}})
+                if self.analytic:
+                    snap["cstar"] = self.cstar.clone()
                 log.append(snap)
         if not record:
             return None

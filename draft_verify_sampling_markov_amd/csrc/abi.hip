@@ -24,6 +24,7 @@ extern "C" size_t dspark_workspace_bytes(int call, int R, int gamma, int V, int 
   switch (call) {
     case DSPARK_CALL_MARKOV_DRAFT: return markov_ws_bytes(R, V);
     case DSPARK_CALL_VERIFY: return verify_ws_bytes(R, gamma, V);
+    case DSPARK_CALL_ANALYTIC_ACCEPT: return accept_ws_bytes(R, gamma, V);
     default: return 0;
   }
 }

@@ -74,5 +74,6 @@ inline int check_sizes(int R, int gamma, int V, int r, int dt) {
 // Workspace layout pieces (bytes, 256-aligned).
 size_t markov_ws_bytes(int R, int V);
 size_t verify_ws_bytes(int R, int gamma, int V);
+size_t accept_ws_bytes(int R, int gamma, int V);
 
 }  // namespace dspark

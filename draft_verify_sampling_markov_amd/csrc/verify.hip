@@ -400,6 +400,168 @@ __global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// analytic acceptance c* = 1 - 1/2 |p_d - p_t|_1 per verified slot
+// ---------------------------------------------------------------------------
+
+// DSpark digest, "Verification scheduling (system side)": the confidence
+// head's training target is the analytic acceptance rate of a slot, one minus
+// the total-variation distance between its draft and target distributions.
+// With both normalisers known (the draft's stored lse, the target row's lse
+// from the row partials), c* = sum_v min(p_d(v), p_t(v)) is one pass over the
+// vocabulary: the draft GEMM engine recomputes every verified slot's draft
+// logits, and the epilogue sums min(p_d, p_t) per 64-entry tile.
+//
+// One job per packed row n (the row that holds the target of slot j + 1 of
+// its request, j = n - cu[r]); rows past a request's verified slots (its bonus
+// row) and past the pack are inactive and point their loads at row 0.
+struct AcceptJobs {
+  int* out;      // r * gamma + j for an active job, -1 otherwise
+  int* urow;     // draft base-logit row r * gamma + j (0 when inactive)
+  int* trow;     // packed target row (0 when inactive)
+  int* xprev;    // token before the slot (anchor for slot 1)
+  float* lse_t;  // target log-sum-exp of trow
+  float* lse_d;  // draft log-sum-exp of the slot
+};
+
+__global__ __launch_bounds__(256) void accept_jobs_kernel(
+    const int* __restrict__ cu_seqlens, const int* __restrict__ anchor,
+    const int* __restrict__ tokens, const float* __restrict__ lse_draft,
+    const float2* __restrict__ rowpart, int n_chunks, int R, int gamma, int rows_ws,
+    AcceptJobs jobs, float* __restrict__ cstar) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < R * gamma) {  // slots no packed row verifies: NaN
+    const int r = i / gamma, k = i % gamma + 1;
+    const int Lv = min(cu_seqlens[r + 1] - cu_seqlens[r] - 1, gamma);
+    if (k > Lv) cstar[i] = __builtin_nanf("");
+  }
+  if (i >= rows_ws) return;
+  const int M = min(cu_seqlens[R], rows_ws);
+  // request of row i: the last r with cu[r] <= i
+  int lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_seqlens[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  const int j = i - cu_seqlens[r];
+  const int Lv = min(cu_seqlens[r + 1] - cu_seqlens[r] - 1, gamma);
+  const bool active = i < M && j >= 0 && j < Lv;
+  int out = -1, xprev = 0, trow = 0;
+  float lse_t = 0.0f, lse_d = 0.0f;
+  if (active) {
+    out = r * gamma + j;
+    xprev = j == 0 ? anchor[r] : tokens[r * gamma + j - 1];
+    trow = i;
+    lse_d = lse_draft[out];
+    float m = -INFINITY, S = 0.0f;
+    for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, rowpart[(size_t)i * n_chunks + c].x);
+    for (int c = 0; c < n_chunks; ++c) {
+      const float2 pv = rowpart[(size_t)i * n_chunks + c];
+      S += pv.y * __expf(pv.x - m);
+    }
+    lse_t = m + __logf(S);
+  }
+  jobs.out[i] = out;
+  jobs.urow[i] = active ? out : 0;
+  jobs.trow[i] = trow;
+  jobs.xprev[i] = xprev;
+  jobs.lse_t[i] = lse_t;
+  jobs.lse_d[i] = lse_d;
+}
+
+// Epilogue: per entry min(exp(z_d - lse_d), exp(z_t - lse_t)) with
+// z_d = W1[x_prev] W2 + U (the draft pass's own sum), summed per tile and
+// job and stored at cpart[n * ldn + part_pos(t, c)].
+template <bool BF16, bool VEC>
+struct AcceptEpi {
+  typedef typename Elem<BF16>::T T;
+  struct Pre {
+    Raw16<BF16> zt, u;
+  };
+  struct St {
+    const T* trow;
+    const T* urow;
+    float lse_t, lse_d;
+    int ng;
+    bool active;
+  };
+  const T* target;
+  const T* U;
+  int V, R, g0;
+  AcceptJobs jobs;
+  float* cpart;
+  int ldn, c;
+  float* junk;
+
+  __device__ __forceinline__ St prepare(int n) const {
+    St s;
+    s.ng = g0 + min(n, R - 1);
+    s.active = n < R && jobs.out[s.ng] >= 0;
+    s.trow = target + (size_t)jobs.trow[s.ng] * V;
+    s.urow = U + (size_t)jobs.urow[s.ng] * V;
+    s.lse_t = jobs.lse_t[s.ng];
+    s.lse_d = jobs.lse_d[s.ng];
+    return s;
+  }
+  __device__ __forceinline__ void side_work() const {}
+  __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
+    load16_clamped<BF16, VEC>(s.trow, v0, nvalid, V, p.zt);
+    load16_clamped<BF16, VEC>(s.urow, v0, nvalid, V, p.u);
+  }
+  __device__ __forceinline__ void finish(const St& s, int v0, int nvalid, const f32x4 acc[4],
+                                         const Pre& p, int t, int lane) const {
+    float zt16[16], u16[16];
+    unpack16<BF16>(p.zt, zt16);
+    unpack16<BF16>(p.u, u16);
+    const int nv = s.active ? nvalid : 0;
+    float sm = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = 4 * j + i;
+        const float zd = acc[j][i] + u16[idx];
+        const float pd = __expf(zd - s.lse_d), pt = __expf(zt16[idx] - s.lse_t);
+        sm += idx < nv ? fminf(pd, pt) : 0.0f;
+      }
+    sm += __shfl_xor(sm, 16, kWave);
+    sm += __shfl_xor(sm, 32, kWave);
+    float* dst = ((lane >> 4) == 0 && s.active) ? cpart + (size_t)s.ng * ldn + part_pos(t, c) : junk;
+    *dst = sm;
+  }
+};
+
+template <bool BF16, int KC, int NW, int NB, bool VEC>
+__global__ __launch_bounds__(NW * 64) void accept_partials_kernel(
+    const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    AcceptJobs jobs, int g0, int R, int V, int r, int n_t, float* __restrict__ cpart, int ldn,
+    int c, float* __restrict__ junk, unsigned* __restrict__ queue) {
+  const AcceptEpi<BF16, VEC> epi{target, U, V, R, g0, jobs, cpart, ldn, c, junk};
+  run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
+                                         r, n_t, epi, queue);
+}
+
+// One 256-thread workgroup per job: the tile sums in a fixed order. The
+// workgroup of job 0 first puts the GEMM pass's queue counters back to zero.
+__global__ __launch_bounds__(kSelThreads) void accept_reduce_kernel(
+    AcceptJobs jobs, const float* __restrict__ cpart, int ldn, int c, int n_t,
+    float* __restrict__ cstar, unsigned* __restrict__ queue, int n_queue) {
+  __shared__ BlockSearchShared sh;
+  const int n = blockIdx.x, tid = threadIdx.x;
+  if (n == 0 && tid < n_queue) queue[tid * kQueueStride] = 0u;
+  const int out = jobs.out[n];
+  if (out < 0) return;  // workgroup-uniform
+  const float* prow = cpart + (size_t)n * ldn;
+  const int t0 = tid * c;
+  const int cnt = max(0, min(c, n_t - t0));
+  float s = 0.0f;
+  for (int i = 0; i < cnt; ++i) s += prow[i * kSelThreads + tid];
+  s = block_sum(s, sh);
+  if (tid == 0) cstar[out] = s;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -523,6 +685,102 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
   return launch_status();
 }
 
+// Analytic-acceptance workspace: row partials and jobs for R * (gamma + 1)
+// packed rows, their tile sums, the junk slot and the tile-queue counters.
+struct AcceptWs {
+  float2* rowpart;
+  float* cpart;
+  float* junk;
+  unsigned* queue;
+  AcceptJobs jobs;
+};
+
+static size_t carve_accept(AcceptWs* w, void* base, int R, int gamma, int V) {
+  const int rows_ws = R * (gamma + 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
+  const size_t o_cp = take((size_t)rows_ws * part_ld(V) * sizeof(float));
+  const size_t o_junk = take(256);
+  const size_t o_q = take((size_t)queue_groups(rows_ws) * kQueueWordsPerGroup * 4);
+  size_t o_j[6];
+  for (int i = 0; i < 6; ++i) o_j[i] = take((size_t)rows_ws * 4);
+  if (w && base) {
+    char* b = static_cast<char*>(base);
+    w->rowpart = reinterpret_cast<float2*>(b + o_row);
+    w->cpart = reinterpret_cast<float*>(b + o_cp);
+    w->junk = reinterpret_cast<float*>(b + o_junk);
+    w->queue = reinterpret_cast<unsigned*>(b + o_q);
+    w->jobs.out = reinterpret_cast<int*>(b + o_j[0]);
+    w->jobs.urow = reinterpret_cast<int*>(b + o_j[1]);
+    w->jobs.trow = reinterpret_cast<int*>(b + o_j[2]);
+    w->jobs.xprev = reinterpret_cast<int*>(b + o_j[3]);
+    w->jobs.lse_t = reinterpret_cast<float*>(b + o_j[4]);
+    w->jobs.lse_d = reinterpret_cast<float*>(b + o_j[5]);
+  }
+  return off;
+}
+
+size_t accept_ws_bytes(int R, int gamma, int V) { return carve_accept(nullptr, nullptr, R, gamma, V); }
+
+template <bool BF16, int KC>
+static int launch_accept(const void* target, const int32_t* cu, const int32_t* anchor,
+                         const int32_t* tokens, const float* lse_draft, const void* U,
+                         const void* W1, const void* W2p, int R, int gamma, int V, int r,
+                         float* cstar, const AcceptWs& ws, hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  const T* tg = static_cast<const T*>(target);
+  const T* Ub = static_cast<const T*>(U);
+  const T* W1b = static_cast<const T*>(W1);
+  const T* W2b = static_cast<const T*>(W2p);
+  const int nch = n_row_chunks(V), n_t = n_vtiles(V);
+  const bool vec = rows_vec_ok(target, V, V, Elem<BF16>::kVec) &&
+                   rows_vec_ok(U, V, V, Elem<BF16>::kVec) && w1_vec_ok(W1, r);
+  const int ldn = part_ld(V), c = part_chunk(V);
+  const int rows_ws = R * (gamma + 1);
+  hipLaunchKernelGGL((row_partials_kernel<BF16>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s, tg, V,
+                     rows_vec_ok(target, V, V, Elem<BF16>::kVec), nch, cu, R, rows_ws, ws.rowpart);
+  int st = launch_status();
+  if (st) return st;
+  hipLaunchKernelGGL(accept_jobs_kernel, dim3(ceil_div(rows_ws, 256)), dim3(256), 0, s, cu, anchor,
+                     tokens, lse_draft, ws.rowpart, nch, R, gamma, rows_ws, ws.jobs, cstar);
+  st = launch_status();
+  if (st) return st;
+  const int ncu = device_cu_count();
+  for (int g0 = 0; g0 < rows_ws; g0 += req_group<BF16>()) {
+    const int Rg = std::min(req_group<BF16>(), rows_ws - g0);
+    const int blocks = ceil_div(Rg, kTileN);
+    unsigned* qg = ws.queue + (size_t)(g0 / req_group<BF16>()) * kQueueWordsPerGroup;
+#define DSPARK_ACC_LAUNCH(NW_, NB_, PERCU)                                                         \
+    {                                                                                              \
+      typedef EngineGeom<BF16, KC, NW_> G;                                                         \
+      const dim3 grid(std::max(1, std::min(n_t, PERCU * ncu)));                                    \
+      if (vec)                                                                                     \
+        hipLaunchKernelGGL((accept_partials_kernel<BF16, KC, NW_, NB_, true>), grid,               \
+                           dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
+                           V, r, n_t, ws.cpart, ldn, c, ws.junk, qg);                              \
+      else                                                                                         \
+        hipLaunchKernelGGL((accept_partials_kernel<BF16, KC, NW_, NB_, false>), grid,              \
+                           dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
+                           V, r, n_t, ws.cpart, ldn, c, ws.junk, qg);                              \
+    }
+    if (blocks <= 4) DSPARK_ACC_LAUNCH(4, 1, 2)
+    else if (blocks <= 8) DSPARK_ACC_LAUNCH(8, 1, 1)
+    else if constexpr (BF16) DSPARK_ACC_LAUNCH(8, 2, 1)
+    else return DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
+#undef DSPARK_ACC_LAUNCH
+    st = launch_status();
+    if (st) return st;
+  }
+  hipLaunchKernelGGL(accept_reduce_kernel, dim3(rows_ws), dim3(kSelThreads), 0, s, ws.jobs, ws.cpart,
+                     ldn, c, n_t, cstar, ws.queue, queue_groups(rows_ws) * kNumXcd);
+  return launch_status();
+}
+
 }  // namespace dspark
 
 using namespace dspark;
@@ -565,4 +823,38 @@ extern "C" int dspark_verify(const void* target_packed, int M_cap, const int32_t
     default: return launch_verify<false, 4>(DSPARK_VERIFY_ARGS);
   }
 #undef DSPARK_VERIFY_ARGS
+}
+
+extern "C" int dspark_analytic_accept(const void* target_packed, int M_cap,
+                                      const int32_t* cu_seqlens, const int32_t* anchor,
+                                      const int32_t* tokens, const float* lse_draft, const void* U,
+                                      const void* W1, const void* W2p, int R, int gamma, int V,
+                                      int r, int dtype, float* cstar, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  int st = check_sizes(R, gamma, V, r, dtype);
+  if (st) return st;
+  if (!target_packed || !cu_seqlens || !anchor || !tokens || !lse_draft || !U || !W1 || !W2p ||
+      !cstar)
+    return DSPARK_EINVAL;
+  if (M_cap < R * (gamma + 1)) return DSPARK_ESIZE;
+  if (!ws || ws_bytes < accept_ws_bytes(R, gamma, V)) return DSPARK_EWORKSPACE;
+  AcceptWs w;
+  carve_accept(&w, ws, R, gamma, V);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define DSPARK_ACCEPT_ARGS \
+  target_packed, cu_seqlens, anchor, tokens, lse_draft, U, W1, W2p, R, gamma, V, r, cstar, w, s
+  if (dtype == DSPARK_BF16) {
+    switch (kc_instance(r)) {
+      case 1: return launch_accept<true, 1>(DSPARK_ACCEPT_ARGS);
+      case 2: return launch_accept<true, 2>(DSPARK_ACCEPT_ARGS);
+      case 4: return launch_accept<true, 4>(DSPARK_ACCEPT_ARGS);
+      default: return launch_accept<true, 8>(DSPARK_ACCEPT_ARGS);
+    }
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_accept<false, 1>(DSPARK_ACCEPT_ARGS);
+    case 2: return launch_accept<false, 2>(DSPARK_ACCEPT_ARGS);
+    default: return launch_accept<false, 4>(DSPARK_ACCEPT_ARGS);
+  }
+#undef DSPARK_ACCEPT_ARGS
 }

@@ -11,7 +11,8 @@
  *   dspark_verify         lossless rejection-sampling verification
  *
  * a sixth, dspark_advance, that carries a decode loop from one step to the
- * next on the device, plus host/device utilities (W2 pre-packing, cost-table preparation,
+ * next on the device, two observability calls (dspark_observe,
+ * dspark_analytic_accept), plus host/device utilities (W2 pre-packing, cost-table preparation,
  * workspace sizing and initialisation, status strings) and one diagnostic
  * call.
  *
@@ -95,7 +96,8 @@ typedef enum {
 /* Selector for dspark_workspace_bytes. */
 typedef enum {
   DSPARK_CALL_MARKOV_DRAFT = 0,
-  DSPARK_CALL_VERIFY = 1
+  DSPARK_CALL_VERIFY = 1,
+  DSPARK_CALL_ANALYTIC_ACCEPT = 2
 } dspark_call;
 
 /* ------------------------------------------------------------------------ */
@@ -271,6 +273,60 @@ int dspark_verify(const void* target_packed, int M_cap, const int32_t* cu_seqlen
 int dspark_advance(int32_t* anchor, const int32_t* accept_len, const int32_t* out_tokens, int R,
                    int gamma, uint64_t* step_dev, float* surv_hist, const float* surv, int n_hist,
                    void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Observability                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Words (uint64) of an observability block for R requests, block length gamma
+ * and n_bins calibration bins (1 <= n_bins <= 32); 0 for invalid sizes. */
+size_t dspark_observe_words(int R, int gamma, int n_bins);
+
+/* Add one step to an observability block ([sglang] "Observability": the
+ * cap-accept ceiling, per-request confidence and calibration such as ECE;
+ * [sglang] "Per-request differentiation on mixed traffic": windows and
+ * utilisation against the ceiling; [digest] "Verification scheduling": c_k is
+ * the pass probability of slot k given an accepted prefix). Inputs are the
+ * step's device buffers: conf, surv [R, gamma] (dspark_confidence), win_len
+ * [R] (dspark_schedule_topb), accept_len and ceiling_len [R] (dspark_verify),
+ * cu_seqlens [R + 1] (dspark_pack_ragged). Per request r let A = accept_len,
+ * C = ceiling_len, L = win_len, Lv = cu[r+1] - cu[r] - 1 (each clamped to
+ * [0, gamma]). The block (uint64 words, zero it before the first step, e.g.
+ * with dspark_workspace_init) accumulates:
+ *   [0] steps  [1] requests x steps  [2] sum (A + 1)  [3] sum A  [4] sum C
+ *   [5] sum L  [6] sum Lv  [7] reserved
+ *   [8 + h * (gamma + 1) + v]  histograms h = 0: L, 1: A, 2: C, of value v
+ *   [8 + 3 (gamma + 1) + q * R + r]  per request: q = 0: sum A, 1: sum C,
+ *                                   2: sum L
+ *   then calibration cells [kind][k - 1][bin][3] = (count, sum of
+ *   floor(p * 2^32), hits), bin = floor(p * n_bins) (p clamped to [0, 1],
+ *   the top edge in the last bin, NaN in bin 0):
+ *     kind 0 (conditional): p = conf[r, k-1], hit = slot k accepted, for
+ *                           k <= min(C + 1, Lv);
+ *     kind 1 (prefix):      p = surv[r, k-1], hit = C >= k, for k <= Lv.
+ * All counts are integers, so the block does not depend on thread order. ECE
+ * = sum over bins |sum p - hits| / count. One workgroup; calls on one block
+ * must be ordered (one stream). */
+int dspark_observe(const float* conf, const float* surv, const int32_t* win_len,
+                   const int32_t* accept_len, const int32_t* ceiling_len,
+                   const int32_t* cu_seqlens, int R, int gamma, int n_bins, uint64_t* stats,
+                   size_t stats_words, void* stream);
+
+/* Analytic acceptance rate of every verified slot ([digest] "Verification
+ * scheduling (system side)": the confidence head's target is
+ * c*_k = 1 - 1/2 ||p_d,k - p_t,k||_1). For slot k <= Lv of request r:
+ *   p_d = softmax(U[r, k-1] + W1[x_{k-1}] W2), normalised by lse_draft[r, k-1];
+ *   p_t = softmax(target_packed[cu[r] + k - 1]);
+ *   cstar[r, k-1] = sum_v min(p_d(v), p_t(v))  (= 1 - TV, float32 sums)
+ * and NaN for slots past Lv. Arguments as for dspark_verify (tokens and
+ * lse_draft from dspark_markov_draft); ws: dspark_workspace_bytes(
+ * DSPARK_CALL_ANALYTIC_ACCEPT, ...) bytes, initialised. A diagnostic pass:
+ * it reads every verified row of U and of the target once more. */
+int dspark_analytic_accept(const void* target_packed, int M_cap, const int32_t* cu_seqlens,
+                           const int32_t* anchor, const int32_t* tokens, const float* lse_draft,
+                           const void* U, const void* W1, const void* W2p, int R, int gamma,
+                           int V, int r, int dtype, float* cstar, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* The first of the two passes dspark_markov_draft runs for every slot, as a
  * call of its own (for callers that time or fuse it): the bias GEMM

@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -101,6 +101,23 @@ def test_host_validation_rejects_before_launch():
     assert lib.dspark_advance(p, p, p, 4, 7, None, p, p, 9, None) == ESIZE
     assert lib.dspark_advance(p, None, p, 4, 7, None, None, None, 0, None) == EINVAL
     assert lib.dspark_advance(p, p, p, 4, 7, None, None, p, 2, None) == EINVAL
+    # observe: sizes, bins, missing buffers, short block
+    assert lib.dspark_observe_words(4, 7, 0) == 0 and lib.dspark_observe_words(4, 7, 33) == 0
+    assert lib.dspark_observe_words(4, 17, 8) == 0
+    assert lib.dspark_observe_words(4, 7, 8) == 8 + 3 * 8 + 3 * 4 + 2 * 7 * 8 * 3
+    assert lib.dspark_observe(p, p, p, p, p, p, 4, 7, 0, p, 1 << 20, None) == ESIZE
+    assert lib.dspark_observe(p, p, p, p, None, p, 4, 7, 8, p, 1 << 20, None) == EINVAL
+    assert lib.dspark_observe(p, p, p, p, p, p, 4, 7, 8, p, 10, None) == EWS
+    # analytic acceptance: sizes, pointers, workspace
+    acc = [p, 32, p, p, p, p, p, p, p, 4, 7, 1024, 32, 0, p, p, 1 << 30, None]
+    assert lib.dspark_analytic_accept(*acc[:9], 4, 7, 1024, 32, 7, *acc[14:]) == EDTYPE
+    acc2 = list(acc); acc2[1] = 31
+    assert lib.dspark_analytic_accept(*acc2) == ESIZE
+    acc2 = list(acc); acc2[14] = None
+    assert lib.dspark_analytic_accept(*acc2) == EINVAL
+    acc2 = list(acc); acc2[16] = 64
+    assert lib.dspark_analytic_accept(*acc2) == EWS
+    assert dv.workspace_bytes(dv.CALL_ANALYTIC_ACCEPT, 64, 7, 151936, 256) > 512 * 2374 * 4
     # prepack
     assert lib.dspark_prepack_w2(p, 32, 1024, 1, p, 10, None) == EWS
     assert lib.dspark_prepack_w2(p, 32, 1024, 3, p, 1 << 30, None) == EDTYPE

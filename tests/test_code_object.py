@@ -26,7 +26,8 @@ import draft_verify_sampling_markov_amd as dv
 LLVM = "/opt/rocm/llvm/bin"
 HOT = ("markov_partials_kernel", "markov_select_kernel", "residual_partials_kernel",
        "residual_select_kernel", "row_partials_kernel", "decide_kernel", "confidence_kernel",
-       "schedule_kernel", "pack_kernel")
+       "schedule_kernel", "pack_kernel", "advance_kernel", "accept_jobs_kernel",
+       "accept_partials_kernel", "accept_reduce_kernel", "observe_kernel")
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
 
