@@ -193,6 +193,70 @@ def measure_observability(dv, dev, inp, spec, B_cap: int, steps: int):
     return out
 
 
+def measure_shards(dv, dev, spec, G: int, reps: int):
+    """One rank's draft kernels at the vocabulary-shard shape V/G (rank 0 of
+    G; same R, r and gamma): per slot the GEMM pass over the rank's columns,
+    the per-request summary, and the shard select, after one full sharded
+    draft has laid out every rank's summaries. Each is timed by replaying a
+    captured graph of the gamma slots (`reps` replays, HIP events around
+    them), so the figures are GPU time, not the host's launch rate: one graph
+    holds the whole per-rank slot (GEMM + summary + select), one the summaries
+    alone and one the selects alone; the GEMM figure is the difference. The
+    collectives between them (an all-gather of G x R x 8 bytes and an
+    all-reduce of R ids and probabilities per slot) are not measured."""
+    import torch
+    sd = dv.ShardedDraft(dev["U"], dev["W1"], dev["W2"], G)
+    sd.draft(dev["anchor"], seed=3, step=5, req_ids=dev["req_ids"])
+    torch.cuda.synchronize()
+    tf = sd.out[0].view(-1)
+    Vg = sd.bounds[1] - sd.bounds[0]
+
+    def slots(phases):
+        for k in range(1, spec.gamma + 1):
+            x_prev, xs = (dev["anchor"], 1) if k == 1 else (tf[k - 2:], spec.gamma)
+            for ph in phases:
+                if ph == "gemm":
+                    Uk = dev["U"].view(-1)[(k - 1) * spec.V:]
+                    dv.markov_shard_partials(Uk, spec.gamma * spec.V, dev["W1"], sd.W2p[0], x_prev,
+                                             xs, R=spec.R, V_g=Vg, V=spec.V, r=spec.r,
+                                             part=sd.ws[0])
+                elif ph == "summary":
+                    dv.markov_shard_summary(sd.ws[0], R=spec.R, V_g=Vg, out=sd.summaries[0])
+                else:
+                    sd.rank_slot(0, k, x_prev, xs, seed=3, step=5, req_ids=dev["req_ids"],
+                                 phase="select")
+
+    def timed(phases):
+        slots(phases)                     # eager once: loads every kernel
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            slots(phases)
+        g.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            g.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / (reps * spec.gamma)
+
+    whole = timed(("gemm", "summary", "select"))
+    summ = timed(("summary",))
+    sel = timed(("select",))
+    gemm = whole - summ - sel
+    b = 2 if spec.dtype == "bf16" else 4
+    n_t = -(-Vg // 64)
+    nbytes = spec.R * Vg * b + spec.r * Vg * b + spec.R * spec.r * b + n_t * spec.R * 8
+    out = {"G": G, "V_g": Vg, "rank": 0, "per_slot_us": round(whole, 2), "gemm_us": round(gemm, 2),
+           "summary_us": round(summ, 2), "select_us": round(sel, 2), "gemm_bytes": nbytes,
+           "gemm_gbs": round(nbytes / (gemm * 1e-6) / 1e9, 1),
+           "draft_us_per_rank": round(whole * spec.gamma, 1)}
+    log(f"[bench] {G}-way vocabulary shard (V_g={Vg}), graph-replayed: per slot {out['per_slot_us']} "
+        f"us = GEMM {out['gemm_us']} ({out['gemm_gbs']} GB/s) + summary {out['summary_us']} + "
+        f"select {out['select_us']}")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +272,10 @@ def main() -> int:
                     help="steps of the multi-step decode loop (compact verify, budget from "
                          "survivals --lag steps old) timed eagerly and as graph replays; 0 skips")
     ap.add_argument("--lag", type=int, default=2)
+    ap.add_argument("--shards", type=int, default=0,
+                    help="G > 1: also time one rank's draft kernels at the V/G vocabulary-shard "
+                         "shape (off by default, so that a kernel trace of the default run holds "
+                         "only the full-vocabulary GEMM launches)")
     ap.add_argument("--observe-calls", type=int, default=10,
                     help="timed calls of each observability pass on a cap-accept step; 0 skips")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -299,21 +367,45 @@ def main() -> int:
         log("[bench] the per-slot draft differs from the draft call")
         return 1
 
+    # ---- the GEMM's duration without per-launch event gaps: replays of a
+    # captured graph of the split draft (gamma GEMM + select pairs) and of its
+    # selects alone; the GEMM is their difference per slot ----
+    def graph_ms(passes, reps):
+        ch.draft_split(passes=passes)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            ch.draft_split(passes=passes)
+        gr.replay()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            gr.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / reps
+
+    pair_ms = graph_ms(("partials", "select"), P)
+    sel_ms = graph_ms(("select",), P)
+    gemm_graph_ms = (pair_ms - sel_ms) / g
+
     # ---- roofline of the dominant kernel (one slot's GEMM + softmax partials) ----
     b = 2 if spec.dtype == "bf16" else 4
     R, V, r = spec.R, spec.V, spec.r
     n_t = -(-V // 64)
     bytes_per_launch = R * V * b + r * V * b + R * r * b + n_t * R * 8
     flops_per_launch = 2 * R * r * V
-    achieved_gbs = bytes_per_launch / (gemm_avg_ms * 1e-3) / 1e9
-    achieved_tfs = flops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
+    achieved_gbs = bytes_per_launch / (gemm_graph_ms * 1e-3) / 1e9
+    achieved_tfs = flops_per_launch / (gemm_graph_ms * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFS
     roofline = {"kernel": "markov_partials_kernel (per-slot bias GEMM + U add + softmax partials)",
                 "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(spec.name),
-                "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(gemm_avg_ms * 1e3, 2),
-                "launches_timed": len(gemm_ms),
+                "bytes_per_launch": bytes_per_launch,
+                "avg_launch_us": round(gemm_graph_ms * 1e3, 2),
+                "timing": "HIP events around graph replays: (GEMM + select pairs - selects) / gamma",
+                "launches_timed": P * g,
+                "avg_launch_us_event_pairs": round(gemm_avg_ms * 1e3, 2),
                 "mfma": {"achieved": round(achieved_tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                          "frac": round(achieved_tfs / mfma_peak, 4), "flops_per_launch": flops_per_launch}}
 
@@ -334,6 +426,8 @@ def main() -> int:
     }
     if args.decode_steps > 0:
         line["decode"] = measure_decode(dv, dev, inp, spec, B_cap, args.decode_steps, args.lag)
+    if args.shards > 1:
+        line["vocab_shards"] = measure_shards(dv, dev, spec, args.shards, 20)
     if args.observe_calls > 0:
         line["observability"] = measure_observability(dv, dev, inp, spec, B_cap, args.observe_calls)
     if args.calibrate_copy:

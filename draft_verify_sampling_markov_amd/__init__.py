@@ -48,6 +48,12 @@ _SIGNATURES = {
     "dspark_verify": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _u64,
                            _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_advance": (_i, [_vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _vp]),
+    "dspark_markov_shard_partials": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                          _vp, _sz, _vp]),
+    "dspark_markov_shard_summary": (_i, [_vp, _sz, _i, _i, _vp, _vp]),
+    "dspark_markov_shard_select": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i,
+                                        _u64, _u64, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                        _vp, _i, _vp]),
     "dspark_observe_words": (_sz, [_i, _i, _i]),
     "dspark_observe": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
     "dspark_analytic_accept": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -366,6 +372,39 @@ def advance(anchor, accept_len, out_tokens, *, step_dev=None, surv_hist=None, su
         _opt(surv, "surv", torch.float32, (R, gamma)), n_hist, _stream(stream)))
 
 
+def markov_shard_partials(U_k, ldU: int, W1, W2p_g, x_prev, xstride: int, *, R: int, V_g: int,
+                          V: int, r: int, part, stream=None):
+    """Rank's GEMM pass over its V_g columns (dspark_markov_shard_partials)."""
+    _check(load_library().dspark_markov_shard_partials(
+        U_k.data_ptr(), int(ldU), _dev(W1, "W1", U_k.dtype, (V, r)), _dev(W2p_g, "W2p", U_k.dtype),
+        x_prev.data_ptr(), int(xstride), R, int(V_g), V, r, _dtype_code(U_k), _dev(part, "part"),
+        part.numel() * part.element_size(), _stream(stream)))
+
+
+def markov_shard_summary(part, *, R: int, V_g: int, out, stream=None):
+    """Rank's (max, sum of exp) per request from its partials workspace into
+    ``out`` (float32 [R, 2] or a view of a [G, R, 2] buffer's row)."""
+    _check(load_library().dspark_markov_shard_summary(
+        _dev(part, "part"), part.numel() * part.element_size(), R, V_g, out.data_ptr(),
+        _stream(stream)))
+
+
+def markov_shard_select(U_k, ldU: int, W1, W2p_g, x_prev, xstride: int, part, summaries, *,
+                        G: int, g: int, v0: int, k: int, R: int, V_g: int, V: int, r: int,
+                        seed: int, step: int, req_ids, tok_out, p_out, lse_out, ostride: int = 1,
+                        step_dev=None, stream=None):
+    """Rank g's select for slot k (dspark_markov_shard_select); pointer-level
+    outputs like markov_select."""
+    torch = _torch()
+    _check(load_library().dspark_markov_shard_select(
+        U_k.data_ptr(), int(ldU), _dev(W1, "W1", U_k.dtype, (V, r)), _dev(W2p_g, "W2p", U_k.dtype),
+        x_prev.data_ptr(), int(xstride), _dev(part, "part"),
+        _dev(summaries, "summaries", torch.float32, (G, R, 2)), int(G), int(g), int(v0), seed, step,
+        _opt(step_dev, "step_dev", torch.int64, (1,)), req_ids.data_ptr(), int(k), R, int(V_g), V, r,
+        _dtype_code(U_k), tok_out.data_ptr(), p_out.data_ptr(), lse_out.data_ptr(), int(ostride),
+        _stream(stream)))
+
+
 def observe_words(R: int, gamma: int, n_bins: int) -> int:
     return int(load_library().dspark_observe_words(R, gamma, n_bins))
 
@@ -447,7 +486,8 @@ def analytic_accept(target_packed, cu_seqlens, anchor, tokens, lse_draft, U, W1,
     return out
 
 
-from .chain import Chain  # noqa: E402  (needs the functions above)
+from .chain import Chain  # noqa: E402
+from .shard import ShardedDraft  # noqa: E402  (needs the functions above)
 
 __all__ = [
     "load_library", "status_string", "DsparkError", "workspace_bytes", "workspace_init",
@@ -455,7 +495,8 @@ __all__ = [
     "prepack_w2", "cost_table_prepare", "markov_draft", "confidence", "schedule_topb",
     "pack_ragged", "verify", "markov_logits", "markov_partials",
     "markov_select", "advance", "observe_words", "new_observe_block", "observe", "parse_observe",
-    "analytic_accept", "Chain", "EXPORTS", "F32", "BF16",
+    "analytic_accept", "markov_shard_partials", "markov_shard_summary", "markov_shard_select", "ShardedDraft", "Chain",
+    "EXPORTS", "F32", "BF16",
     "VERIFY_STATIC", "VERIFY_COMPACT", "VERIFY_CAP_ACCEPT", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "VERIFY_MODES", "SCHED_MODES",
 ]

@@ -98,11 +98,15 @@ class Chain:
                             step=self.step, req_ids=i["req_ids"], out=self.draft_out,
                             ws=self.ws_draft)
 
-    def draft_split(self, events=None):
-        """The draft as its two per-slot passes -- the same launches draft()
-        makes through dspark_markov_draft. ``events``: optional list of gamma
-        (start, end) torch.cuda.Event pairs recorded around each slot's GEMM +
-        partials launch, on the current stream."""
+    def draft_split(self, events=None, passes=("partials", "select")):
+        """The draft as its two per-slot passes, through the split calls: the
+        same GEMM and select kernels dspark_markov_draft launches, except that
+        the slot's draft uniform is drawn in the select rather than in the
+        GEMM's prologue. ``events``: optional list of gamma (start, end)
+        torch.cuda.Event pairs recorded around each slot's GEMM + partials
+        launch, on the current stream. ``passes``: ("select",) re-runs only
+        the selects over the partials already in the workspace (repeatable:
+        a select reads the partials and leaves the tile queue at zero)."""
         i = self.inp
         U, W1 = i["U"], i["W1"]
         tok, p, lse = self.draft_out
@@ -111,15 +115,18 @@ class Chain:
         for k in range(1, g + 1):
             Uk = Uf[(k - 1) * V:]
             x_prev, xs = (self.anchor, 1) if k == 1 else (tf[k - 2:], g)
-            if events is not None:
-                events[k - 1][0].record()
-            markov_partials(Uk, g * V, W1, self.W2p, x_prev, xs, R=self.R, V=V, r=self.r,
-                            part=self.ws_draft)
-            if events is not None:
-                events[k - 1][1].record()
-            markov_select(Uk, g * V, W1, self.W2p, x_prev, xs, self.ws_draft, k=k, R=self.R, V=V,
-                          r=self.r, seed=self.seed, step=self.step, req_ids=i["req_ids"],
-                          tok_out=tf[k - 1:], p_out=pf[k - 1:], lse_out=lf[k - 1:], ostride=g)
+            if "partials" in passes:
+                if events is not None:
+                    events[k - 1][0].record()
+                markov_partials(Uk, g * V, W1, self.W2p, x_prev, xs, R=self.R, V=V, r=self.r,
+                                part=self.ws_draft)
+                if events is not None:
+                    events[k - 1][1].record()
+            if "select" in passes:
+                markov_select(Uk, g * V, W1, self.W2p, x_prev, xs, self.ws_draft, k=k, R=self.R,
+                              V=V, r=self.r, seed=self.seed, step=self.step,
+                              req_ids=i["req_ids"], tok_out=tf[k - 1:], p_out=pf[k - 1:],
+                              lse_out=lf[k - 1:], ostride=g)
 
     def confidence(self):
         i = self.inp

@@ -521,7 +521,7 @@ __device__ __forceinline__ void tile_logits(const f32x4 acc[4], const float u16[
 // sums in tile order, a fixed-order scan over the lanes of each wave, then the
 // wave totals in wave order) and T = u S, finds the first thread whose
 // inclusive prefix exceeds T, and that thread walks its tiles to the first one
-// where the running sum crosses T. Result (in every thread): the crossing
+// where the running sum crosses T (ABS: T = u as given). Result (in every thread): the crossing
 // tile and the mass before it (pb). When rounding leaves no crossing, the
 // result is the last tile with positive weight and pb = -inf, which makes the
 // in-tile search end at that tile's last positive entry. CMAX > 0: the
@@ -569,7 +569,7 @@ __device__ __forceinline__ float block_sum(float v, BlockSearchShared& sh) {
   return s;
 }
 
-template <int CMAX, typename WFn>
+template <int CMAX, bool ABS = false, typename WFn>
 __device__ __forceinline__ WaveSearch block_tile_search(WFn w, int t0, int cnt, float u,
                                                         BlockSearchShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -605,7 +605,7 @@ __device__ __forceinline__ WaveSearch block_tile_search(WFn w, int t0, int cnt, 
   }
   WaveSearch r;
   r.S = S;
-  r.T = u * S;
+  r.T = ABS ? u : u * S;  // ABS: u is the threshold itself, not a fraction of S
   const float prev = wave_shift_up1(incl) + off;
   incl += off;
   const unsigned long long pm = __ballot(incl > r.T);

@@ -124,12 +124,12 @@ template <bool BF16, int KC, int NW, int NB, bool VEC>
 __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
-    const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t,
+    const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t, int w1_rows,
     float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk,
     unsigned* __restrict__ queue, DrawArgs draw) {
   const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk, draw};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
-                                         R, V, r, n_t, epi, queue);
+                                         R, V, r, n_t, epi, queue, w1_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -210,6 +210,141 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
     tok_out[(size_t)n * ostride] = t * kTileV + sel;
     p_out[(size_t)n * ostride] = esel / ws.S;
     lse_out[(size_t)n * ostride] = m + __logf(ws.S);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// vocabulary-sharded draft: per-rank summary and select
+// ---------------------------------------------------------------------------
+
+// SGLang DSpark blog, "Performance optimisation and zero-overhead scheduling":
+// the block drafter's matmul is sharded. With tensor parallelism over the
+// vocabulary, rank g of G holds columns [v0, v0 + V_g) of W2 and of U_k and
+// runs the GEMM pass on them unchanged (dspark_markov_partials). A slot then
+// needs one exchange of per-rank softmax summaries (m_g, S_g) per request and
+// one of the chosen token; every rank merges the gathered summaries in rank
+// order, so all ranks see the same global (m, S), the same threshold u S and
+// the same mass P_g before each rank, and exactly one rank (the one with
+// P_g <= u S < P_{g+1}, the last rank for anything above) finds the token in
+// its own tiles.
+
+// Per request: the rank's (max, sum of exp) over its tile partials.
+template <int CMAX>
+__global__ __launch_bounds__(kSelThreads) void markov_shard_summary_kernel(
+    const float2* __restrict__ part, int ldn, int c, int n_t, float2* __restrict__ summary) {
+  __shared__ BlockSearchShared sh;
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const float2* prow = part + (size_t)n * ldn;
+  const int t0 = tid * c;
+  const int cnt = max(0, min(c, n_t - t0));
+  float2 pv[CMAX > 0 ? CMAX : 1];
+  float lm = -INFINITY;
+  if constexpr (CMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) pv[i] = prow[min(i, c - 1) * kSelThreads + tid];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) lm = fmaxf(lm, i < cnt ? pv[i].x : -INFINITY);
+  } else {
+    for (int i = 0; i < cnt; ++i) lm = fmaxf(lm, prow[i * kSelThreads + tid].x);
+  }
+  const float m = block_max(lm, sh);
+  __syncthreads();  // block_sum below reuses the reduction slots
+  float ls = 0.0f;
+  if constexpr (CMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) ls += i < cnt ? pv[i].y * __expf(pv[i].x - m) : 0.0f;
+  } else {
+    for (int i = 0; i < cnt; ++i) {
+      const float2 q = prow[i * kSelThreads + tid];
+      ls += q.y * __expf(q.x - m);
+    }
+  }
+  const float S = block_sum(ls, sh);
+  if (tid == 0) summary[n] = make_float2(m, S);
+}
+
+// Per request: merge the G gathered summaries, decide the owner of u S, and
+// on the owning rank search its own tiles (the select's search and one-tile
+// recompute, with the global max and an absolute threshold). Writes, at
+// n * ostride: the global token id and its probability on the owning rank,
+// -1 and 0 elsewhere (ready for MAX / SUM reductions), and the global
+// log-sum-exp on every rank.
+template <bool BF16, int KC, int CMAX, bool VW>
+__global__ __launch_bounds__(kSelThreads) void markov_shard_select_kernel(
+    const typename Elem<BF16>::T* __restrict__ U, long long ldU,
+    const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
+    const int* __restrict__ xprev, int xstride, int Vg, int Vfull, int r, int n_t,
+    const float2* __restrict__ part, int ldn, int c, const float2* __restrict__ summaries, int R,
+    int G, int g, int v0, uint64_t seed, StepArg step, const uint32_t* __restrict__ req_ids, int k,
+    int* __restrict__ tok_out, float* __restrict__ p_out, float* __restrict__ lse_out,
+    int ostride, unsigned* __restrict__ queue, int n_queue) {
+  typedef typename Elem<BF16>::Frag Frag;
+  __shared__ BlockSearchShared sh;
+  const int n = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+  if (n == 0 && tid < n_queue) queue[tid * kQueueStride] = 0u;
+  const float2* prow = part + (size_t)n * ldn;
+  const int t0 = tid * c;
+  const int cnt = max(0, min(c, n_t - t0));
+  float2 pv[CMAX > 0 ? CMAX : 1];
+  if constexpr (CMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) pv[i] = prow[min(i, c - 1) * kSelThreads + tid];
+  }
+  // the W1 row is gathered with the global token id (W1 is not sharded)
+  const int x = clamp_token(xprev[(size_t)n * xstride], Vfull);
+  Frag b[KC];
+  load_b_row<BF16, KC, VW>(W1 + (size_t)x * r, r, lane, b);
+  const float u = slot_uniform(seed, step.get(), req_ids[n], k, kPurposeDraft);
+  // global merge in rank order (identical on every rank)
+  float m = -INFINITY;
+  for (int h = 0; h < G; ++h) m = fmaxf(m, summaries[(size_t)h * R + n].x);
+  float S = 0.0f, P = 0.0f, own = 0.0f;
+  for (int h = 0; h < G; ++h) {
+    const float2 q = summaries[(size_t)h * R + n];
+    const float sh_ = q.x == -INFINITY ? 0.0f : q.y * __expf(q.x - m);
+    if (h < g) P += sh_;
+    if (h == g) own = sh_;
+    S += sh_;
+  }
+  const float T = u * S;
+  const bool owner = P <= T && (g == G - 1 || T < P + own);  // workgroup-uniform
+  if (!owner) {
+    if (tid == 0) {
+      tok_out[(size_t)n * ostride] = -1;
+      p_out[(size_t)n * ostride] = 0.0f;
+      lse_out[(size_t)n * ostride] = m + __logf(S);
+    }
+    return;
+  }
+  WaveSearch ws;
+  if constexpr (CMAX > 0) {
+    float w[CMAX];
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) w[i] = i < cnt ? pv[i].y * __expf(pv[i].x - m) : 0.0f;
+    ws = block_tile_search<CMAX, true>([&](int i) { return w[i]; }, t0, cnt, T - P, sh);
+  } else {
+    ws = block_tile_search<0, true>([&](int i) {
+      const float2 q = prow[i * kSelThreads + tid];
+      return q.y * __expf(q.x - m);
+    }, t0, cnt, T - P, sh);
+  }
+  if (tid >= kWave) return;  // wave 0 finishes; no barrier below
+  const int t = min(max(ws.tstar, 0), n_t - 1);
+  ATile<BF16, KC> at;
+  load_a_tile<BF16, KC>(W2p, t, lane, at);
+  const int v = t * kTileV + lane;
+  const bool valid = v < Vg;
+  const float uo = to_f32(U[(size_t)n * ldU + min(v, Vg - 1)]);
+  f32x4 acc[4];
+  tile_mma_regs<BF16, KC>(at, b, acc);
+  const float zo = own_entry(acc, lane) + uo;
+  const float e = valid ? __expf(zo - m) : 0.0f;
+  const int sel = tile_pick(e, valid, ws.pb, ws.T, lane);
+  const float esel = readlane_f(e, sel);
+  if (lane == 0) {
+    tok_out[(size_t)n * ostride] = v0 + t * kTileV + sel;
+    p_out[(size_t)n * ostride] = esel / S;
+    lse_out[(size_t)n * ostride] = m + __logf(S);
   }
 }
 
@@ -295,8 +430,8 @@ template <bool BF16, int KC, int NW, int NB>
 static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                                const int32_t* xprev, int xstride, int Rg, int V, int r,
-                               float2* part, float2* junk, unsigned* queue, DrawArgs draw,
-                               hipStream_t s) {
+                               int w1_rows, float2* part, float2* junk, unsigned* queue,
+                               DrawArgs draw, hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
   const int per_cu = NW == 4 ? 2 : 1;
@@ -304,12 +439,12 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
   const int ldn = part_ld(V), c = part_chunk(V);
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
-                       G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, part, ldn,
-                       c, junk, queue, draw);
+                       G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, w1_rows,
+                       part, ldn, c, junk, queue, draw);
   else
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
                        dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
-                       n_t, part, ldn, c, junk, queue, draw);
+                       n_t, w1_rows, part, ldn, c, junk, queue, draw);
   return launch_status();
 }
 
@@ -318,8 +453,8 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
 template <bool BF16, int KC>
 static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                            const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
-                           const int32_t* xprev, int xstride, int R, int V, int r, float2* part,
-                           DrawArgs draw, hipStream_t s) {
+                           const int32_t* xprev, int xstride, int R, int V, int r, int w1_rows,
+                           float2* part, DrawArgs draw, hipStream_t s) {
   float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
   unsigned* queue = markov_queue(part, R, V);
   const int ldn = part_ld(V);
@@ -337,11 +472,11 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
     }
     int st;
     if (blocks <= 4)
-      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, dg, s);
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, s);
     else if (blocks <= 8)
-      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, dg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, s);
     else if constexpr (BF16)
-      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, pg, junk, qg, dg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, s);
     else
       st = DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
     if (st) return st;
@@ -378,6 +513,35 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
 }
 
 template <bool BF16, int KC>
+static int launch_shard_select(const void* U, long long ldU, const void* W1, const void* W2p,
+                               const int32_t* xprev, int xstride, const float2* part,
+                               const float2* summaries, int G, int g, int v0, uint64_t seed,
+                               StepArg step, const uint32_t* req_ids, int k, int R, int Vg,
+                               int Vfull, int r, int32_t* tok, float* p, float* lse, int ostride,
+                               hipStream_t s) {
+  typedef typename Elem<BF16>::T T;
+  const int n_t = n_vtiles(Vg), c = part_chunk(Vg), ldn = part_ld(Vg);
+  unsigned* queue = markov_queue(const_cast<float2*>(part), R, Vg);
+  const int n_queue = queue_groups(R) * kNumXcd;
+  const T* Ub = static_cast<const T*>(U);
+  const T* W1b = static_cast<const T*>(W1);
+  const T* W2b = static_cast<const T*>(W2p);
+#define DSPARK_SHSEL(CM, VW_)                                                                     \
+  hipLaunchKernelGGL((markov_shard_select_kernel<BF16, KC, CM, VW_>), dim3(R), dim3(kSelThreads), 0, \
+                     s, Ub, ldU, W1b, W2b, xprev, xstride, Vg, Vfull, r, n_t, part, ldn, c,        \
+                     summaries, R, G, g, v0, seed, step, req_ids, k, tok, p, lse, ostride, queue,  \
+                     n_queue)
+  const bool vw = w1_vec_ok(W1, r);
+  if (c <= 16) {
+    if (vw) DSPARK_SHSEL(16, true); else DSPARK_SHSEL(16, false);
+  } else {
+    if (vw) DSPARK_SHSEL(0, true); else DSPARK_SHSEL(0, false);
+  }
+#undef DSPARK_SHSEL
+  return launch_status();
+}
+
+template <bool BF16, int KC>
 static int launch_markov(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
                          uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                          int V, int r, int32_t* tokens, float* p_draft, float* lse_draft,
@@ -394,7 +558,7 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
     const T* Uk = Ub + (size_t)(k - 1) * V;
     const DrawArgs draw{seed, step, req_ids, k, markov_u(part, R, V)};
     int st = launch_partials<BF16, KC>(Uk, ldU, vec_u && vec_w1, W1b, W2b, xprev, xstride, R, V, r,
-                                       part, draw, s);
+                                       V, part, draw, s);
     if (st) return st;
     st = launch_select<BF16, KC>(Uk, ldU, vec_u, vec_w1, W1b, W2b, xprev, xstride, R, V, r, part,
                                  seed, step, req_ids, k, tokens + (k - 1), p_draft + (k - 1),
@@ -407,13 +571,13 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
 template <bool BF16, int KC>
 static int launch_partials_api(const void* U, long long ldU, const void* W1, const void* W2p,
                                const int32_t* x_prev, int xstride, int R, int V, int r,
-                               float2* part, hipStream_t s) {
+                               int w1_rows, float2* part, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
   const bool vec = u_vec_ok<BF16>(U, ldU, V) && w1_vec_ok(W1, r);
   const DrawArgs none{0, StepArg{0, nullptr}, nullptr, 0, nullptr};
   return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
-                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, part, none,
-                                   s);
+                                   static_cast<const T*>(W2p), x_prev, xstride, R, V, r, w1_rows,
+                                   part, none, s);
 }
 
 template <bool BF16, int KC>
@@ -523,15 +687,16 @@ extern "C" int dspark_markov_logits(const void* U_k, long long ldU, const void* 
 }
 
 static int partials_dispatch(const void* U, long long ldU, const void* W1, const void* W2p,
-                             const int32_t* x_prev, int xstride, int R, int V, int r, int dtype,
-                             float2* part, hipStream_t s) {
+                             const int32_t* x_prev, int xstride, int R, int V, int r, int w1_rows,
+                             int dtype, float2* part, hipStream_t s) {
   if (dtype == DSPARK_BF16) {
-    DSPARK_KC_DISPATCH(true, launch_partials_api, U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s)
+    DSPARK_KC_DISPATCH(true, launch_partials_api, U, ldU, W1, W2p, x_prev, xstride, R, V, r, w1_rows,
+                       part, s)
   }
   switch (kc_instance(r)) {
-    case 1: return launch_partials_api<false, 1>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s);
-    case 2: return launch_partials_api<false, 2>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s);
-    default: return launch_partials_api<false, 4>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, part, s);
+    case 1: return launch_partials_api<false, 1>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, w1_rows, part, s);
+    case 2: return launch_partials_api<false, 2>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, w1_rows, part, s);
+    default: return launch_partials_api<false, 4>(U, ldU, W1, W2p, x_prev, xstride, R, V, r, w1_rows, part, s);
   }
 }
 
@@ -544,7 +709,20 @@ extern "C" int dspark_markov_partials(const void* U_k, long long ldU, const void
   if (!U_k || !W1 || !W2p || !x_prev || !part) return DSPARK_EINVAL;
   if (ldU < V || xstride < 1) return DSPARK_ESIZE;
   if (part_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
-  return partials_dispatch(U_k, ldU, W1, W2p, x_prev, xstride, R, V, r, dtype,
+  return partials_dispatch(U_k, ldU, W1, W2p, x_prev, xstride, R, V, r, V, dtype,
+                           static_cast<float2*>(part), static_cast<hipStream_t>(stream));
+}
+
+extern "C" int dspark_markov_shard_partials(const void* U_k, long long ldU, const void* W1,
+                                            const void* W2p, const int32_t* x_prev, int xstride,
+                                            int R, int V_g, int V, int r, int dtype, void* part,
+                                            size_t part_bytes, void* stream) {
+  int st = check_sizes(R, 1, V, r, dtype);
+  if (st) return st;
+  if (!U_k || !W1 || !W2p || !x_prev || !part) return DSPARK_EINVAL;
+  if (V_g < 1 || V_g > V || ldU < V_g || xstride < 1) return DSPARK_ESIZE;
+  if (part_bytes < markov_ws_bytes(R, V_g)) return DSPARK_EWORKSPACE;
+  return partials_dispatch(U_k, ldU, W1, W2p, x_prev, xstride, R, V_g, r, V, dtype,
                            static_cast<float2*>(part), static_cast<hipStream_t>(stream));
 }
 
@@ -590,4 +768,60 @@ extern "C" int dspark_markov_select(const void* U_k, long long ldU, const void* 
     default: return launch_select_api<false, 4>(DSPARK_SEL_ARGS);
   }
 #undef DSPARK_SEL_ARGS
+}
+
+extern "C" int dspark_markov_shard_summary(const void* part, size_t part_bytes, int R, int V_g,
+                                           float* summary, void* stream) {
+  if (R < 1 || R > kMaxRows || V_g < 1) return DSPARK_ESIZE;
+  if (!part || !summary) return DSPARK_EINVAL;
+  if (part_bytes < markov_ws_bytes(R, V_g)) return DSPARK_EWORKSPACE;
+  const int n_t = n_vtiles(V_g), c = part_chunk(V_g), ldn = part_ld(V_g);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float2* pt = static_cast<const float2*>(part);
+  float2* out = reinterpret_cast<float2*>(summary);
+  if (c <= 16)
+    hipLaunchKernelGGL(markov_shard_summary_kernel<16>, dim3(R), dim3(kSelThreads), 0, s, pt, ldn,
+                       c, n_t, out);
+  else
+    hipLaunchKernelGGL(markov_shard_summary_kernel<0>, dim3(R), dim3(kSelThreads), 0, s, pt, ldn, c,
+                       n_t, out);
+  return launch_status();
+}
+
+extern "C" int dspark_markov_shard_select(const void* U_k, long long ldU, const void* W1,
+                                          const void* W2p, const int32_t* x_prev, int xstride,
+                                          const void* part, const float* summaries, int G, int g,
+                                          int v0, uint64_t seed, uint64_t step,
+                                          const uint64_t* step_dev, const uint32_t* req_ids, int k,
+                                          int R, int V_g, int V, int r, int dtype,
+                                          int32_t* tok_out, float* p_out, float* lse_out,
+                                          int ostride, void* stream) {
+  int st = check_sizes(R, 1, V, r, dtype);
+  if (st) return st;
+  if (!U_k || !W1 || !W2p || !x_prev || !part || !summaries || !req_ids || !tok_out || !p_out ||
+      !lse_out)
+    return DSPARK_EINVAL;
+  if (G < 1 || G > 64 || g < 0 || g >= G || V_g < 1 || v0 < 0 || (long long)v0 + V_g > V)
+    return DSPARK_ESIZE;
+  if (ldU < V_g || xstride < 1 || ostride < 1 || k < 1 || k > kMaxGamma + 1) return DSPARK_ESIZE;
+  const StepArg sa{step, step_dev};
+  const float2* pt = static_cast<const float2*>(part);
+  const float2* sm = reinterpret_cast<const float2*>(summaries);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define DSPARK_SHARD_ARGS U_k, ldU, W1, W2p, x_prev, xstride, pt, sm, G, g, v0, seed, sa, req_ids, \
+                          k, R, V_g, V, r, tok_out, p_out, lse_out, ostride, s
+  if (dtype == DSPARK_BF16) {
+    switch (kc_instance(r)) {
+      case 1: return launch_shard_select<true, 1>(DSPARK_SHARD_ARGS);
+      case 2: return launch_shard_select<true, 2>(DSPARK_SHARD_ARGS);
+      case 4: return launch_shard_select<true, 4>(DSPARK_SHARD_ARGS);
+      default: return launch_shard_select<true, 8>(DSPARK_SHARD_ARGS);
+    }
+  }
+  switch (kc_instance(r)) {
+    case 1: return launch_shard_select<false, 1>(DSPARK_SHARD_ARGS);
+    case 2: return launch_shard_select<false, 2>(DSPARK_SHARD_ARGS);
+    default: return launch_shard_select<false, 4>(DSPARK_SHARD_ARGS);
+  }
+#undef DSPARK_SHARD_ARGS
 }

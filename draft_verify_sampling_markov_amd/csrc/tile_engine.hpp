@@ -61,7 +61,7 @@ struct EngineGeom {
 // load, so the prologue has no branch that would drain the loads in flight.
 template <bool BF16, int KC, int NB, bool VEC, typename TokFn>
 __device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restrict__ W1, TokFn tok,
-                                         int R, int r, int V, int wave, int nw, int lane,
+                                         int R, int r, int w1_rows, int wave, int nw, int lane,
                                          typename Elem<BF16>::Frag b[NB][KC]) {
   typedef typename Elem<BF16>::T T;
   typedef typename Elem<BF16>::Frag Frag;
@@ -69,7 +69,7 @@ __device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restric
   for (int nb = 0; nb < NB; ++nb) {
     const int n = (wave + nw * nb) * kTileN + (lane & 15);
     const bool ok = n < R;
-    const int x = clamp_token(tok(min(n, R - 1)), V);
+    const int x = clamp_token(tok(min(n, R - 1)), w1_rows);
     const T* row = W1 + (size_t)x * r;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -160,12 +160,15 @@ __device__ __forceinline__ void engine_step(
   for (int k = 0; k < Geo::kPer; ++k) nxt[Geo::slot(k, tid)] = w_ready[k];
 }
 
-// queue: this launch's kQueueWordsPerGroup counters (zero on entry).
+// queue: this launch's kQueueWordsPerGroup counters (zero on entry). w1_rows:
+// rows of W1 (token ids are clamped into them); V: vocabulary columns of this
+// launch (fewer than w1_rows for one shard of a vocabulary-sharded draft).
 template <bool BF16, int KC, int NW, int NB, bool VEC, class Epi, typename TokFn>
 __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __restrict__ W1,
                                                 const typename Elem<BF16>::T* __restrict__ W2p,
                                                 TokFn tok, int R, int V, int r, int n_t,
-                                                const Epi& epi, unsigned* __restrict__ queue) {
+                                                const Epi& epi, unsigned* __restrict__ queue,
+                                                int w1_rows) {
   typedef EngineGeom<BF16, KC, NW> Geo;
   typedef typename Elem<BF16>::Frag Frag;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -194,7 +197,7 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
     for (int i = 0; i < Geo::kPer; ++i) first[i] = s[Geo::slot(i, tid)];
   }
   Frag b[NB][KC];
-  gather_b<BF16, KC, NB, VEC>(W1, tok, R, r, V, wave, NW, lane, b);
+  gather_b<BF16, KC, NB, VEC>(W1, tok, R, r, w1_rows, wave, NW, lane, b);
   typename Epi::St st[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st[nb] = epi.prepare((wave + NW * nb) * kTileN + nl);

@@ -360,6 +360,58 @@ int dspark_markov_select(const void* U_k, long long ldU, const void* W1, const v
                          float* lse_out, int ostride, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Vocabulary-sharded draft (per-rank calls)                                 */
+/* ------------------------------------------------------------------------ */
+
+/* [sglang] "Performance optimisation and zero-overhead scheduling": the block
+ * drafter's matmul is sharded. Under tensor parallelism over the vocabulary,
+ * rank g of G owns columns [v0, v0 + V_g) of W2 (pre-packed on its own with
+ * dspark_prepack_w2 for V_g columns) and of U; W1 is whole on every rank and
+ * token ids are global. One draft slot k on rank g is:
+ *   1. dspark_markov_shard_partials -- the GEMM pass on the rank's columns;
+ *   2. dspark_markov_shard_summary -- the rank's (m_g, S_g) per request;
+ *   3. all-gather of the G summaries into [G, R, 2] (a collective);
+ *   4. dspark_markov_shard_select  -- merge, owner test, in-shard search;
+ *   5. all-reduce MAX of the token and SUM of the probability (a collective);
+ *      every rank then holds x_k for slot k + 1.
+ * The draw is the single-device draw: the threshold u S over the global
+ * vocabulary in ascending id order, u the slot's draft uniform. */
+
+/* dspark_markov_partials on rank g's V_g columns: U_k points at the rank's
+ * first column (rows ldU elements apart), W2p is the rank's pre-packed
+ * [r, V_g] slice, and the previous tokens are global ids in [0, V) that pick
+ * rows of the whole W1 [V, r]. part: dspark_workspace_bytes(
+ * DSPARK_CALL_MARKOV_DRAFT, R, 1, V_g, r) bytes, initialised. */
+int dspark_markov_shard_partials(const void* U_k, long long ldU, const void* W1, const void* W2p,
+                                 const int32_t* x_prev, int xstride, int R, int V_g, int V, int r,
+                                 int dtype, void* part, size_t part_bytes, void* stream);
+
+/* Per request n: summary[n] = (max over the rank's tiles, sum of exp(z - max))
+ * as two floats, from the partials of dspark_markov_partials over V_g
+ * columns (part: the workspace of dspark_markov_shard_partials, part_bytes its
+ * size). */
+int dspark_markov_shard_summary(const void* part, size_t part_bytes, int R, int V_g,
+                                float* summary, void* stream);
+
+/* Rank g's select for slot k. summaries [G, R, 2]: every rank's summary, rank
+ * major. Every rank merges them in rank order into the global (m, S), forms
+ * T = u S and the mass P_h before each rank h; the rank with
+ * P_g <= T < P_{g+1} (the last rank for T >= P_{G-1}) searches its own tiles
+ * for T - P_g, recomputing the crossing tile. Writes at n * ostride: tok_out =
+ * the global id on the owning rank, -1 elsewhere; p_out = the id's draft
+ * probability on the owning rank, 0 elsewhere; lse_out = m + ln S on every
+ * rank. U_k, ldU, x_prev, xstride, part as for dspark_markov_select (U_k at
+ * the rank's first column); V is the full vocabulary (W1 rows, token range).
+ * Restores the partials workspace's tile queue, like dspark_markov_select.
+ * 1 <= G <= 64, 0 <= g < G, v0 + V_g <= V. */
+int dspark_markov_shard_select(const void* U_k, long long ldU, const void* W1, const void* W2p,
+                               const int32_t* x_prev, int xstride, const void* part,
+                               const float* summaries, int G, int g, int v0, uint64_t seed,
+                               uint64_t step, const uint64_t* step_dev, const uint32_t* req_ids,
+                               int k, int R, int V_g, int V, int r, int dtype, int32_t* tok_out,
+                               float* p_out, float* lse_out, int ostride, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Diagnostic                                                                */
 /* ------------------------------------------------------------------------ */
 

@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -118,6 +118,22 @@ def test_host_validation_rejects_before_launch():
     acc2 = list(acc); acc2[16] = 64
     assert lib.dspark_analytic_accept(*acc2) == EWS
     assert dv.workspace_bytes(dv.CALL_ANALYTIC_ACCEPT, 64, 7, 151936, 256) > 512 * 2374 * 4
+    # sharded draft: sizes, rank range, shard range, workspace
+    assert lib.dspark_markov_shard_partials(p, 1024, p, p, p, 1, 4, 2000, 1024, 32, 0, p, 1 << 30, None) == ESIZE
+    assert lib.dspark_markov_shard_partials(p, 1024, None, p, p, 1, 4, 512, 1024, 32, 0, p, 1 << 30, None) == EINVAL
+    assert lib.dspark_markov_shard_partials(p, 1024, p, p, p, 1, 4, 512, 1024, 32, 0, p, 64, None) == EWS
+    assert lib.dspark_markov_shard_summary(p, 1 << 30, 0, 100, p, None) == ESIZE
+    assert lib.dspark_markov_shard_summary(None, 1 << 30, 4, 100, p, None) == EINVAL
+    assert lib.dspark_markov_shard_summary(p, 16, 4, 100, p, None) == EWS
+    sel = [p, 1024, p, p, p, 1, p, p, 2, 0, 0, 0, 0, None, p, 1, 4, 512, 1024, 32, 0, p, p, p, 1, None]
+    bad = list(sel); bad[9] = 2                      # g >= G
+    assert lib.dspark_markov_shard_select(*bad) == ESIZE
+    bad = list(sel); bad[10] = 600                   # v0 + V_g > V
+    assert lib.dspark_markov_shard_select(*bad) == ESIZE
+    bad = list(sel); bad[7] = None                   # summaries
+    assert lib.dspark_markov_shard_select(*bad) == EINVAL
+    bad = list(sel); bad[20] = 9                     # dtype
+    assert lib.dspark_markov_shard_select(*bad) == EDTYPE
     # prepack
     assert lib.dspark_prepack_w2(p, 32, 1024, 1, p, 10, None) == EWS
     assert lib.dspark_prepack_w2(p, 32, 1024, 3, p, 1 << 30, None) == EDTYPE
