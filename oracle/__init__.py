@@ -42,6 +42,8 @@ from .pack import pack_ragged
 from .verify import verify, VERIFY_STATIC, VERIFY_COMPACT, VERIFY_CAP_ACCEPT
 from .chain import chain, decode
 from .observe import analytic_acceptance, new_stats, observe, ece, utilisation
+from .calibrate import sts_fit, ece_of
+from . import calibrate
 
 __all__ = [
     "philox4x64_10", "uniform24", "uniforms", "PURPOSE_DRAFT", "PURPOSE_ACCEPT",
@@ -50,5 +52,5 @@ __all__ = [
     "quantize_survival", "schedule_topb", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "pack_ragged", "verify", "VERIFY_STATIC", "VERIFY_COMPACT",
     "VERIFY_CAP_ACCEPT", "chain", "decode", "analytic_acceptance", "new_stats", "observe",
-    "ece", "utilisation",
+    "ece", "utilisation", "sts_fit", "ece_of", "calibrate",
 ]
