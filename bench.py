@@ -158,11 +158,15 @@ def measure_observability(dv, dev, inp, spec, B_cap: int, steps: int):
     (dspark_analytic_accept), each timed with HIP events over `steps` calls on
     the chain's stream. The analytic pass's algorithmic bytes are the packed
     target rows once for their log-sum-exps, then the U row and target row of
-    every verified slot, and W2 once per group of rows the GEMM engine holds."""
+    every verified slot, and W2 once per group of rows the GEMM engine holds.
+    Then 32 decode steps of the same chain give a calibration set (the head's
+    logits, soft labels prod c*) for one timed sequential-temperature fit
+    (dspark_sts_fit) over a grid of 31 inverse temperatures."""
     import numpy as np
     import torch
     ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B_cap,
-                  verify_mode=dv.VERIFY_CAP_ACCEPT, observe_bins=16, analytic=True)
+                  verify_mode=dv.VERIFY_CAP_ACCEPT, observe_bins=16, analytic=True,
+                  keep_logits=True)
     ch.run(gather=False)
     torch.cuda.synchronize()
     res = ch.results()
@@ -190,6 +194,32 @@ def measure_observability(dv, dev, inp, spec, B_cap: int, steps: int):
     out["ece_conditional"] = round(summ["ece_conditional"], 4)
     log(f"[bench] observability: analytic c* pass {out['analytic_us']} us "
         f"({out['analytic_gbs']} GB/s), accumulator {out['observe_us']} us")
+
+    # sequential temperature scaling on a calibration set from the decode
+    # loop: the head's logits against soft labels prod c* (analytic acceptance)
+    rec = ch.decode(32, lag=2, record=True)
+    torch.cuda.synchronize()
+    z = torch.from_numpy(np.concatenate([r_["logit"] for r_ in rec])).cuda()
+    y = torch.from_numpy(np.cumprod(np.concatenate([r_["cstar"] for r_ in rec]), axis=1)
+                         .astype(np.float32)).cuda()
+    betas_l = sorted({float(np.float32(0.25 * 1.1 ** i)) for i in range(30)} | {1.0})
+    betas = torch.tensor(betas_l, dtype=torch.float32, device="cuda")
+    dv.sts_fit(z, y, betas)                            # loads the kernels
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    inv, ece = dv.sts_fit(z, y, betas)
+    ev[1].record()
+    torch.cuda.synchronize()
+    inv_l, ece_np = inv.cpu().numpy(), ece.cpu().numpy()
+    j1 = betas_l.index(1.0)
+    picked = [betas_l.index(float(b_)) for b_ in inv_l]
+    out["sts"] = {"samples": int(z.shape[0]), "grid": len(betas_l), "fit_us": round(ev[0].elapsed_time(ev[1]) * 1e3, 1),
+                  "inv_temp": [round(float(b_), 4) for b_ in inv_l],
+                  "ece_beta1": [round(float(ece_np[k, j1]), 4) for k in range(spec.gamma)],
+                  "ece_fit": [round(float(ece_np[k, picked[k]]), 4) for k in range(spec.gamma)],
+                  "labels": "soft: prod of analytic acceptance c* over the prefix"}
+    log(f"[bench] temperature fit over {out['sts']['samples']} samples x {len(betas_l)} candidates: "
+        f"{out['sts']['fit_us']} us; prefix ECE {out['sts']['ece_beta1']} -> {out['sts']['ece_fit']}")
     return out
 
 

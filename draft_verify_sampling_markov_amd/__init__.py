@@ -6,7 +6,7 @@ raises if the library is missing -- there is no fallback path.
 
 Calls (same names as the C ABI in include/dspark.h, without the prefix):
     prepack_w2, markov_draft, confidence, schedule_topb, pack_ragged, verify,
-    advance, observe, analytic_accept, cost_table_prepare, workspace_bytes, markov_logits
+    advance, observe, analytic_accept, sts_fit, cost_table_prepare, workspace_bytes, markov_logits
 and ``Chain``, which holds preallocated buffers for repeated steps.
 """
 from __future__ import annotations
@@ -41,7 +41,7 @@ _SIGNATURES = {
     "dspark_markov_draft": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i, _i, _i,
                                  _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_confidence": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i,
-                               _vp, _vp, _vp]),
+                               _vp, _vp, _vp, _vp]),
     "dspark_schedule_topb": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "dspark_pack_ragged": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
@@ -54,6 +54,8 @@ _SIGNATURES = {
     "dspark_markov_shard_select": (_i, [_vp, _c.c_longlong, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i,
                                         _u64, _u64, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                                         _vp, _i, _vp]),
+    "dspark_sts_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "dspark_sts_fit": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "dspark_observe_words": (_sz, [_i, _i, _i]),
     "dspark_observe": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
     "dspark_analytic_accept": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -229,8 +231,10 @@ def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, st
     return tokens, p, lse
 
 
-def confidence(h, W1, anchor, tokens, w, b: float, inv_temp=None, out=None, stream=None):
-    """h [R, gamma, d]; W1 [V, r]; w [d + r] f32. Returns (conf, surv) f32 [R, gamma]."""
+def confidence(h, W1, anchor, tokens, w, b: float, inv_temp=None, out=None, logit=None,
+               stream=None):
+    """h [R, gamma, d]; W1 [V, r]; w [d + r] f32. Returns (conf, surv) f32 [R, gamma];
+    ``logit`` (f32 [R, gamma], optional) receives the pre-temperature logits."""
     torch = _torch()
     R, gamma, d = h.shape
     V, r = W1.shape
@@ -243,7 +247,8 @@ def confidence(h, W1, anchor, tokens, w, b: float, inv_temp=None, out=None, stre
         _dev(tokens, "tokens", torch.int32, (R, gamma)), _dev(w, "w", torch.float32, (d + r,)),
         float(b), _opt(inv_temp, "inv_temp", torch.float32, (gamma,)), R, gamma, d, V, r,
         _dtype_code(h), _dev(conf, "conf", torch.float32, (R, gamma)),
-        _dev(surv, "surv", torch.float32, (R, gamma)), _stream(stream)))
+        _dev(surv, "surv", torch.float32, (R, gamma)), _opt(logit, "logit", torch.float32, (R, gamma)),
+        _stream(stream)))
     return conf, surv
 
 
@@ -405,6 +410,28 @@ def markov_shard_select(U_k, ldU: int, W1, W2p_g, x_prev, xstride: int, part, su
         _stream(stream)))
 
 
+def sts_fit(z, y, betas, *, n_bins: int = 16, mask=None, stream=None):
+    """Per-position inverse temperatures (dspark_sts_fit). z, y: f32 [N, gamma];
+    betas: f32 [n_grid] device tensor; mask: optional uint8/bool [N, gamma].
+    Returns (inv_temp f32 [gamma], ece f32 [gamma, n_grid])."""
+    torch = _torch()
+    N, gamma = z.shape
+    n_grid = betas.numel()
+    nbytes = int(load_library().dspark_sts_workspace_bytes(N, gamma, n_grid, n_bins))
+    if nbytes == 0:
+        raise DsparkError("unsupported temperature-fit sizes")
+    ws = _empty((nbytes,), torch.uint8, z.device)
+    inv = _empty((gamma,), torch.float32, z.device)
+    ece = _empty((gamma, n_grid), torch.float32, z.device)
+    if mask is not None and mask.dtype == torch.bool:
+        mask = mask.to(torch.uint8)
+    _check(load_library().dspark_sts_fit(
+        _dev(z, "z", torch.float32, (N, gamma)), _dev(y, "y", torch.float32, (N, gamma)),
+        _opt(mask, "mask", torch.uint8, (N, gamma)), N, gamma, _dev(betas, "betas", torch.float32),
+        n_grid, int(n_bins), inv.data_ptr(), ece.data_ptr(), ws.data_ptr(), nbytes, _stream(stream)))
+    return inv, ece
+
+
 def observe_words(R: int, gamma: int, n_bins: int) -> int:
     return int(load_library().dspark_observe_words(R, gamma, n_bins))
 
@@ -495,7 +522,7 @@ __all__ = [
     "prepack_w2", "cost_table_prepare", "markov_draft", "confidence", "schedule_topb",
     "pack_ragged", "verify", "markov_logits", "markov_partials",
     "markov_select", "advance", "observe_words", "new_observe_block", "observe", "parse_observe",
-    "analytic_accept", "markov_shard_partials", "markov_shard_summary", "markov_shard_select", "ShardedDraft", "Chain",
+    "analytic_accept", "sts_fit", "markov_shard_partials", "markov_shard_summary", "markov_shard_select", "ShardedDraft", "Chain",
     "EXPORTS", "F32", "BF16",
     "VERIFY_STATIC", "VERIFY_COMPACT", "VERIFY_CAP_ACCEPT", "SCHED_ARGMAX", "SCHED_GREEDY",
     "SCHED_FIXED", "VERIFY_MODES", "SCHED_MODES",

@@ -35,6 +35,11 @@ class Chain:
     The chain keeps its own copy of the anchors (``self.anchor``), which
     ``decode`` moves on from step to step.
 
+    inv_temp: optional f32 [gamma] device tensor of per-position inverse
+    temperatures for the confidence head (sequential temperature scaling,
+    from sts_fit); keep_logits=True also keeps the head's pre-temperature
+    logits in ``logit_out``.
+
     Optional observability, run after every verify when enabled:
     observe_bins > 0 accumulates dspark_observe counts into ``obs_block``
     (read with ``observe_summary``); analytic=True writes the analytic
@@ -44,7 +49,7 @@ class Chain:
     def __init__(self, inputs: Dict[str, "object"], *, b: float, tiers: Sequence[int],
                  B_cap: int, verify_mode: int, sched_mode: int = SCHED_ARGMAX, K_fixed: int = 0,
                  seed: int = 0, step: int = 0, W2p=None, observe_bins: int = 0,
-                 analytic: bool = False):
+                 analytic: bool = False, inv_temp=None, keep_logits: bool = False):
         import torch
         self.t = torch
         self.inp = inputs
@@ -73,6 +78,8 @@ class Chain:
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
         self.draft_out = (e((R, g), i32), e((R, g), f32), e((R, g), f32))
         self.conf_out = (e((R, g), f32), e((R, g), f32))
+        self.inv_temp = inv_temp
+        self.logit_out = e((R, g), f32) if keep_logits else None
         self.sched_out = (e((R,), i32), e((1,), i32))
         self.pack_out = {"cu_seqlens": e((R + 1,), i32), "packed_tokens": e((self.M_cap,), i32),
                          "packed_req": e((self.M_cap,), i32), "packed_slot": e((self.M_cap,), i32),
@@ -131,7 +138,7 @@ class Chain:
     def confidence(self):
         i = self.inp
         return confidence(i["h"], i["W1"], self.anchor, self.draft_out[0], i["w"], self.b,
-                          out=self.conf_out)
+                          inv_temp=self.inv_temp, out=self.conf_out, logit=self.logit_out)
 
     def schedule(self):
         return schedule_topb(self.conf_out[1], self.inp["sps_milli"], B_cap=self.B_cap,
@@ -204,6 +211,8 @@ class Chain:
                "win_len": s[0], "K": s[1], **self.pack_out, **self.verify_out}
         if self.analytic:
             out["cstar"] = self.cstar
+        if self.logit_out is not None:
+            out["logit"] = self.logit_out
         return {k: v.cpu().numpy() for k, v in out.items()}
 
     # -- decode loop -------------------------------------------------------
@@ -308,6 +317,8 @@ class Chain:
                              **{k: t.clone() for k, t in v.items() if t is not None}})
                 if self.analytic:
                     snap["cstar"] = self.cstar.clone()
+                if self.logit_out is not None:
+                    snap["logit"] = self.logit_out.clone()
                 log.append(snap)
         if not record:
             return None

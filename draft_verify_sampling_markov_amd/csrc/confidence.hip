@@ -65,7 +65,7 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
     const typename Elem<BF16>::T* __restrict__ h, const typename Elem<BF16>::T* __restrict__ W1,
     const int* __restrict__ anchor, const int* __restrict__ tokens, const float* __restrict__ w,
     float b, const float* __restrict__ inv_temp, int gamma, int d, int V, int r, bool vec_h,
-    bool vec_w1, float* __restrict__ conf, float* __restrict__ surv) {
+    bool vec_w1, float* __restrict__ conf, float* __restrict__ surv, float* __restrict__ logit) {
   typedef typename Elem<BF16>::T T;
   __shared__ float cs[kMaxGamma];
   const int req = blockIdx.x;
@@ -75,6 +75,7 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
     const float zh = wave_dot<BF16>(h + ((size_t)req * gamma + (k - 1)) * d, w, d, vec_h, lane);
     const float ze = wave_dot<BF16>(W1 + (size_t)prev * r, w + d, r, vec_w1, lane);
     float z = zh + ze + b;
+    if (logit != nullptr && lane == 0) logit[(size_t)req * gamma + k - 1] = z;
     if (inv_temp) z *= inv_temp[k - 1];
     if (lane == 0) cs[k - 1] = 1.0f / (1.0f + __expf(-z));
   }
@@ -96,7 +97,8 @@ using namespace dspark;
 extern "C" int dspark_confidence(const void* h, const void* W1, const int32_t* anchor,
                                  const int32_t* tokens, const float* w, float b,
                                  const float* inv_temp, int R, int gamma, int d, int V, int r,
-                                 int dtype, float* conf, float* surv, void* stream) {
+                                 int dtype, float* conf, float* surv, float* logit,
+                                 void* stream) {
   int st = check_sizes(R, gamma, V, r, dtype);
   if (st) return st;
   if (d < 1) return DSPARK_ESIZE;
@@ -113,10 +115,10 @@ extern "C" int dspark_confidence(const void* h, const void* W1, const int32_t* a
   if (dtype == DSPARK_BF16)
     hipLaunchKernelGGL(confidence_kernel<true>, dim3(R), block, 0, s,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W1), anchor,
-                       tokens, w, b, inv_temp, gamma, d, V, r, vec_h, vec_w1, conf, surv);
+                       tokens, w, b, inv_temp, gamma, d, V, r, vec_h, vec_w1, conf, surv, logit);
   else
     hipLaunchKernelGGL(confidence_kernel<false>, dim3(R), block, 0, s,
                        static_cast<const float*>(h), static_cast<const float*>(W1), anchor, tokens,
-                       w, b, inv_temp, gamma, d, V, r, vec_h, vec_w1, conf, surv);
+                       w, b, inv_temp, gamma, d, V, r, vec_h, vec_w1, conf, surv, logit);
   return launch_status();
 }

@@ -181,11 +181,15 @@ int dspark_markov_draft(const void* U, const void* W1, const void* W2p, const in
  *   anchor   [R], tokens [R, gamma]
  *   w        [d + r] f32    head weight, hidden part first
  *   b        head bias
- *   inv_temp [gamma] f32 or NULL (NULL: 1; a per-position temperature hook)
- *   conf, surv [R, gamma] f32  out */
+ *   inv_temp [gamma] f32 or NULL (NULL: 1; the per-position inverse
+ *            temperatures of sequential temperature scaling, dspark_sts_fit)
+ *   conf, surv [R, gamma] f32  out
+ *   logit    [R, gamma] f32 out or NULL: the logit before the temperature,
+ *            z = w . [h_k ; W1[x_{k-1}]] + b (the input of dspark_sts_fit) */
 int dspark_confidence(const void* h, const void* W1, const int32_t* anchor, const int32_t* tokens,
                       const float* w, float b, const float* inv_temp, int R, int gamma, int d,
-                      int V, int r, int dtype, float* conf, float* surv, void* stream);
+                      int V, int r, int dtype, float* conf, float* surv, float* logit,
+                      void* stream);
 
 /* Global top-B prefix scheduler ([vllm] "DSpark confidence-scheduling
  * mechanism"; [digest] "Verification scheduling" and "Infra"). Integer fixed
@@ -358,6 +362,38 @@ int dspark_markov_select(const void* U_k, long long ldU, const void* W1, const v
                          uint64_t step, const uint64_t* step_dev, const uint32_t* req_ids, int k,
                          int R, int V, int r, int dtype, int32_t* tok_out, float* p_out,
                          float* lse_out, int ostride, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sequential temperature scaling                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes of dspark_sts_fit (0 for invalid sizes: 1 <= gamma <= 16,
+ * 1 <= n_grid <= 256, 1 <= n_bins <= 32, N * gamma <= 2^31). */
+size_t dspark_sts_workspace_bytes(int N, int gamma, int n_grid, int n_bins);
+
+/* Fit per-position inverse temperatures for the confidence head ([digest]
+ * "Verification scheduling (system side)": sequential temperature scaling
+ * calibrates the running products prod_{i<=k} c_i left to right by a 1-D
+ * grid search minimising ECE). Over N samples (rows of z, y, mask):
+ *   for k = 1..gamma: for every candidate beta_j of betas[n_grid],
+ *     a_k = a_{k-1} * sigmoid(z[n, k-1] * beta_j)  (float32, a_0 = 1, the
+ *           chosen betas of earlier positions fixed);
+ *     ece[k-1, j] = ECE of the pairs (a_k, y[n, k-1]) with mask[n, k-1] != 0
+ *           (mask NULL: every pair), n_bins equal-width bins on [0, 1] (p
+ *           clamped, the top edge in the last bin): sum over bins of
+ *           |sum a - sum y| / pairs, from integer bin sums of floor(p 2^32);
+ *     inv_temp[k-1] = the first beta_j with the smallest ECE.
+ *   z   [N, gamma] f32: the head's logits (dspark_confidence's logit output)
+ *   y   [N, gamma] f32 in [0, 1]: labels for the prefix products, hard (the
+ *       prefix of length k was accepted) or soft (e.g. prod_{i<=k} c*_i from
+ *       dspark_analytic_accept)
+ *   betas [n_grid] f32 > 0, device; inv_temp [gamma] out, ece [gamma, n_grid]
+ *   out (NaN where a position has no pairs); ws: dspark_sts_workspace_bytes.
+ * Pass inv_temp to dspark_confidence to apply the fit. 3 gamma + 1 launches,
+ * no read-back. */
+int dspark_sts_fit(const float* z, const float* y, const uint8_t* mask, int N, int gamma,
+                   const float* betas, int n_grid, int n_bins, float* inv_temp, float* ece,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Vocabulary-sharded draft (per-rank calls)                                 */

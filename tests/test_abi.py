@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -72,8 +72,8 @@ def test_host_validation_rejects_before_launch():
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, p, p, 8, None) == EWS
     assert lib.dspark_markov_draft(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, p, None, 1 << 30, None) == EWS
     # confidence
-    assert lib.dspark_confidence(p, p, p, p, p, 0.0, None, 4, 7, 0, 1024, 32, 0, p, p, None) == ESIZE
-    assert lib.dspark_confidence(p, None, p, p, p, 0.0, None, 4, 7, 64, 1024, 32, 0, p, p, None) == EINVAL
+    assert lib.dspark_confidence(p, p, p, p, p, 0.0, None, 4, 7, 0, 1024, 32, 0, p, p, None, None) == ESIZE
+    assert lib.dspark_confidence(p, None, p, p, p, 0.0, None, 4, 7, 64, 1024, 32, 0, p, p, None, None) == EINVAL
     # schedule
     assert lib.dspark_schedule_topb(p, None, p, 32, 4, 7, 12, 3, 0, p, p, None) == EINVAL
     assert lib.dspark_schedule_topb(p, None, p, 3, 4, 7, 12, 0, 0, p, p, None) == ESIZE
@@ -134,6 +134,13 @@ def test_host_validation_rejects_before_launch():
     assert lib.dspark_markov_shard_select(*bad) == EINVAL
     bad = list(sel); bad[20] = 9                     # dtype
     assert lib.dspark_markov_shard_select(*bad) == EDTYPE
+    # temperature fit: sizes, pointers, workspace
+    assert lib.dspark_sts_workspace_bytes(100, 7, 0, 16) == 0
+    assert lib.dspark_sts_workspace_bytes(100, 7, 16, 33) == 0
+    assert lib.dspark_sts_workspace_bytes(100, 7, 16, 16) >= 100 * 4 + 16 * 16 * 3 * 8
+    assert lib.dspark_sts_fit(p, p, None, 100, 17, p, 16, 16, p, p, p, 1 << 20, None) == ESIZE
+    assert lib.dspark_sts_fit(p, None, None, 100, 7, p, 16, 16, p, p, p, 1 << 20, None) == EINVAL
+    assert lib.dspark_sts_fit(p, p, None, 100, 7, p, 16, 16, p, p, p, 64, None) == EWS
     # prepack
     assert lib.dspark_prepack_w2(p, 32, 1024, 1, p, 10, None) == EWS
     assert lib.dspark_prepack_w2(p, 32, 1024, 3, p, 1 << 30, None) == EDTYPE
