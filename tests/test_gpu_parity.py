@@ -147,6 +147,41 @@ def test_step_and_seed_change_draws(dv):
 
 
 # ---------------------------------------------------------------------------
+# edge cases: degenerate sizes, an empty budget, the row limit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [dict(R=1, gamma=1, V=1, r=1, d=4, dtype="f32"),
+                                   dict(R=1, gamma=16, V=65, r=8, d=8, dtype="bf16"),
+                                   dict(R=3, gamma=2, V=64, r=32, d=16, dtype="bf16")],
+                         ids=["V1-gamma1-r1", "gamma16-V65", "one-tile"])
+def test_degenerate_sizes(dv, shape):
+    # a one-entry vocabulary (every draft is token 0 with probability 1, every
+    # accept test passes), the longest block, exactly one vocabulary tile; each
+    # in every verify mode, with an empty budget and with the full one
+    sp = synth.small_spec("edge", seed=3, **shape)
+    inp = synth.generate(sp)
+    for vmode in ("static", "compact", "cap_accept"):
+        for B in (0, sp.R * sp.gamma):
+            res, _ = run_and_check(dv, sp, vmode, B_cap=B, inp=inp)
+            if B == 0:
+                assert int(res["K"][0]) == 0 and np.all(res["win_len"] == 0)
+            if shape["V"] == 1:
+                assert np.all(res["tokens"] == 0) and np.allclose(res["p_draft"], 1.0)
+
+
+def test_row_limit(dv):
+    # R (gamma + 1) = 4096 packed rows, the documented maximum: 3840 scheduler
+    # keys, the largest pack; a cheap per-token cost so that K is large
+    sp = synth.small_spec("rowlimit", R=256, gamma=15, V=700, r=32, d=16, dtype="bf16", seed=6,
+                          cost=("stair_T", 2e-3, 1e-8, 0.005))
+    inp = synth.generate(sp)
+    res, _ = run_and_check(dv, sp, "static", sample=10, inp=inp)
+    assert int(res["totals"][0]) == 4096
+    res, _ = run_and_check(dv, sp, "compact", sample=10, inp=inp)
+    assert int(res["K"][0]) > 1000
+
+
+# ---------------------------------------------------------------------------
 # the five named workloads at full size
 # ---------------------------------------------------------------------------
 
