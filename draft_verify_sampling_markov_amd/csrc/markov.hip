@@ -200,6 +200,9 @@ __global__ __launch_bounds__(kSelThreads) void markov_select_kernel(
   const int v = t * kTileV + lane;
   const bool valid = v < V;
   const float uo = to_f32(U[(size_t)n * ldU + min(v, V - 1)]);
+  // every load of the tile in flight before the first product (one memory
+  // latency, not one per batch the scheduler would otherwise interleave)
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 acc[4];
   tile_mma_regs<BF16, KC>(at, b, acc);
   const float zo = own_entry(acc, lane) + uo;  // the same sum the GEMM pass formed
@@ -335,6 +338,7 @@ __global__ __launch_bounds__(kSelThreads) void markov_shard_select_kernel(
   const int v = t * kTileV + lane;
   const bool valid = v < Vg;
   const float uo = to_f32(U[(size_t)n * ldU + min(v, Vg - 1)]);
+  __builtin_amdgcn_sched_barrier(0);  // all of the tile's loads before the first product
   f32x4 acc[4];
   tile_mma_regs<BF16, KC>(at, b, acc);
   const float zo = own_entry(acc, lane) + uo;

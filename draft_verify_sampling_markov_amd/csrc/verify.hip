@@ -389,6 +389,7 @@ __global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
   const int vc = min(v, V - 1);
   const float zt = to_f32(target[(size_t)trow * V + vc]);
   const float ud = residual ? to_f32(U[((size_t)n * gamma + dslot) * V + vc]) : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);  // all of the tile's loads before the first product
   f32x4 acc[4];
   tile_mma_regs<BF16, KC>(at, b, acc);
   const float zd = own_entry(acc, lane) + ud;  // the same sum the residual pass formed
