@@ -574,34 +574,21 @@ __device__ __forceinline__ WaveSearch block_tile_search(WFn w, int t0, int cnt, 
                                                         BlockSearchShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   float ls = 0.0f;
-  int last = -1;
   if constexpr (CMAX > 0) {
 #pragma unroll
     for (int i = 0; i < CMAX; ++i)
-      if (i < cnt) {
-        const float wi = w(i);
-        if (wi > 0.0f) last = t0 + i;
-        ls += wi;
-      }
+      if (i < cnt) ls += w(i);
   } else {
-    for (int i = 0; i < cnt; ++i) {
-      const float wi = w(i);
-      if (wi > 0.0f) last = t0 + i;
-      ls += wi;
-    }
+    for (int i = 0; i < cnt; ++i) ls += w(i);
   }
   float incl = wave_inclusive_scan(ls, lane);
-  const int wl = wave_max_int(last);
   if (lane == kWave - 1) sh.wsum[wave] = incl;
-  if (lane == 0) sh.wlast[wave] = wl;
   __syncthreads();
   float off = 0.0f, S = 0.0f;
-  int glast = -1;
 #pragma unroll
   for (int q = 0; q < kSelWaves; ++q) {
     if (q < wave) off += sh.wsum[q];
     S += sh.wsum[q];
-    glast = max(glast, sh.wlast[q]);
   }
   WaveSearch r;
   r.S = S;
@@ -614,41 +601,66 @@ __device__ __forceinline__ WaveSearch block_tile_search(WFn w, int t0, int cnt, 
   int pstar = 0x7fffffff;
 #pragma unroll
   for (int q = 0; q < kSelWaves; ++q) pstar = min(pstar, sh.wfirst[q]);
-  if (pstar == 0x7fffffff) {
-    r.tstar = glast;
-    r.pb = -INFINITY;
-    return r;  // uniform over the workgroup: no barrier follows on this path
-  }
-  if (tid == pstar) {
-    float cum = prev, pbv = -INFINITY;
-    int found = -1;
-    if constexpr (CMAX > 0) {
+  // -1 below: rounding left no crossing (or the crossing thread holds no
+  // positive weight); the result is then the workgroup's last positive tile
+  int tstar = -1;
+  r.pb = -INFINITY;
+  if (pstar != 0x7fffffff) {  // uniform over the workgroup
+    if (tid == pstar) {
+      float cum = prev, pbv = -INFINITY;
+      int found = -1, last = -1;
+      if constexpr (CMAX > 0) {
 #pragma unroll
-      for (int i = 0; i < CMAX; ++i)
-        if (i < cnt) {
-          const float cn = cum + w(i);
-          if (found < 0 && cn > r.T) {
+        for (int i = 0; i < CMAX; ++i)
+          if (i < cnt) {
+            const float wi = w(i);
+            const float cn = cum + wi;
+            if (found < 0 && cn > r.T) {
+              found = t0 + i;
+              pbv = cum;
+            }
+            if (wi > 0.0f) last = t0 + i;
+            cum = cn;
+          }
+      } else {
+        for (int i = 0; i < cnt && found < 0; ++i) {
+          const float wi = w(i);
+          const float cn = cum + wi;
+          if (cn > r.T) {
             found = t0 + i;
             pbv = cum;
           }
+          if (wi > 0.0f) last = t0 + i;
           cum = cn;
         }
-    } else {
-      for (int i = 0; i < cnt && found < 0; ++i) {
-        const float cn = cum + w(i);
-        if (cn > r.T) {
-          found = t0 + i;
-          pbv = cum;
-        }
-        cum = cn;
       }
+      sh.tstar = found >= 0 ? found : last;
+      sh.pb = found >= 0 ? pbv : -INFINITY;
     }
-    sh.tstar = found >= 0 ? found : (last >= 0 ? last : glast);
-    sh.pb = found >= 0 ? pbv : -INFINITY;
+    __syncthreads();
+    tstar = sh.tstar;
+    r.pb = sh.pb;
   }
-  __syncthreads();
-  r.tstar = sh.tstar;
-  r.pb = sh.pb;
+  if (tstar < 0) {  // uniform (read from shared memory, or pstar absent)
+    int last = -1;
+    if constexpr (CMAX > 0) {
+#pragma unroll
+      for (int i = 0; i < CMAX; ++i)
+        if (i < cnt && w(i) > 0.0f) last = t0 + i;
+    } else {
+      for (int i = 0; i < cnt; ++i)
+        if (w(i) > 0.0f) last = t0 + i;
+    }
+    const int wl = wave_max_int(last);
+    if (lane == 0) sh.wlast[wave] = wl;
+    __syncthreads();
+    int glast = -1;
+#pragma unroll
+    for (int q = 0; q < kSelWaves; ++q) glast = max(glast, sh.wlast[q]);
+    tstar = glast;
+    r.pb = -INFINITY;
+  }
+  r.tstar = tstar;
   return r;
 }
 

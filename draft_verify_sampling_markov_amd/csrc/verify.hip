@@ -677,7 +677,13 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
     hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
                        tg, Ub, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,             \
                        out_tokens, ws.queue, queue_groups(R) * kNumXcd)
-  if (c <= 16) {
+  // the partial row in registers, unrolled to the smallest of 8 / 12 / 16
+  // chunks that holds it (masked iterations cost as much as live ones)
+  if (c <= 8) {
+    DSPARK_RES_SELECT(8);
+  } else if (c <= 12) {
+    DSPARK_RES_SELECT(12);
+  } else if (c <= 16) {
     DSPARK_RES_SELECT(16);
   } else {
     DSPARK_RES_SELECT(0);
