@@ -60,7 +60,7 @@ struct SchedShared {
 
 // orig[i] = ((2^20 - a_q) << 32) | i for i = r*gamma + j (a_q the prefix-min
 // quantised survival of request r), padded to NP keys that sort last.
-__device__ void build_keys(const float* __restrict__ a, int R, int gamma, int NP,
+__device__ __forceinline__ void build_keys(const float* __restrict__ a, int R, int gamma, int NP,
                            unsigned long long* keys) {
   const int N = R * gamma;
   for (int req = threadIdx.x; req < R; req += blockDim.x) {
@@ -77,7 +77,7 @@ __device__ void build_keys(const float* __restrict__ a, int R, int gamma, int NP
 }
 
 // In-place exclusive prefix sum of x[0..n) over the workgroup (n <= 8192).
-__device__ void block_exclusive_scan(uint32_t* x, int n, uint32_t* wsum) {
+__device__ __forceinline__ void block_exclusive_scan(uint32_t* x, int n, uint32_t* wsum) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   constexpr int kE = kRadixBuckets * kSchedMaxRows / kSchedThreads;  // 8
   const int e0 = tid * kE;
@@ -106,7 +106,7 @@ __device__ void block_exclusive_scan(uint32_t* x, int n, uint32_t* wsum) {
 // keys: a key's place = keys of smaller digits + keys of its digit in earlier
 // rows (digit-major histogram scan) + earlier keys of its digit in its row
 // (ballot masks).
-__device__ void radix_pass(const unsigned long long* src, unsigned long long* dst, int NR,
+__device__ __forceinline__ void radix_pass(const unsigned long long* src, unsigned long long* dst, int NR,
                            int shift, SchedShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   constexpr int kRowsPerWave = kSchedMaxRows / kSchedWaves;  // 4
@@ -152,7 +152,7 @@ __device__ void radix_pass(const unsigned long long* src, unsigned long long* ds
 }
 
 // Sort orig[0 .. 64 NR) ascending into sh.a (orig is kept).
-__device__ void radix_sort(int NR, SchedShared& sh) {
+__device__ __forceinline__ void radix_sort(int NR, SchedShared& sh) {
   radix_pass(sh.orig, sh.a, NR, 0, sh);
   radix_pass(sh.a, sh.b, NR, kRadixBits, sh);
   radix_pass(sh.b, sh.a, NR, 2 * kRadixBits, sh);

@@ -1,10 +1,11 @@
 """Static checks on the gfx950 code objects inside libdspark.so (no GPU needed).
 
-Two properties that cost microseconds per launch when they slip:
+Three properties that cost microseconds per launch when they slip:
 - no kernel enables the dispatch-packet pointer (the packet lives in host
   memory; the compiler reaches for it when it moves a small private array into
   LDS and needs the workgroup size to address it);
-- the hot-path kernels use no scratch (private segment) memory.
+- the hot-path kernels use no scratch (private segment) memory;
+- no kernel calls a device function (every helper is inlined).
 
 The library is built here, so this reads our own build output. Each
 translation unit contributes one offload bundle to the .hip_fatbin section.
@@ -62,26 +63,37 @@ def _kernel_descriptors(co, readelf):
     return out
 
 
-def _descriptors():
+def _unbundle(d):
+    """The gfx950 code object of every translation unit, written into d."""
     if not os.path.exists(dv.LIB_PATH):
         pytest.skip("libdspark.so not built")
-    objcopy, bundler, readelf = _tool("llvm-objcopy"), _tool("clang-offload-bundler"), _tool("llvm-readelf")
-    if not (objcopy and bundler and readelf):
+    objcopy, bundler = _tool("llvm-objcopy"), _tool("clang-offload-bundler")
+    if not (objcopy and bundler):
+        pytest.skip("LLVM tools not available")
+    fat = os.path.join(d, "fatbin")
+    subprocess.run([objcopy, "--dump-section", f".hip_fatbin={fat}", dv.LIB_PATH,
+                    os.path.join(d, "copy.so")], check=True, capture_output=True)
+    blob = open(fat, "rb").read()
+    starts = [m.start() for m in re.finditer(re.escape(BUNDLE_MAGIC), blob)]
+    cos = []
+    for n, st in enumerate(starts):
+        end = starts[n + 1] if n + 1 < len(starts) else len(blob)
+        part, co = os.path.join(d, f"b{n}"), os.path.join(d, f"b{n}.co")
+        with open(part, "wb") as fh:
+            fh.write(blob[st:end])
+        subprocess.run([bundler, "--type=o", f"--targets={TARGET}", f"--input={part}",
+                        f"--output={co}", "--unbundle"], check=True, capture_output=True)
+        cos.append(co)
+    return cos
+
+
+def _descriptors():
+    readelf = _tool("llvm-readelf")
+    if not readelf:
         pytest.skip("LLVM tools not available")
     out = {}
     with tempfile.TemporaryDirectory() as d:
-        fat = os.path.join(d, "fatbin")
-        subprocess.run([objcopy, "--dump-section", f".hip_fatbin={fat}", dv.LIB_PATH,
-                        os.path.join(d, "copy.so")], check=True, capture_output=True)
-        blob = open(fat, "rb").read()
-        starts = [m.start() for m in re.finditer(re.escape(BUNDLE_MAGIC), blob)]
-        for n, st in enumerate(starts):
-            end = starts[n + 1] if n + 1 < len(starts) else len(blob)
-            part, co = os.path.join(d, f"b{n}"), os.path.join(d, f"b{n}.co")
-            with open(part, "wb") as fh:
-                fh.write(blob[st:end])
-            subprocess.run([bundler, "--type=o", f"--targets={TARGET}", f"--input={part}",
-                            f"--output={co}", "--unbundle"], check=True, capture_output=True)
+        for co in _unbundle(d):
             out.update(_kernel_descriptors(co, readelf))
     assert out, "no kernel descriptors found"
     return out
@@ -105,3 +117,19 @@ def test_vector_path_hot_kernels_use_no_scratch():
     bad = [k for k, v in desc.items()
            if v["private"] and any(h in k for h in HOT) and not re.search(r"Lb0EEEv", k)]
     assert not bad, f"hot kernels with scratch: {bad}"
+
+
+def test_no_kernel_calls_a_device_function():
+    # a device function that is not inlined becomes a call (s_swappc) with its
+    # own stack frame: a single-workgroup kernel that called its sort pass
+    # that way ran several times slower
+    objdump = _tool("llvm-objdump")
+    if not objdump:
+        pytest.skip("llvm-objdump not available")
+    with tempfile.TemporaryDirectory() as d:
+        calls = 0
+        for co in _unbundle(d):
+            text = subprocess.run([objdump, "-d", co], check=True, capture_output=True,
+                                  text=True).stdout
+            calls += len(re.findall(r"\bs_swappc_b64\b", text))
+    assert calls == 0, f"{calls} device-function calls in the code objects"
