@@ -42,6 +42,9 @@ _SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_confidence": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _vp, _vp]),
+    "dspark_markov_draft_confidence": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i,
+                                            _i, _i, _vp, _vp, _f, _vp, _i, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _sz, _vp]),
     "dspark_schedule_topb": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "dspark_pack_ragged": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
@@ -229,6 +232,42 @@ def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, st
         _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
         _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
     return tokens, p, lse
+
+
+def markov_draft_confidence(U, W1, W2p, anchor, h, w, b: float, *, r: int, inv_temp=None,
+                            seed: int = 0, step: int = 0, step_dev=None, req_ids=None, out=None,
+                            conf_out=None, logit=None, ws=None, stream=None):
+    """markov_draft and confidence in one call (each slot's GEMM launch also
+    scores the slot). h [R, gamma, d]; w [d + r] f32. Returns (tokens, p_draft,
+    lse_draft, conf, surv)."""
+    torch = _torch()
+    R, gamma, V = U.shape
+    d = h.shape[2]
+    dev = U.device
+    if req_ids is None:
+        req_ids = torch.arange(R, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (_empty((R, gamma), torch.int32, dev), _empty((R, gamma), torch.float32, dev),
+               _empty((R, gamma), torch.float32, dev))
+    if conf_out is None:
+        conf_out = (_empty((R, gamma), torch.float32, dev), _empty((R, gamma), torch.float32, dev))
+    if ws is None:
+        ws = new_workspace(CALL_MARKOV_DRAFT, R, gamma, V, r, dev, stream)
+    tokens, p, lse = out
+    conf, surv = conf_out
+    _check(load_library().dspark_markov_draft_confidence(
+        _dev(U, "U"), _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
+        _dev(anchor, "anchor", torch.int32, (R,)), seed, step,
+        _opt(step_dev, "step_dev", torch.int64, (1,)), _dev(req_ids, "req_ids", None, (R,)),
+        R, gamma, V, r, _dtype_code(U), _dev(h, "h", U.dtype, (R, gamma, d)),
+        _dev(w, "w", torch.float32, (d + r,)), float(b),
+        _opt(inv_temp, "inv_temp", torch.float32, (gamma,)), d,
+        _dev(tokens, "tokens", torch.int32, (R, gamma)),
+        _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
+        _dev(conf, "conf", torch.float32, (R, gamma)), _dev(surv, "surv", torch.float32, (R, gamma)),
+        _opt(logit, "logit", torch.float32, (R, gamma)),
+        _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return tokens, p, lse, conf, surv
 
 
 def confidence(h, W1, anchor, tokens, w, b: float, inv_temp=None, out=None, logit=None,

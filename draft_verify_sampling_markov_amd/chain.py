@@ -1,8 +1,9 @@
 """Decode steps of the DSpark chain over preallocated device buffers.
 
-draft (dspark_markov_draft) -> confidence (dspark_confidence) -> schedule
-(dspark_schedule_topb) -> pack (dspark_pack_ragged) -> [target forward] ->
-verify (dspark_verify), all enqueued on one stream with no host read-back.
+draft and confidence (dspark_markov_draft_confidence, or dspark_markov_draft
+then dspark_confidence) -> schedule (dspark_schedule_topb) -> pack
+(dspark_pack_ragged) -> [target forward] -> verify (dspark_verify), all
+enqueued on one stream with no host read-back.
 ``decode`` repeats the step, carrying x_0, the Philox step and a short
 survival history from one step to the next on the device (dspark_advance), so
 that the verify budget can come from confidences ``lag`` steps old (DSpark
@@ -20,7 +21,8 @@ from __future__ import annotations
 
 from typing import Dict, Optional, Sequence
 
-from . import (markov_draft, markov_partials, markov_select, confidence, schedule_topb,
+from . import (markov_draft, markov_draft_confidence, markov_partials, markov_select, confidence,
+               schedule_topb,
                pack_ragged, verify, advance, observe, new_observe_block, parse_observe,
                analytic_accept, prepack_w2, new_workspace, CALL_MARKOV_DRAFT, CALL_VERIFY,
                CALL_ANALYTIC_ACCEPT, VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX, SCHED_GREEDY)
@@ -104,6 +106,16 @@ class Chain:
         return markov_draft(i["U"], i["W1"], self.W2p, self.anchor, r=self.r, seed=self.seed,
                             step=self.step, req_ids=i["req_ids"], out=self.draft_out,
                             ws=self.ws_draft)
+
+    def draft_confidence(self, step_dev=None):
+        """The draft and the confidence head in one call (dspark_markov_draft_
+        confidence): each slot's GEMM launch also scores the slot."""
+        i = self.inp
+        markov_draft_confidence(i["U"], i["W1"], self.W2p, self.anchor, i["h"], i["w"], self.b,
+                                r=self.r, inv_temp=self.inv_temp, seed=self.seed,
+                                step=self.step, step_dev=step_dev, req_ids=i["req_ids"],
+                                out=self.draft_out, conf_out=self.conf_out, logit=self.logit_out,
+                                ws=self.ws_draft)
 
     def draft_split(self, events=None, passes=("partials", "select")):
         """The draft as its two per-slot passes, through the split calls: the
@@ -195,8 +207,7 @@ class Chain:
     def run(self, gather: bool = True):
         """One whole step; ``gather`` re-runs the target stand-in between pack
         and verify (needed whenever the windows may have changed)."""
-        self.draft()
-        self.confidence()
+        self.draft_confidence()
         self.schedule()
         self.pack()
         if gather:
@@ -221,9 +232,7 @@ class Chain:
         and verify read the Philox step from ``step_dev``; dspark_advance then
         moves x_0, the step and the survival history on."""
         i, d = self.inp, self.draft_out
-        markov_draft(i["U"], i["W1"], self.W2p, self.anchor, r=self.r, seed=self.seed,
-                     step_dev=self.step_dev, req_ids=i["req_ids"], out=d, ws=self.ws_draft)
-        self.confidence()
+        self.draft_confidence(step_dev=self.step_dev)
         schedule_topb(self.conf_out[1], i["sps_milli"], B_cap=self.B_cap, mode=mode,
                       K_fixed=self.K_fixed, surv_budget=budget, out=self.sched_out)
         self.pack()

@@ -11,54 +11,13 @@
 //
 // One workgroup per request, one wave per slot: two dot products with 16-byte
 // loads (the hidden state, then the gathered W1 row), a fixed-order wave sum,
-// and a float32 running product over the slots in order.
+// and a float32 running product over the slots in order. The draft's GEMM
+// pass can score its slot with the same wave code (conf_logit), which gives the
+// same values.
 #include "dspark_device.hpp"
 #include "dspark_host.hpp"
 
 namespace dspark {
-
-// Dot product of `len` stored elements with float weights, by one wave: 16-byte
-// loads when `vec` (len a multiple of the vector width, rows aligned), all of a
-// lane's loads issued before the sums.
-template <bool BF16>
-__device__ __forceinline__ float wave_dot(const typename Elem<BF16>::T* __restrict__ x,
-                                          const float* __restrict__ w, int len, bool vec, int lane) {
-  constexpr int VEC = Elem<BF16>::kVec;
-  float acc = 0.0f;
-  if (vec) {
-    const int nv = len / VEC;
-    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    constexpr int U = 4;
-    for (int base = 0; base < nv; base += U * kWave) {
-      u32x4 q[U];
-#pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const int c = base + i * kWave + lane;
-        q[i] = c < nv ? xv[c] : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const int c = base + i * kWave + lane;
-        if (c < nv) {
-          const float* wc = w + c * VEC;
-          if constexpr (BF16) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc += __uint_as_float(q[i][e] << 16) * wc[2 * e];
-              acc += __uint_as_float(q[i][e] & 0xFFFF0000u) * wc[2 * e + 1];
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc += __uint_as_float(q[i][e]) * wc[e];
-          }
-        }
-      }
-    }
-  } else {
-    for (int i = lane; i < len; i += kWave) acc += to_f32(x[i]) * w[i];
-  }
-  return wave_sum(acc);
-}
 
 template <bool BF16>
 __global__ __launch_bounds__(1024) void confidence_kernel(
@@ -72,9 +31,8 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
   const int lane = threadIdx.x & (kWave - 1), k = 1 + threadIdx.x / kWave;  // one wave per slot
   if (k <= gamma) {
     const int prev = clamp_token(k == 1 ? anchor[req] : tokens[(size_t)req * gamma + k - 2], V);
-    const float zh = wave_dot<BF16>(h + ((size_t)req * gamma + (k - 1)) * d, w, d, vec_h, lane);
-    const float ze = wave_dot<BF16>(W1 + (size_t)prev * r, w + d, r, vec_w1, lane);
-    float z = zh + ze + b;
+    float z = conf_logit<BF16>(h + ((size_t)req * gamma + (k - 1)) * d, W1 + (size_t)prev * r, w,
+                               b, d, r, vec_h, vec_w1, lane);
     if (logit != nullptr && lane == 0) logit[(size_t)req * gamma + k - 1] = z;
     if (inv_temp) z *= inv_temp[k - 1];
     if (lane == 0) cs[k - 1] = 1.0f / (1.0f + __expf(-z));
@@ -94,6 +52,17 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
 
 using namespace dspark;
 
+void dspark::confidence_vec_flags(const void* h, const void* W1, const float* w, int d, int r,
+                                  int dtype, bool& vec_h, bool& vec_w1) {
+  const int vec = dtype == DSPARK_BF16 ? 8 : 4;
+  const bool al_h = (reinterpret_cast<uintptr_t>(h) % 16) == 0;
+  const bool al_w1 = (reinterpret_cast<uintptr_t>(W1) % 16) == 0;
+  const bool al_w = (reinterpret_cast<uintptr_t>(w) % 16) == 0;
+  // the weight is read in vector-width groups starting at 0 and at d
+  vec_h = al_h && al_w && d % vec == 0;
+  vec_w1 = al_w1 && al_w && r % vec == 0 && (d * 4) % 16 == 0;
+}
+
 extern "C" int dspark_confidence(const void* h, const void* W1, const int32_t* anchor,
                                  const int32_t* tokens, const float* w, float b,
                                  const float* inv_temp, int R, int gamma, int d, int V, int r,
@@ -104,13 +73,8 @@ extern "C" int dspark_confidence(const void* h, const void* W1, const int32_t* a
   if (d < 1) return DSPARK_ESIZE;
   if (!h || !W1 || !anchor || !tokens || !w || !conf || !surv) return DSPARK_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int vec = dtype == DSPARK_BF16 ? 8 : 4;
-  const bool al_h = (reinterpret_cast<uintptr_t>(h) % 16) == 0;
-  const bool al_w1 = (reinterpret_cast<uintptr_t>(W1) % 16) == 0;
-  const bool al_w = (reinterpret_cast<uintptr_t>(w) % 16) == 0;
-  // the weight is read in vector-width groups starting at 0 and at d
-  const bool vec_h = al_h && al_w && d % vec == 0;
-  const bool vec_w1 = al_w1 && al_w && r % vec == 0 && (d * 4) % 16 == 0;
+  bool vec_h, vec_w1;
+  confidence_vec_flags(h, W1, w, d, r, dtype, vec_h, vec_w1);
   const dim3 block(gamma * kWave);
   if (dtype == DSPARK_BF16)
     hipLaunchKernelGGL(confidence_kernel<true>, dim3(R), block, 0, s,

@@ -377,6 +377,75 @@ __device__ __forceinline__ void wave_argmax_u64(unsigned long long& th, int& k) 
   k = __builtin_amdgcn_readlane(k, kWave - 1);
 }
 
+// Dot product of `len` stored elements with float weights, by one wave: 16-byte
+// loads when `vec` (len a multiple of the vector width, rows aligned), all of a
+// lane's loads issued before the sums.
+template <bool BF16>
+__device__ __forceinline__ float wave_dot(const typename Elem<BF16>::T* __restrict__ x,
+                                          const float* __restrict__ w, int len, bool vec, int lane) {
+  constexpr int VEC = Elem<BF16>::kVec;
+  float acc = 0.0f;
+  if (vec) {
+    const int nv = len / VEC;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    constexpr int U = 4;
+    for (int base = 0; base < nv; base += U * kWave) {
+      u32x4 q[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int c = base + i * kWave + lane;
+        q[i] = c < nv ? xv[c] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int c = base + i * kWave + lane;
+        if (c < nv) {
+          const float* wc = w + c * VEC;
+          if constexpr (BF16) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc += __uint_as_float(q[i][e] << 16) * wc[2 * e];
+              acc += __uint_as_float(q[i][e] & 0xFFFF0000u) * wc[2 * e + 1];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc += __uint_as_float(q[i][e]) * wc[e];
+          }
+        }
+      }
+    }
+  } else {
+    for (int i = lane; i < len; i += kWave) acc += to_f32(x[i]) * w[i];
+  }
+  return wave_sum(acc);
+}
+
+// The confidence head's logit for one slot, by one wave: w . [h_k ; W1[x_{k-1}]] + b
+// (the hidden-state dot, then the W1-row dot, each a fixed-order wave sum).
+template <bool BF16>
+__device__ __forceinline__ float conf_logit(const typename Elem<BF16>::T* __restrict__ h_row,
+                                            const typename Elem<BF16>::T* __restrict__ w1_row,
+                                            const float* __restrict__ w, float b, int d, int r,
+                                            bool vec_h, bool vec_w1, int lane) {
+  const float zh = wave_dot<BF16>(h_row, w, d, vec_h, lane);
+  const float ze = wave_dot<BF16>(w1_row, w + d, r, vec_w1, lane);
+  return zh + ze + b;
+}
+
+// Inputs of the confidence head for a draft call that also scores its slots
+// (h == nullptr: it does not). Layouts as dspark_confidence's.
+struct ConfArgs {
+  const void* h;          // [R, gamma, d] hidden states, storage type
+  const float* w;         // [d + r]
+  float b;
+  const float* inv_temp;  // [gamma] or nullptr
+  int d;
+  bool vec_h, vec_w1;     // 16-byte loads allowed (alignment and lengths checked on the host)
+  float* conf;            // [R, gamma]
+  float* surv;            // [R, gamma]
+  float* logit;           // [R, gamma] or nullptr
+};
+
 // Merge two (max, sum of exp(z - max)) softmax partials.
 __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
   const float mm = fmaxf(m, m2);

@@ -73,6 +73,10 @@ inline int check_sizes(int R, int gamma, int V, int r, int dt) {
 
 // Workspace layout pieces (bytes, 256-aligned).
 size_t markov_ws_bytes(int R, int V);
+// 16-byte load flags of the confidence head's two dot products (alignment and
+// lengths of h, the W1 rows and the weight vector)
+void confidence_vec_flags(const void* h, const void* W1, const float* w, int d, int r, int dtype,
+                          bool& vec_h, bool& vec_w1);
 size_t verify_ws_bytes(int R, int gamma, int V);
 size_t accept_ws_bytes(int R, int gamma, int V);
 

@@ -91,6 +91,10 @@ struct MarkovEpi {
   int ldn, c;
   float2* junk;
   DrawArgs draw;
+  ConfArgs ca;     // ca.h == nullptr: the slot is not scored here
+  const T* W1;     // for the head's W1-row dot product
+  const int* xprev;
+  int xstride, r, gamma;
 
   __device__ __forceinline__ St prepare(int n) const {
     St s;
@@ -99,11 +103,34 @@ struct MarkovEpi {
     s.row = U + (size_t)min(n, R - 1) * ldU;
     return s;
   }
-  // called once per workgroup in the engine's prologue
+  // called once per workgroup in the engine's prologue, with the first
+  // tiles' loads in flight: the slot's draft uniforms, then (optional) the
+  // confidence head for the slot (digest, "Verification scheduling"):
+  // c_k = sigmoid(z inv_temp_k), z = w . [h_k ; W1[x_{k-1}]] + b, and the
+  // survival a_k = a_{k-1} c_k, a_{k-1} from the previous slot's launch. One
+  // wave per request (workgroup b, wave j: requests b + G (j + waves i)), with
+  // the wave code of the confidence kernel, so the values are the same.
   __device__ __forceinline__ void side_work() const {
     const int q = (int)blockIdx.x * kWave + (int)threadIdx.x;
     if (draw.u_out != nullptr && threadIdx.x < kWave && q < R)
       draw.u_out[q] = slot_uniform(draw.seed, draw.step.get(), draw.req_ids[q], draw.k, kPurposeDraft);
+    if (ca.h == nullptr) return;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int waves = blockDim.x / kWave, k = draw.k;
+    for (int n = blockIdx.x + gridDim.x * wave; n < R; n += gridDim.x * waves) {  // wave-uniform
+      const size_t o = (size_t)n * gamma + (k - 1);
+      const int x = clamp_token(xprev[(size_t)n * xstride], V);
+      float z = conf_logit<BF16>(static_cast<const T*>(ca.h) + o * ca.d, W1 + (size_t)x * r, ca.w,
+                                 ca.b, ca.d, r, ca.vec_h, ca.vec_w1, lane);
+      if (lane == 0) {
+        if (ca.logit != nullptr) ca.logit[o] = z;
+        if (ca.inv_temp != nullptr) z *= ca.inv_temp[k - 1];
+        const float cf = 1.0f / (1.0f + __expf(-z));
+        const float a_prev = k == 1 ? 1.0f : ca.surv[o - 1];
+        ca.conf[o] = cf;
+        ca.surv[o] = a_prev * cf;
+      }
+    }
   }
   __device__ __forceinline__ void load(const St& s, int v0, int nvalid, Pre& p) const {
     load16_clamped<BF16, VEC>(s.row, v0, nvalid, V, p);
@@ -126,8 +153,9 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t, int w1_rows,
     float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk,
-    unsigned* __restrict__ queue, DrawArgs draw) {
-  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk, draw};
+    unsigned* __restrict__ queue, DrawArgs draw, ConfArgs ca, int gamma) {
+  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk, draw, ca, W1, xprev, xstride,
+                                 r, gamma};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
                                          R, V, r, n_t, epi, queue, w1_rows);
 }
@@ -435,7 +463,7 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                                const int32_t* xprev, int xstride, int Rg, int V, int r,
                                int w1_rows, float2* part, float2* junk, unsigned* queue,
-                               DrawArgs draw, hipStream_t s) {
+                               DrawArgs draw, const ConfArgs& ca, int gamma, hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
   const int per_cu = NW == 4 ? 2 : 1;
@@ -444,11 +472,11 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
                        G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, w1_rows,
-                       part, ldn, c, junk, queue, draw);
+                       part, ldn, c, junk, queue, draw, ca, gamma);
   else
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
                        dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
-                       n_t, w1_rows, part, ldn, c, junk, queue, draw);
+                       n_t, w1_rows, part, ldn, c, junk, queue, draw, ca, gamma);
   return launch_status();
 }
 
@@ -458,7 +486,8 @@ template <bool BF16, int KC>
 static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                            const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                            const int32_t* xprev, int xstride, int R, int V, int r, int w1_rows,
-                           float2* part, DrawArgs draw, hipStream_t s) {
+                           float2* part, DrawArgs draw, const ConfArgs& ca, int gamma,
+                           hipStream_t s) {
   float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
   unsigned* queue = markov_queue(part, R, V);
   const int ldn = part_ld(V);
@@ -474,13 +503,20 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
       dg.u_out += g0;
       dg.req_ids += g0;
     }
+    ConfArgs cg = ca;  // the group's rows of h and of the [R, gamma] outputs
+    if (cg.h != nullptr) {
+      cg.h = static_cast<const typename Elem<BF16>::T*>(cg.h) + (size_t)g0 * gamma * cg.d;
+      cg.conf += (size_t)g0 * gamma;
+      cg.surv += (size_t)g0 * gamma;
+      if (cg.logit != nullptr) cg.logit += (size_t)g0 * gamma;
+    }
     int st;
     if (blocks <= 4)
-      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, s);
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
     else if (blocks <= 8)
-      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
     else if constexpr (BF16)
-      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, s);
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
     else
       st = DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
     if (st) return st;
@@ -555,7 +591,7 @@ template <bool BF16, int KC>
 static int launch_markov(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
                          uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                          int V, int r, int32_t* tokens, float* p_draft, float* lse_draft,
-                         float2* part, hipStream_t s) {
+                         float2* part, const ConfArgs& ca, hipStream_t s) {
   typedef typename Elem<BF16>::T T;
   const T* Ub = static_cast<const T*>(U);
   const T* W1b = static_cast<const T*>(W1);
@@ -568,7 +604,7 @@ static int launch_markov(const void* U, const void* W1, const void* W2p, const i
     const T* Uk = Ub + (size_t)(k - 1) * V;
     const DrawArgs draw{seed, step, req_ids, k, markov_u(part, R, V)};
     int st = launch_partials<BF16, KC>(Uk, ldU, vec_u && vec_w1, W1b, W2b, xprev, xstride, R, V, r,
-                                       V, part, draw, s);
+                                       V, part, draw, ca, gamma, s);
     if (st) return st;
     st = launch_select<BF16, KC>(Uk, ldU, vec_u, vec_w1, W1b, W2b, xprev, xstride, R, V, r, part,
                                  seed, step, req_ids, k, tokens + (k - 1), p_draft + (k - 1),
@@ -587,7 +623,7 @@ static int launch_partials_api(const void* U, long long ldU, const void* W1, con
   const DrawArgs none{0, StepArg{0, nullptr}, nullptr, 0, nullptr};
   return launch_partials<BF16, KC>(static_cast<const T*>(U), ldU, vec, static_cast<const T*>(W1),
                                    static_cast<const T*>(W2p), x_prev, xstride, R, V, r, w1_rows,
-                                   part, none, s);
+                                   part, none, ConfArgs{}, 1, s);
 }
 
 template <bool BF16, int KC>
@@ -645,15 +681,15 @@ extern "C" int dspark_prepack_w2(const void* W2, int r, int V, int dtype, void* 
 static int markov_dispatch(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
                            uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                            int V, int r, int dtype, int32_t* tokens, float* p, float* lse,
-                           float2* part, hipStream_t s) {
+                           float2* part, const ConfArgs& ca, hipStream_t s) {
   if (dtype == DSPARK_BF16) {
     DSPARK_KC_DISPATCH(true, launch_markov, U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V,
-                       r, tokens, p, lse, part, s)
+                       r, tokens, p, lse, part, ca, s)
   }
   switch (kc_instance(r)) {
-    case 1: return launch_markov<false, 1>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, s);
-    case 2: return launch_markov<false, 2>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, s);
-    default: return launch_markov<false, 4>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, s);
+    case 1: return launch_markov<false, 1>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, ca, s);
+    case 2: return launch_markov<false, 2>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, ca, s);
+    default: return launch_markov<false, 4>(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens, p, lse, part, ca, s);
   }
 }
 
@@ -669,6 +705,34 @@ extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2
   if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
   return markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
                          r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws),
+                         ConfArgs{}, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int dspark_markov_draft_confidence(
+    const void* U, const void* W1, const void* W2p, const int32_t* anchor, uint64_t seed,
+    uint64_t step, const uint64_t* step_dev, const uint32_t* req_ids, int R, int gamma, int V,
+    int r, int dtype, const void* h, const float* w, float b, const float* inv_temp, int d,
+    int32_t* tokens, float* p_draft, float* lse_draft, float* conf, float* surv, float* logit,
+    void* ws, size_t ws_bytes, void* stream) {
+  int st = check_sizes(R, gamma, V, r, dtype);
+  if (st) return st;
+  if (d < 1) return DSPARK_ESIZE;
+  if (!U || !W1 || !W2p || !anchor || !req_ids || !tokens || !p_draft || !lse_draft || !h || !w ||
+      !conf || !surv)
+    return DSPARK_EINVAL;
+  if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
+  ConfArgs ca;
+  ca.h = h;
+  ca.w = w;
+  ca.b = b;
+  ca.inv_temp = inv_temp;
+  ca.d = d;
+  confidence_vec_flags(h, W1, w, d, r, dtype, ca.vec_h, ca.vec_w1);
+  ca.conf = conf;
+  ca.surv = surv;
+  ca.logit = logit;
+  return markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
+                         r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws), ca,
                          static_cast<hipStream_t>(stream));
 }
 

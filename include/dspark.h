@@ -6,6 +6,7 @@
  *
  *   dspark_markov_draft   draft a gamma-token block with the Markov head
  *   dspark_confidence     confidence c_k and prefix survival a_{r,j}
+ *                         (dspark_markov_draft_confidence: both in one call)
  *   dspark_schedule_topb  global top-B prefix selection (verify windows)
  *   dspark_pack_ragged    cu_seqlens packing rounded up to a capture tier
  *   dspark_verify         lossless rejection-sampling verification
@@ -190,6 +191,23 @@ int dspark_confidence(const void* h, const void* W1, const int32_t* anchor, cons
                       const float* w, float b, const float* inv_temp, int R, int gamma, int d,
                       int V, int r, int dtype, float* conf, float* surv, float* logit,
                       void* stream);
+
+/* dspark_markov_draft and dspark_confidence in one call ([sglang] "Performance
+ * optimisation and zero-overhead scheduling": the drafter's sampling path is
+ * fused). The head for slot k needs only x_{k-1}, which slot k's GEMM pass
+ * already reads, so that launch also scores the slot: in its prologue, with
+ * its first tiles' loads in flight, one wave per request runs the head's two
+ * dot products and the survival product. Arguments as in the two calls; the
+ * outputs equal theirs bit for bit (same wave code, same order). Errors:
+ * those of both calls. */
+int dspark_markov_draft_confidence(const void* U, const void* W1, const void* W2p,
+                                   const int32_t* anchor, uint64_t seed, uint64_t step,
+                                   const uint64_t* step_dev, const uint32_t* req_ids, int R,
+                                   int gamma, int V, int r, int dtype, const void* h,
+                                   const float* w, float b, const float* inv_temp, int d,
+                                   int32_t* tokens, float* p_draft, float* lse_draft, float* conf,
+                                   float* surv, float* logit, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Global top-B prefix scheduler ([vllm] "DSpark confidence-scheduling
  * mechanism"; [digest] "Verification scheduling" and "Infra"). Integer fixed

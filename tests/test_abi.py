@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -74,6 +74,14 @@ def test_host_validation_rejects_before_launch():
     # confidence
     assert lib.dspark_confidence(p, p, p, p, p, 0.0, None, 4, 7, 0, 1024, 32, 0, p, p, None, None) == ESIZE
     assert lib.dspark_confidence(p, None, p, p, p, 0.0, None, 4, 7, 64, 1024, 32, 0, p, p, None, None) == EINVAL
+    # draft + confidence in one call: the checks of both
+    dc = lib.dspark_markov_draft_confidence
+    assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 5, p, p, 0.0, None, 64, p, p, p, p, p, None, p, 1 << 30, None) == EDTYPE
+    assert dc(p, p, p, p, 0, 0, None, p, 4, 17, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, p, None, p, 1 << 30, None) == ESIZE
+    assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 0, p, p, p, p, p, None, p, 1 << 30, None) == ESIZE
+    assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, None, p, 0.0, None, 64, p, p, p, p, p, None, p, 1 << 30, None) == EINVAL
+    assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, None, None, p, 1 << 30, None) == EINVAL
+    assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, p, None, p, 8, None) == EWS
     # schedule
     assert lib.dspark_schedule_topb(p, None, p, 32, 4, 7, 12, 3, 0, p, p, None) == EINVAL
     assert lib.dspark_schedule_topb(p, None, p, 3, 4, 7, 12, 0, 0, p, p, None) == ESIZE
