@@ -708,6 +708,19 @@ extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2
                          ConfArgs{}, static_cast<hipStream_t>(stream));
 }
 
+// The confidence head rides in the GEMM prologue (one wave per request, in
+// workgroups 0 .. R-1) when at most a quarter of the GEMM's workgroups carry a
+// request, so that the queue hands their share of tiles to the others; with
+// more requests every workgroup would start late and the head runs as a
+// launch of its own after the draft (the same values either way).
+static bool conf_in_prologue(int R, int V, bool bf16) {
+  const int group = bf16 ? req_group<true>() : req_group<false>();
+  if (R > group) return false;
+  const int nw = ceil_div(R, kTileN) <= 4 ? 4 : 8;
+  const int grid = std::max(1, std::min(n_vtiles(V), device_cu_count() * (nw == 4 ? 2 : 1)));
+  return 4 * R <= grid;
+}
+
 extern "C" int dspark_markov_draft_confidence(
     const void* U, const void* W1, const void* W2p, const int32_t* anchor, uint64_t seed,
     uint64_t step, const uint64_t* step_dev, const uint32_t* req_ids, int R, int gamma, int V,
@@ -721,6 +734,16 @@ extern "C" int dspark_markov_draft_confidence(
       !conf || !surv)
     return DSPARK_EINVAL;
   if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!conf_in_prologue(R, V, dtype == DSPARK_BF16)) {
+    // every GEMM workgroup would carry a request: the head as a launch of its own
+    st = markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
+                         r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws),
+                         ConfArgs{}, s);
+    if (st) return st;
+    return dspark_confidence(h, W1, anchor, tokens, w, b, inv_temp, R, gamma, d, V, r, dtype, conf,
+                             surv, logit, stream);
+  }
   ConfArgs ca;
   ca.h = h;
   ca.w = w;
@@ -732,8 +755,7 @@ extern "C" int dspark_markov_draft_confidence(
   ca.surv = surv;
   ca.logit = logit;
   return markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
-                         r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws), ca,
-                         static_cast<hipStream_t>(stream));
+                         r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws), ca, s);
 }
 
 static int logits_dispatch(const void* U, long long ldU, const void* W1, const void* W2p,

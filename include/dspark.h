@@ -197,9 +197,11 @@ int dspark_confidence(const void* h, const void* W1, const int32_t* anchor, cons
  * fused). The head for slot k needs only x_{k-1}, which slot k's GEMM pass
  * already reads, so that launch also scores the slot: in its prologue, with
  * its first tiles' loads in flight, one wave per request runs the head's two
- * dot products and the survival product. Arguments as in the two calls; the
- * outputs equal theirs bit for bit (same wave code, same order). Errors:
- * those of both calls. */
+ * dot products and the survival product. That is done when at most a quarter
+ * of the GEMM's workgroups carry a request (e.g. 64 requests on an MI355X);
+ * with more requests the head runs as one launch after the draft. Arguments
+ * as in the two calls; the outputs equal theirs bit for bit either way (same
+ * wave code, same order). Errors: those of both calls. */
 int dspark_markov_draft_confidence(const void* U, const void* W1, const void* W2p,
                                    const int32_t* anchor, uint64_t seed, uint64_t step,
                                    const uint64_t* step_dev, const uint32_t* req_ids, int R,

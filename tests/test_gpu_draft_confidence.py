@@ -8,7 +8,10 @@ probabilities and log-normalisers, confidences, survivals and logits. The oracle
 fused call is covered by the chain parity tests, whose steps use it.
 Shapes: a single request and slot, ragged request counts and vocabularies,
 bfloat16 and float32, hidden sizes and ranks that are not multiples of the
-vector width (scalar dot products), inverse temperatures on and off.
+vector width (scalar dot products), inverse temperatures on and off; both
+placements of the head (in the GEMM prologue when few of the GEMM's
+workgroups carry a request, e.g. 64 requests over a 151936 vocabulary; a launch
+of its own after the draft otherwise, e.g. 256 requests).
 """
 import numpy as np
 import pytest
@@ -31,7 +34,8 @@ def dv():
 # (R, gamma, V, r, d, dtype, temperatures)
 SHAPES = [(1, 1, 65, 32, 16, "bf16", False), (7, 5, 3000, 64, 96, "bf16", True),
           (33, 4, 2950, 96, 100, "bf16", True), (20, 6, 1000, 36, 48, "f32", False),
-          (64, 7, 151936, 256, 2560, "bf16", True), (5, 16, 517, 100, 37, "f32", True)]
+          (64, 7, 151936, 256, 2560, "bf16", True), (5, 16, 517, 100, 37, "f32", True),
+          (40, 3, 151936, 64, 200, "f32", True), (256, 2, 129280, 256, 512, "bf16", False)]
 
 
 @pytest.mark.parametrize("R,gamma,V,r,d,dtype,temps", SHAPES)
