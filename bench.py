@@ -374,18 +374,18 @@ def main() -> int:
         step_graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    graph_ms = wall * 1e3 / args.steps
+    graph_step_ms = wall * 1e3 / args.steps
     # the step's throughput is its faster launch mechanism on this host: the
     # same work either way (both runs time exactly K whole steps)
-    use_graph = graph_ms <= eager_ms
-    ms_per_step = graph_ms if use_graph else eager_ms
+    use_graph = graph_step_ms <= eager_ms
+    ms_per_step = graph_step_ms if use_graph else eager_ms
     after = ch.results()
     for key in ("win_len", "cu_seqlens", "totals", "tokens", "p_draft", "accept_len", "out_tokens"):
         if not np.array_equal(first[key], after[key]):
             log(f"[bench] {key} changed between steps: the pre-laid target rows are stale")
             return 1
     value = slots_per_step / (ms_per_step * 1e-3)
-    log(f"[bench] {args.steps} steps: graph replays {graph_ms:.4f} ms/step, eager launches "
+    log(f"[bench] {args.steps} steps: graph replays {graph_step_ms:.4f} ms/step, eager launches "
         f"{eager_ms:.4f} ms/step -> {ms_per_step:.4f} ms/step")
 
     # ---- per-kernel / per-stage event timing on the chain's stream ----
@@ -503,7 +503,7 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "step_timing": ("replays of one captured HIP graph of the whole step" if use_graph else
                         "eager launches of the whole step (faster than graph replays on this host)"),
-        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_ms_per_step": round(graph_step_ms, 4),
         "eager_ms_per_step": round(eager_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": spec.dtype, "data": "synthetic",

@@ -458,6 +458,14 @@ static bool u_vec_ok(const void* U, long long ldU, int V) {
   return rows_vec_ok(U, ldU, V, Elem<BF16>::kVec);
 }
 
+// Engine shape of a GEMM launch over Rg requests: waves per workgroup (4 up to
+// four 16-request blocks, else 8) and the grid (two 4-wave or one 8-wave
+// workgroup per CU, at most one per vocabulary tile).
+static int partials_waves(int Rg) { return ceil_div(Rg, kTileN) <= 4 ? 4 : 8; }
+static int partials_grid(int nw, int V) {
+  return std::max(1, std::min(n_vtiles(V), device_cu_count() * (nw == 4 ? 2 : 1)));
+}
+
 template <bool BF16, int KC, int NW, int NB>
 static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
@@ -466,8 +474,7 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
                                DrawArgs draw, const ConfArgs& ca, int gamma, hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
-  const int per_cu = NW == 4 ? 2 : 1;
-  const int grid = std::max(1, std::min(n_t, device_cu_count() * per_cu));
+  const int grid = partials_grid(NW, V);
   const int ldn = part_ld(V), c = part_chunk(V);
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
@@ -511,7 +518,7 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
       if (cg.logit != nullptr) cg.logit += (size_t)g0 * gamma;
     }
     int st;
-    if (blocks <= 4)
+    if (partials_waves(Rg) == 4)
       st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
     else if (blocks <= 8)
       st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
@@ -716,9 +723,7 @@ extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2
 static bool conf_in_prologue(int R, int V, bool bf16) {
   const int group = bf16 ? req_group<true>() : req_group<false>();
   if (R > group) return false;
-  const int nw = ceil_div(R, kTileN) <= 4 ? 4 : 8;
-  const int grid = std::max(1, std::min(n_vtiles(V), device_cu_count() * (nw == 4 ? 2 : 1)));
-  return 4 * R <= grid;
+  return 4 * R <= partials_grid(partials_waves(R), V);
 }
 
 extern "C" int dspark_markov_draft_confidence(
