@@ -5,8 +5,9 @@ kernels. PyTorch supplies device memory and the current stream. The binding
 raises if the library is missing -- there is no fallback path.
 
 Calls (same names as the C ABI in include/dspark.h, without the prefix):
-    prepack_w2, markov_draft, confidence, schedule_topb, pack_ragged, verify,
-    advance, observe, analytic_accept, sts_fit, cost_table_prepare, workspace_bytes, markov_logits
+    prepack_w2, markov_draft, confidence, markov_draft_confidence, schedule_topb, pack_ragged,
+    schedule_pack, verify, advance, observe, analytic_accept, sts_fit, cost_table_prepare,
+    workspace_bytes, markov_logits
 and ``Chain``, which holds preallocated buffers for repeated steps.
 """
 from __future__ import annotations
@@ -48,6 +49,8 @@ _SIGNATURES = {
     "dspark_schedule_topb": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "dspark_pack_ragged": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
+    "dspark_schedule_pack": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i,
+                                  _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "dspark_verify": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _u64,
                            _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_advance": (_i, [_vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _vp]),
@@ -306,6 +309,40 @@ def schedule_topb(surv, sps_milli, *, B_cap: int, mode: int, K_fixed: int = 0, s
         _dev(sps_milli, "sps_milli"), M_max, R, gamma, int(B_cap), int(mode), int(K_fixed),
         _dev(win, "win_len", torch.int32, (R,)), _dev(K, "K_out", torch.int32, (1,)), _stream(stream)))
     return win, K
+
+
+def schedule_pack(surv, sps_milli, anchor, tokens, tiers: Sequence[int], M_cap: int, *,
+                  B_cap: int, mode: int, K_fixed: int = 0, surv_budget=None,
+                  pack_windows: bool = True, sched_out=None, pack_out=None, stream=None):
+    """schedule_topb then pack_ragged in one launch. pack_windows=False packs
+    full blocks (as pack_ragged with win_len None). Returns ((win_len, K),
+    pack dict)."""
+    torch = _torch()
+    R, gamma = surv.shape
+    M_max = sps_milli.numel() - 1
+    dev = surv.device
+    if sched_out is None:
+        sched_out = (_empty((R,), torch.int32, dev), _empty((1,), torch.int32, dev))
+    if pack_out is None:
+        pack_out = {"cu_seqlens": _empty((R + 1,), torch.int32, dev),
+                    "packed_tokens": _empty((M_cap,), torch.int32, dev),
+                    "packed_req": _empty((M_cap,), torch.int32, dev),
+                    "packed_slot": _empty((M_cap,), torch.int32, dev),
+                    "totals": _empty((2,), torch.int32, dev)}
+    win, K = sched_out
+    tr = np.ascontiguousarray(tiers, dtype=np.int32)
+    _check(load_library().dspark_schedule_pack(
+        _dev(surv, "surv", torch.float32), _opt(surv_budget, "surv_budget", torch.float32, (R, gamma)),
+        _dev(sps_milli, "sps_milli"), M_max, R, gamma, int(B_cap), int(mode), int(K_fixed),
+        _dev(win, "win_len", torch.int32, (R,)), _dev(K, "K_out", torch.int32, (1,)),
+        _dev(anchor, "anchor", torch.int32, (R,)), _dev(tokens, "tokens", torch.int32, (R, gamma)),
+        1 if pack_windows else 0, tr.ctypes.data, tr.shape[0], M_cap,
+        _dev(pack_out["cu_seqlens"], "cu_seqlens", torch.int32, (R + 1,)),
+        _dev(pack_out["packed_tokens"], "packed_tokens", torch.int32),
+        _dev(pack_out["packed_req"], "packed_req", torch.int32),
+        _dev(pack_out["packed_slot"], "packed_slot", torch.int32),
+        _dev(pack_out["totals"], "totals", torch.int32, (2,)), _stream(stream)))
+    return sched_out, pack_out
 
 
 def pack_ragged(anchor, tokens, win_len, tiers: Sequence[int], M_cap: int, out=None, stream=None):

@@ -1,9 +1,9 @@
 """Decode steps of the DSpark chain over preallocated device buffers.
 
 draft and confidence (dspark_markov_draft_confidence, or dspark_markov_draft
-then dspark_confidence) -> schedule (dspark_schedule_topb) -> pack
-(dspark_pack_ragged) -> [target forward] -> verify (dspark_verify), all
-enqueued on one stream with no host read-back.
+then dspark_confidence) -> schedule and pack (dspark_schedule_pack, or
+dspark_schedule_topb then dspark_pack_ragged) -> [target forward] -> verify
+(dspark_verify), all enqueued on one stream with no host read-back.
 ``decode`` repeats the step, carrying x_0, the Philox step and a short
 survival history from one step to the next on the device (dspark_advance), so
 that the verify budget can come from confidences ``lag`` steps old (DSpark
@@ -22,7 +22,7 @@ from __future__ import annotations
 from typing import Dict, Optional, Sequence
 
 from . import (markov_draft, markov_draft_confidence, markov_partials, markov_select, confidence,
-               schedule_topb,
+               schedule_topb, schedule_pack,
                pack_ragged, verify, advance, observe, new_observe_block, parse_observe,
                analytic_accept, prepack_w2, new_workspace, CALL_MARKOV_DRAFT, CALL_VERIFY,
                CALL_ANALYTIC_ACCEPT, VERIFY_STATIC, VERIFY_CAP_ACCEPT, SCHED_ARGMAX, SCHED_GREEDY)
@@ -156,6 +156,14 @@ class Chain:
         return schedule_topb(self.conf_out[1], self.inp["sps_milli"], B_cap=self.B_cap,
                              mode=self.sched_mode, K_fixed=self.K_fixed, out=self.sched_out)
 
+    def schedule_and_pack(self, mode=None, budget=None):
+        """The scheduler and the pack in one launch (dspark_schedule_pack)."""
+        schedule_pack(self.conf_out[1], self.inp["sps_milli"], self.anchor, self.draft_out[0],
+                      self.tiers, self.M_cap, B_cap=self.B_cap,
+                      mode=self.sched_mode if mode is None else mode, K_fixed=self.K_fixed,
+                      surv_budget=budget, pack_windows=not self.full_block,
+                      sched_out=self.sched_out, pack_out=self.pack_out)
+
     def pack(self):
         win = None if self.full_block else self.sched_out[0]
         return pack_ragged(self.anchor, self.draft_out[0], win, self.tiers, self.M_cap,
@@ -208,8 +216,7 @@ class Chain:
         """One whole step; ``gather`` re-runs the target stand-in between pack
         and verify (needed whenever the windows may have changed)."""
         self.draft_confidence()
-        self.schedule()
-        self.pack()
+        self.schedule_and_pack()
         if gather:
             self.gather_target()
         self.verify()
@@ -233,9 +240,7 @@ class Chain:
         moves x_0, the step and the survival history on."""
         i, d = self.inp, self.draft_out
         self.draft_confidence(step_dev=self.step_dev)
-        schedule_topb(self.conf_out[1], i["sps_milli"], B_cap=self.B_cap, mode=mode,
-                      K_fixed=self.K_fixed, surv_budget=budget, out=self.sched_out)
-        self.pack()
+        self.schedule_and_pack(mode=mode, budget=budget)
         if not self.full_block:
             self.gather_target()
         verify(self.target_packed, self.pack_out["cu_seqlens"], self.anchor, d[0], d[1], d[2],

@@ -158,11 +158,13 @@ __device__ __forceinline__ void radix_sort(int NR, SchedShared& sh) {
   radix_pass(sh.b, sh.a, NR, 2 * kRadixBits, sh);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
+// The scheduler's work for one workgroup of kSchedThreads threads. win_s
+// (nullable, shared memory): also receives the windows, for a pack that
+// follows in the same launch.
+__device__ __forceinline__ void schedule_body(
     const float* __restrict__ surv, const float* __restrict__ surv_budget,
     const uint32_t* __restrict__ sps, int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
-    int* __restrict__ win_len, int* __restrict__ K_out) {
-  __shared__ SchedShared sh;
+    int* __restrict__ win_len, int* __restrict__ K_out, SchedShared& sh, int* win_s) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int N = R * gamma;
   const int NR = (N + kWave - 1) / kWave;
@@ -250,8 +252,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     int cnt = 0;
     for (int j = 0; j < gamma; ++j) cnt += sh.orig[r * gamma + j] < thr;
     win_len[r] = cnt;
+    if (win_s != nullptr) win_s[r] = cnt;
   }
   if (tid == 0) K_out[0] = K;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
+    const float* __restrict__ surv, const float* __restrict__ surv_budget,
+    const uint32_t* __restrict__ sps, int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
+    int* __restrict__ win_len, int* __restrict__ K_out) {
+  __shared__ SchedShared sh;
+  schedule_body(surv, surv_budget, sps, M_max, R, gamma, B_cap, mode, K_fixed, win_len, K_out, sh,
+                nullptr);
 }
 
 struct TierList {
@@ -259,13 +271,20 @@ struct TierList {
   int v[kMaxTiers];
 };
 
-__global__ __launch_bounds__(1024) void pack_kernel(
-    const int* __restrict__ anchor, const int* __restrict__ tokens, const int* __restrict__ win_len,
-    int R, int gamma, TierList tiers, int M_cap, int* __restrict__ cu_seqlens,
+struct PackShared {
+  int cu[kMaxRows / 2 + 1];
+  int wtot[1024 / kWave];
+};
+
+// The pack's work for one workgroup of 1024 threads. win_len (nullable: every
+// window is gamma) may point to global or shared memory.
+__device__ __forceinline__ void pack_body(
+    const int* __restrict__ anchor, const int* __restrict__ tokens, const int* win_len,
+    int R, int gamma, const TierList& tiers, int M_cap, int* __restrict__ cu_seqlens,
     int* __restrict__ ptok, int* __restrict__ preq, int* __restrict__ pslot,
-    int* __restrict__ totals) {
-  __shared__ int cu[kMaxRows / 2 + 1];
-  __shared__ int wtot[1024 / kWave];
+    int* __restrict__ totals, PackShared& ps) {
+  int* cu = ps.cu;
+  int* wtot = ps.wtot;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   // requests 2*tid, 2*tid + 1 (R <= 2048)
   int len[2] = {0, 0};
@@ -327,6 +346,36 @@ __global__ __launch_bounds__(1024) void pack_kernel(
   }
 }
 
+__global__ __launch_bounds__(1024) void pack_kernel(
+    const int* __restrict__ anchor, const int* __restrict__ tokens, const int* __restrict__ win_len,
+    int R, int gamma, TierList tiers, int M_cap, int* __restrict__ cu_seqlens,
+    int* __restrict__ ptok, int* __restrict__ preq, int* __restrict__ pslot,
+    int* __restrict__ totals) {
+  __shared__ PackShared ps;
+  pack_body(anchor, tokens, win_len, R, gamma, tiers, M_cap, cu_seqlens, ptok, preq, pslot, totals,
+            ps);
+}
+
+// Schedule, then pack, in one workgroup: the windows pass through shared
+// memory. pack_windows == 0: the pack keeps every window at gamma (the static
+// and cap-accept blocks), as a pack call with win_len NULL.
+__global__ __launch_bounds__(kSchedThreads) void schedule_pack_kernel(
+    const float* __restrict__ surv, const float* __restrict__ surv_budget,
+    const uint32_t* __restrict__ sps, int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
+    int* __restrict__ win_len, int* __restrict__ K_out, const int* __restrict__ anchor,
+    const int* __restrict__ tokens, int pack_windows, TierList tiers, int M_cap,
+    int* __restrict__ cu_seqlens, int* __restrict__ ptok, int* __restrict__ preq,
+    int* __restrict__ pslot, int* __restrict__ totals) {
+  __shared__ SchedShared sh;
+  __shared__ PackShared ps;
+  __shared__ int win_s[kMaxRows / 2];
+  schedule_body(surv, surv_budget, sps, M_max, R, gamma, B_cap, mode, K_fixed, win_len, K_out, sh,
+                win_s);
+  __syncthreads();
+  pack_body(anchor, tokens, pack_windows ? win_s : nullptr, R, gamma, tiers, M_cap, cu_seqlens,
+            ptok, preq, pslot, totals, ps);
+}
+
 }  // namespace dspark
 
 using namespace dspark;
@@ -372,6 +421,35 @@ extern "C" int dspark_pack_ragged(const int32_t* anchor, const int32_t* tokens,
   for (int i = 0; i < kMaxTiers; ++i) tl.v[i] = i < n_tiers ? tiers[i] : 0;
   hipLaunchKernelGGL(pack_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), anchor,
                      tokens, win_len, R, gamma, tl, M_cap, cu_seqlens, packed_tokens, packed_req,
+                     packed_slot, totals);
+  return launch_status();
+}
+
+extern "C" int dspark_schedule_pack(const float* surv, const float* surv_budget,
+                                    const uint32_t* sps_milli, int M_max, int R, int gamma,
+                                    int B_cap, int mode, int K_fixed, int32_t* win_len,
+                                    int32_t* K_out, const int32_t* anchor, const int32_t* tokens,
+                                    int pack_windows, const int32_t* tiers, int n_tiers, int M_cap,
+                                    int32_t* cu_seqlens, int32_t* packed_tokens,
+                                    int32_t* packed_req, int32_t* packed_slot, int32_t* totals,
+                                    void* stream) {
+  if (!surv || !sps_milli || !win_len || !K_out) return DSPARK_EINVAL;
+  if (!anchor || !tokens || !cu_seqlens || !packed_tokens || !packed_req || !packed_slot || !totals)
+    return DSPARK_EINVAL;
+  if (mode < DSPARK_SCHED_ARGMAX || mode > DSPARK_SCHED_FIXED) return DSPARK_EINVAL;
+  if (R < 1 || gamma < 1 || gamma > kMaxGamma) return DSPARK_ESIZE;
+  if ((long long)R * (gamma + 1) > kMaxRows) return DSPARK_ESIZE;
+  if (M_max < R || M_max > kMaxRows) return DSPARK_ESIZE;
+  if (M_cap < R * (gamma + 1)) return DSPARK_ESIZE;
+  int st = check_tiers(tiers, n_tiers);
+  if (st) return st;
+  TierList tl;
+  tl.n = n_tiers;
+  for (int i = 0; i < kMaxTiers; ++i) tl.v[i] = i < n_tiers ? tiers[i] : 0;
+  hipLaunchKernelGGL(schedule_pack_kernel, dim3(1), dim3(kSchedThreads), 0,
+                     static_cast<hipStream_t>(stream), surv, surv_budget, sps_milli, M_max, R,
+                     gamma, B_cap, mode, K_fixed, win_len, K_out, anchor, tokens,
+                     pack_windows ? 1 : 0, tl, M_cap, cu_seqlens, packed_tokens, packed_req,
                      packed_slot, totals);
   return launch_status();
 }

@@ -9,6 +9,7 @@
  *                         (dspark_markov_draft_confidence: both in one call)
  *   dspark_schedule_topb  global top-B prefix selection (verify windows)
  *   dspark_pack_ragged    cu_seqlens packing rounded up to a capture tier
+ *                         (dspark_schedule_pack: schedule and pack in one launch)
  *   dspark_verify         lossless rejection-sampling verification
  *
  * a sixth, dspark_advance, that carries a decode loop from one step to the
@@ -249,6 +250,21 @@ int dspark_pack_ragged(const int32_t* anchor, const int32_t* tokens, const int32
                        int R, int gamma, const int32_t* tiers, int n_tiers, int M_cap,
                        int32_t* cu_seqlens, int32_t* packed_tokens, int32_t* packed_req,
                        int32_t* packed_slot, int32_t* totals, void* stream);
+
+/* dspark_schedule_topb then dspark_pack_ragged in one launch (one workgroup;
+ * the windows pass to the pack through shared memory). Arguments as in the two
+ * calls. pack_windows != 0 packs the scheduled windows (compact verify);
+ * pack_windows == 0 packs every window at gamma, as dspark_pack_ragged with
+ * win_len NULL (static and cap-accept verify), while win_len and K_out still
+ * receive the schedule. The outputs equal the two calls'. Errors: those of
+ * both calls. */
+int dspark_schedule_pack(const float* surv, const float* surv_budget, const uint32_t* sps_milli,
+                         int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
+                         int32_t* win_len, int32_t* K_out, const int32_t* anchor,
+                         const int32_t* tokens, int pack_windows, const int32_t* tiers,
+                         int n_tiers, int M_cap, int32_t* cu_seqlens, int32_t* packed_tokens,
+                         int32_t* packed_req, int32_t* packed_slot, int32_t* totals,
+                         void* stream);
 
 /* Rejection-sampling verification ([digest] summary and "Architecture": the
  * longest conforming prefix is accepted by rejection sampling, lossless

@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
@@ -82,6 +82,15 @@ def test_host_validation_rejects_before_launch():
     assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, None, p, 0.0, None, 64, p, p, p, p, p, None, p, 1 << 30, None) == EINVAL
     assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, None, None, p, 1 << 30, None) == EINVAL
     assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, p, None, p, 8, None) == EWS
+    # schedule + pack in one launch: the checks of both
+    sp = lib.dspark_schedule_pack
+    tiers = (ctypes.c_int32 * 2)(16, 32)
+    bad_tiers = (ctypes.c_int32 * 2)(32, 16)
+    assert sp(p, None, p, 32, 4, 7, 12, 3, 0, p, p, p, p, 1, tiers, 2, 32, p, p, p, p, p, None) == EINVAL
+    assert sp(p, None, p, 32, 4, 7, 12, 0, 0, p, p, None, p, 1, tiers, 2, 32, p, p, p, p, p, None) == EINVAL
+    assert sp(p, None, p, 32, 4, 7, 12, 0, 0, p, p, p, p, 1, tiers, 2, 31, p, p, p, p, p, None) == ESIZE
+    assert sp(p, None, p, 3, 4, 7, 12, 0, 0, p, p, p, p, 1, tiers, 2, 32, p, p, p, p, p, None) == ESIZE
+    assert sp(p, None, p, 32, 4, 7, 12, 0, 0, p, p, p, p, 1, bad_tiers, 2, 32, p, p, p, p, p, None) == ETIER
     # schedule
     assert lib.dspark_schedule_topb(p, None, p, 32, 4, 7, 12, 3, 0, p, p, None) == EINVAL
     assert lib.dspark_schedule_topb(p, None, p, 3, 4, 7, 12, 0, 0, p, p, None) == ESIZE

@@ -30,7 +30,7 @@ HOT = ("markov_partials_kernel", "markov_select_kernel", "residual_partials_kern
        "schedule_kernel", "pack_kernel", "advance_kernel", "accept_jobs_kernel",
        "accept_partials_kernel", "accept_reduce_kernel", "observe_kernel",
        "markov_shard_summary_kernel", "markov_shard_select_kernel", "sts_curve_kernel",
-       "sts_pick_kernel", "sts_advance_kernel")
+       "sts_pick_kernel", "sts_advance_kernel", "schedule_pack_kernel")
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
 

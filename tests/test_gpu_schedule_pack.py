@@ -1,0 +1,73 @@
+"""dspark_schedule_pack against dspark_schedule_topb followed by
+dspark_pack_ragged, through the C ABI.
+
+The fused launch runs the same scheduler and pack code in one workgroup, with
+the windows passed through shared memory, so every output must be identical:
+windows, K, cu_seqlens, packed tokens / requests / slots and the totals. The
+oracle parity of the fused call is covered by the chain parity tests, whose
+steps use it. Cases: the three scheduler modes, a stale budget array, full
+blocks (pack_windows off) and scheduled windows, an empty budget, the row
+limit R (gamma + 1) = 4096, and a total that exceeds every tier.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dv():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_verify_sampling_markov_amd as dv
+    dv.load_library()
+    return dv
+
+
+def _case(dv, R, gamma, V, B, mode, K_fixed, stale, windows, tiers, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    c = rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
+    surv = torch.from_numpy(np.cumprod(c, axis=1)).cuda()
+    budget = torch.from_numpy(np.cumprod(rng.uniform(0.3, 1.0, (R, gamma)), axis=1)
+                              .astype(np.float32)).cuda() if stale else None
+    M_max = R * (gamma + 1)
+    raw = 1e-3 + 4e-6 * np.arange(M_max + 1, dtype=np.float64)
+    sps = torch.from_numpy(dv.cost_table_prepare(raw, tiers, True).astype(np.int32)).cuda()
+    anchor = torch.from_numpy(rng.integers(0, V, R).astype(np.int32)).cuda()
+    tokens = torch.from_numpy(rng.integers(0, V, (R, gamma)).astype(np.int32)).cuda()
+    M_cap = M_max
+    win_a, K_a = dv.schedule_topb(surv, sps, B_cap=B, mode=mode, K_fixed=K_fixed, surv_budget=budget)
+    pack_a = dv.pack_ragged(anchor, tokens, win_a if windows else None, tiers, M_cap)
+    (win_b, K_b), pack_b = dv.schedule_pack(surv, sps, anchor, tokens, tiers, M_cap, B_cap=B,
+                                            mode=mode, K_fixed=K_fixed, surv_budget=budget,
+                                            pack_windows=windows)
+    torch.cuda.synchronize()
+    assert np.array_equal(win_a.cpu().numpy(), win_b.cpu().numpy())
+    assert int(K_a.item()) == int(K_b.item())
+    for k in pack_a:
+        assert np.array_equal(pack_a[k].cpu().numpy(), pack_b[k].cpu().numpy()), k
+    return int(K_b.item()), pack_b["totals"].cpu().numpy()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("windows", [True, False])
+def test_fused_equals_two_calls(dv, mode, windows):
+    tiers = [8, 16, 32, 64, 128, 256, 512]
+    for R, gamma, B, stale, seed in [(64, 7, 448, False, 1), (64, 7, 100, True, 2),
+                                     (13, 16, 50, False, 3), (1, 1, 1, False, 4),
+                                     (64, 7, 0, False, 5)]:
+        K, tot = _case(dv, R, gamma, 1000, B, mode, 37, stale, windows, tiers, seed)
+        log(f"[sched+pack] mode={mode} windows={windows} R={R} gamma={gamma} B={B}: K={K} "
+            f"totals={tot.tolist()}")
+
+
+def test_row_limit_and_tier_overflow(dv):
+    # R (gamma + 1) = 4096 packed rows; tiers that stop below the full block
+    K, tot = _case(dv, 256, 15, 5000, 3840, 0, 0, False, True, [512, 1024, 2048, 4096], 7)
+    assert tot[0] <= 4096
+    K, tot = _case(dv, 256, 15, 5000, 3840, 0, 0, False, False, [512, 1024, 2048], 8)
+    assert tot.tolist() == [4096, -1]
