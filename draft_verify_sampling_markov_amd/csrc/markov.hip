@@ -550,10 +550,13 @@ static int launch_select(const typename Elem<BF16>::T* Uk, long long ldU, bool v
     hipLaunchKernelGGL((markov_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
                        Uk, ldU, W1, W2p, xprev, xstride, V, r, n_t, part, ldn, c, seed,           \
                        step, req_ids, k, tok, p, lse, ostride, queue, n_queue, u_pre)
-  // the partial row in registers, unrolled to the smallest of 8 / 12 / 16
-  // chunks that holds it (masked iterations cost as much as live ones)
+  // the partial row in registers, unrolled to the smallest of 8 / 10 / 12 /
+  // 16 chunks that holds it (masked iterations cost as much as live ones;
+  // 8 and 10 chunks are vocabularies up to 131072 and 163840)
   if (c <= 8) {
     DSPARK_SELECT(8);
+  } else if (c <= 10) {
+    DSPARK_SELECT(10);
   } else if (c <= 12) {
     DSPARK_SELECT(12);
   } else if (c <= 16) {

@@ -677,10 +677,13 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
     hipLaunchKernelGGL((residual_select_kernel<BF16, KC, CM, false>), dim3(R), dim3(kSelThreads), 0, s, \
                        tg, Ub, W1b, W2b, ws.jobs, gamma, V, r, n_t, ws.rpart, ldn, c,             \
                        out_tokens, ws.queue, queue_groups(R) * kNumXcd)
-  // the partial row in registers, unrolled to the smallest of 8 / 12 / 16
-  // chunks that holds it (masked iterations cost as much as live ones)
+  // the partial row in registers, unrolled to the smallest of 8 / 10 / 12 /
+  // 16 chunks that holds it (masked iterations cost as much as live ones;
+  // 8 and 10 chunks are vocabularies up to 131072 and 163840)
   if (c <= 8) {
     DSPARK_RES_SELECT(8);
+  } else if (c <= 10) {
+    DSPARK_RES_SELECT(10);
   } else if (c <= 12) {
     DSPARK_RES_SELECT(12);
   } else if (c <= 16) {
