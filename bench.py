@@ -313,8 +313,8 @@ def main() -> int:
                          "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the chain has no multi-GPU path).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the chain has no "
+              f"multi-GPU path (its sharding is a design only).", file=sys.stderr)
         return 2
 
     import numpy as np
