@@ -6,7 +6,7 @@ other words with the round key), and a Weyl increment of the key between rounds.
 
 The method samples its drafts left to right and verifies them by rejection
 sampling (DSpark digest, "Architecture (drafter)"; the stream is keyed by
-(seed, request, position)). Counter layout used by this build:
+(seed, request, position)). Counter layout used here:
 
     counter = (k, req_id, step, 0)      k = slot 1..gamma+1 within the block
     key     = (seed, 0)

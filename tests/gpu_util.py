@@ -1,7 +1,7 @@
 """Helpers for GPU parity tests: device upload of synth inputs, the tolerance
 rules, and stage-by-stage comparison of the HIP chain against the oracle.
 
-Tolerances (the benchmark spec, restated in the design doc):
+Tolerances:
   * ids, lengths, selection and packing: bit-exact;
   * probabilities, log-sum-exps, confidences, survivals: 1e-5 absolute;
   * an accept/reject decision may differ only where |u - p_t/p_d| < 1e-5;
