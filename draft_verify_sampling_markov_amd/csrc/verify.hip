@@ -52,9 +52,14 @@ struct Jobs {
 // row partials
 // ---------------------------------------------------------------------------
 
-template <bool BF16>
+// Every load of the chunk is issued before the first value is used: addresses
+// are clamped into the chunk and out-of-range values replaced afterwards (a
+// branch around a load would make the compiler wait for it before the next
+// one goes out). On the vector path V and the chunk bounds are multiples of
+// the vector width, so a vector lies wholly inside or wholly outside.
+template <bool BF16, bool VECP>
 __global__ __launch_bounds__(kRowThreads) void row_partials_kernel(
-    const typename Elem<BF16>::T* __restrict__ target, int V, bool vec, int n_chunks,
+    const typename Elem<BF16>::T* __restrict__ target, int V, int n_chunks,
     const int* __restrict__ cu_seqlens, int R, int rows_ws, float2* __restrict__ part) {
   typedef typename Elem<BF16>::T T;
   constexpr int VEC = Elem<BF16>::kVec;
@@ -68,33 +73,34 @@ __global__ __launch_bounds__(kRowThreads) void row_partials_kernel(
   const T* z = target + (size_t)row * V;
   const int tid = threadIdx.x;
   float vals[PER];
-  if (vec) {
+  if constexpr (VECP) {
+    u32x4 q[PER / VEC];
 #pragma unroll
     for (int it = 0; it < PER / VEC; ++it) {
       const int v = v_begin + (it * kRowThreads + tid) * VEC;
-      if (v + VEC <= v_end) {
-        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + v));
-        if constexpr (BF16) {
+      q[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + min(v, v_end - VEC)));
+    }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vals[it * VEC + 2 * i] = __uint_as_float(q[i] << 16);
-            vals[it * VEC + 2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
-          }
-        } else {
+    for (int it = 0; it < PER / VEC; ++it) {
+      const bool ok = v_begin + (it * kRowThreads + tid) * VEC < v_end;
+      if constexpr (BF16) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vals[it * VEC + i] = __uint_as_float(q[i]);
+        for (int i = 0; i < 4; ++i) {
+          vals[it * VEC + 2 * i] = ok ? __uint_as_float(q[it][i] << 16) : -INFINITY;
+          vals[it * VEC + 2 * i + 1] = ok ? __uint_as_float(q[it][i] & 0xFFFF0000u) : -INFINITY;
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) vals[it * VEC + i] = (v + i < v_end) ? to_f32(z[v + i]) : -INFINITY;
+        for (int i = 0; i < 4; ++i) vals[it * VEC + i] = ok ? __uint_as_float(q[it][i]) : -INFINITY;
       }
     }
   } else {
+    T raw[PER];
 #pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int v = v_begin + it * kRowThreads + tid;
-      vals[it] = v < v_end ? to_f32(z[v]) : -INFINITY;
-    }
+    for (int it = 0; it < PER; ++it) raw[it] = z[min(v_begin + it * kRowThreads + tid, v_end - 1)];
+#pragma unroll
+    for (int it = 0; it < PER; ++it)
+      vals[it] = v_begin + it * kRowThreads + tid < v_end ? to_f32(raw[it]) : -INFINITY;
   }
   float m = -INFINITY;
 #pragma unroll
@@ -628,8 +634,12 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
   const int ldn = part_ld(V), c = part_chunk(V);
   const int rows_ws = R * (gamma + 1);
   (void)M_cap;
-  hipLaunchKernelGGL((row_partials_kernel<BF16>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s, tg, V,
-                     vec, nch, cu, R, rows_ws, ws.rowpart);
+  if (rows_vec_ok(target, V, V, Elem<BF16>::kVec))
+    hipLaunchKernelGGL((row_partials_kernel<BF16, true>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s,
+                       tg, V, nch, cu, R, rows_ws, ws.rowpart);
+  else
+    hipLaunchKernelGGL((row_partials_kernel<BF16, false>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s,
+                       tg, V, nch, cu, R, rows_ws, ws.rowpart);
   int st = launch_status();
   if (st) return st;
   if (nch <= 32)
@@ -650,7 +660,7 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
 #define DSPARK_RES_LAUNCH(NW_, NB_, PERCU)                                                         \
     {                                                                                              \
       typedef EngineGeom<BF16, KC, NW_> G;                                                         \
-      const dim3 grid(std::max(1, std::min(n_t, PERCU * ncu)));                                    \
+      const dim3 grid(engine_grid(n_t, PERCU * ncu));                                                     \
       if (vec_engine)                                                                              \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, true>), grid,             \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
@@ -752,8 +762,12 @@ static int launch_accept(const void* target, const int32_t* cu, const int32_t* a
                    rows_vec_ok(U, V, V, Elem<BF16>::kVec) && w1_vec_ok(W1, r);
   const int ldn = part_ld(V), c = part_chunk(V);
   const int rows_ws = R * (gamma + 1);
-  hipLaunchKernelGGL((row_partials_kernel<BF16>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s, tg, V,
-                     rows_vec_ok(target, V, V, Elem<BF16>::kVec), nch, cu, R, rows_ws, ws.rowpart);
+  if (rows_vec_ok(target, V, V, Elem<BF16>::kVec))
+    hipLaunchKernelGGL((row_partials_kernel<BF16, true>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s,
+                       tg, V, nch, cu, R, rows_ws, ws.rowpart);
+  else
+    hipLaunchKernelGGL((row_partials_kernel<BF16, false>), dim3(nch, rows_ws), dim3(kRowThreads), 0, s,
+                       tg, V, nch, cu, R, rows_ws, ws.rowpart);
   int st = launch_status();
   if (st) return st;
   hipLaunchKernelGGL(accept_jobs_kernel, dim3(ceil_div(rows_ws, 256)), dim3(256), 0, s, cu, anchor,
@@ -768,7 +782,7 @@ static int launch_accept(const void* target, const int32_t* cu, const int32_t* a
 #define DSPARK_ACC_LAUNCH(NW_, NB_, PERCU)                                                         \
     {                                                                                              \
       typedef EngineGeom<BF16, KC, NW_> G;                                                         \
-      const dim3 grid(std::max(1, std::min(n_t, PERCU * ncu)));                                    \
+      const dim3 grid(engine_grid(n_t, PERCU * ncu));                                                     \
       if (vec)                                                                                     \
         hipLaunchKernelGGL((accept_partials_kernel<BF16, KC, NW_, NB_, true>), grid,               \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
