@@ -150,16 +150,22 @@ __device__ __forceinline__ void load16_clamped(const typename Elem<BF16>::T* __r
   }
 }
 
+constexpr float kLog2e = 1.44269504088896340736f;
+
 // Softmax partial of 16 masked logits (-inf = masked) merged over the four
-// lanes holding one request's 64 entries, without branches.
+// lanes holding one request's 64 entries, without branches. The 16 terms are
+// 2^(z log2 e - m log2 e) with the exponent formed by one fused multiply-add
+// (v_exp_f32 computes 2^x); m log2 e is rounded once per tile, which scales
+// the tile's terms alike by at most 2^(ulp(m log2 e) / 2).
 __device__ __forceinline__ void softmax16_merge4(const float z[16], float& m_out, float& s_out) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, z[i]);
   const float mref = (m == -INFINITY) ? 0.0f : m;
+  const float mb = -mref * kLog2e;
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s += __expf(z[i] - mref);
+  for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, mb));
 #pragma unroll
   for (int o = 16; o <= 32; o <<= 1) {
     const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
@@ -568,6 +574,15 @@ __device__ __forceinline__ void stage_rows(const typename Elem<BF16>::T* __restr
 template <bool BF16>
 __device__ __forceinline__ void tile_logits(const f32x4 acc[4], const float u16[16], int nvalid,
                                             bool active, float z[16]) {
+  // every lane of the wave holds 16 valid entries of an active request (all
+  // tiles but the last, when R fills the blocks): no masks
+  if (__all(active && nvalid >= 16)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[4 * j + i] = acc[j][i] + u16[4 * j + i];
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll

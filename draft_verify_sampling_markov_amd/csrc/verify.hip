@@ -232,12 +232,25 @@ __device__ __forceinline__ float corr_weight(float zt, float zd, float lse_t, fl
   return fmaxf(pt - pd, 0.0f);
 }
 
-// q and p_t for the 16 entries a lane holds (invalid entries: 0).
-template <bool BF16>
+// q and p_t for the 16 entries a lane holds (invalid entries: 0). FAST: take
+// an unmasked path when every lane of the wave holds 16 valid entries (it
+// costs registers, which the two-block engine shape does not have to spare).
+template <bool BF16, bool FAST>
 __device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float zt16[16],
                                                  const float u16[16], int nvalid, float lse_t,
                                                  float lse_d, bool residual, float q[16],
                                                  float pt[16]) {
+  if (FAST && __all(nvalid >= 16)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = 4 * j + i;
+        q[idx] = corr_weight(zt16[idx], acc[j][i] + u16[idx], lse_t, lse_d, residual);
+        pt[idx] = __expf(zt16[idx] - lse_t);
+      }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -259,7 +272,7 @@ __device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float
 // rpart[n * ldn + part_pos(t, c)]. The job fields are read
 // once per kernel (prepare); a bonus job reads its target row in place of the
 // U row, so the loads need no branch.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool FAST>
 struct ResidualEpi {
   typedef typename Elem<BF16>::T T;
   struct Pre {
@@ -301,8 +314,8 @@ struct ResidualEpi {
     float zt16[16], u16[16], q[16], pt[16];
     unpack16<BF16>(p.zt, zt16);
     unpack16<BF16>(p.u, u16);
-    corr_tile_values<BF16>(acc, zt16, u16, (s.active ? nvalid : 0), s.lse_t, s.lse_d, s.residual, q,
-                           pt);
+    corr_tile_values<BF16, FAST>(acc, zt16, u16, (s.active ? nvalid : 0), s.lse_t, s.lse_d,
+                                 s.residual, q, pt);
     float sq = 0.0f, sp = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     Jobs jobs, int g0, int R, int gamma, int V, int r, int n_t, float2* __restrict__ rpart, int ldn,
     int c, float2* __restrict__ junk, unsigned* __restrict__ queue) {
-  const ResidualEpi<BF16, VEC> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c, junk};
+  const ResidualEpi<BF16, VEC, NB == 1> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c, junk};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
                                          r, n_t, epi, queue, V);
 }
