@@ -223,12 +223,20 @@ __global__ __launch_bounds__(256) void decide_kernel(
 // residual / bonus weights
 // ---------------------------------------------------------------------------
 
-// q for one entry: max(0, p_t - p_d) for a residual, p_t for a bonus.
-__device__ __forceinline__ float corr_weight(float zt, float zd, float lse_t, float lse_d,
+// exp(z - lse) as 2^(z log2 e + b) with b = -lse log2 e (one fused
+// multiply-add before the exponential; b is rounded once per request)
+__device__ __forceinline__ float shifted_exp(float z, float b) {
+  return __builtin_amdgcn_exp2f(fmaf(z, kLog2e, b));
+}
+__device__ __forceinline__ float exp_shift(float lse) { return -lse * kLog2e; }
+
+// q for one entry: max(0, p_t - p_d) for a residual, p_t for a bonus; bt and
+// bd are exp_shift of the target and draft log-sum-exps.
+__device__ __forceinline__ float corr_weight(float zt, float zd, float bt, float bd,
                                              bool residual) {
-  const float pt = __expf(zt - lse_t);
+  const float pt = shifted_exp(zt, bt);
   if (!residual) return pt;
-  const float pd = __expf(zd - lse_d);
+  const float pd = shifted_exp(zd, bd);
   return fmaxf(pt - pd, 0.0f);
 }
 
@@ -237,8 +245,8 @@ __device__ __forceinline__ float corr_weight(float zt, float zd, float lse_t, fl
 // costs registers, which the two-block engine shape does not have to spare).
 template <bool BF16, bool FAST>
 __device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float zt16[16],
-                                                 const float u16[16], int nvalid, float lse_t,
-                                                 float lse_d, bool residual, float q[16],
+                                                 const float u16[16], int nvalid, float bt,
+                                                 float bd, bool residual, float q[16],
                                                  float pt[16]) {
   if (FAST && __all(nvalid >= 16)) {
 #pragma unroll
@@ -246,8 +254,8 @@ __device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = 4 * j + i;
-        q[idx] = corr_weight(zt16[idx], acc[j][i] + u16[idx], lse_t, lse_d, residual);
-        pt[idx] = __expf(zt16[idx] - lse_t);
+        q[idx] = corr_weight(zt16[idx], acc[j][i] + u16[idx], bt, bd, residual);
+        pt[idx] = shifted_exp(zt16[idx], bt);
       }
     return;
   }
@@ -258,8 +266,8 @@ __device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float
       const int idx = 4 * j + i;
       const bool ok = idx < nvalid;
       const float zd = acc[j][i] + u16[idx];
-      q[idx] = ok ? corr_weight(zt16[idx], zd, lse_t, lse_d, residual) : 0.0f;
-      pt[idx] = ok ? __expf(zt16[idx] - lse_t) : 0.0f;
+      q[idx] = ok ? corr_weight(zt16[idx], zd, bt, bd, residual) : 0.0f;
+      pt[idx] = ok ? shifted_exp(zt16[idx], bt) : 0.0f;
     }
 }
 
@@ -281,7 +289,7 @@ struct ResidualEpi {
   struct St {
     const T* trow;
     const T* urow;
-    float lse_t, lse_d;
+    float bt, bd;  // exp_shift of the job's target and draft log-sum-exps
     int ng;
     bool residual, active;
   };
@@ -300,8 +308,8 @@ struct ResidualEpi {
     s.residual = jobs.kind[s.ng] == 0;
     s.trow = target + (size_t)jobs.trow[s.ng] * V;
     s.urow = s.residual ? U + ((size_t)s.ng * gamma + jobs.slot[s.ng] - 1) * V : s.trow;
-    s.lse_t = jobs.lse_t[s.ng];
-    s.lse_d = jobs.lse_d[s.ng];
+    s.bt = exp_shift(jobs.lse_t[s.ng]);
+    s.bd = exp_shift(jobs.lse_d[s.ng]);
     return s;
   }
   __device__ __forceinline__ void side_work() const {}
@@ -314,8 +322,8 @@ struct ResidualEpi {
     float zt16[16], u16[16], q[16], pt[16];
     unpack16<BF16>(p.zt, zt16);
     unpack16<BF16>(p.u, u16);
-    corr_tile_values<BF16, FAST>(acc, zt16, u16, (s.active ? nvalid : 0), s.lse_t, s.lse_d,
-                                 s.residual, q, pt);
+    corr_tile_values<BF16, FAST>(acc, zt16, u16, (s.active ? nvalid : 0), s.bt, s.bd, s.residual,
+                                 q, pt);
     float sq = 0.0f, sp = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -412,8 +420,8 @@ __global__ __launch_bounds__(kSelThreads) void residual_select_kernel(
   f32x4 acc[4];
   tile_mma_regs<BF16, KC>(at, b, acc);
   const float zd = own_entry(acc, lane) + ud;  // the same sum the residual pass formed
-  const float q = corr_weight(zt, zd, lse_t, lse_d, residual);
-  const float pt = __expf(zt - lse_t);
+  const float q = corr_weight(zt, zd, exp_shift(lse_t), exp_shift(lse_d), residual);
+  const float pt = shifted_exp(zt, exp_shift(lse_t));
   const float wi = valid ? (use_pt ? pt : q) : 0.0f;
   const int sel = tile_pick(wi, valid, ws.pb, ws.T, lane);
   if (lane == 0) out_tokens[(size_t)n * (gamma + 1) + jobs.slot[n] - 1] = t * kTileV + sel;
