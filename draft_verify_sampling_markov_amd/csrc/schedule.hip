@@ -346,19 +346,58 @@ __device__ __forceinline__ void pack_body(
   }
 }
 
+// The pack of full blocks (every window gamma): row i of request i / (gamma
+// + 1) at slot i mod (gamma + 1), so no scan and no search and no barrier;
+// the same outputs as pack_body with win_len == nullptr.
+__device__ __forceinline__ void pack_full_body(
+    const int* __restrict__ anchor, const int* __restrict__ tokens, int R, int gamma,
+    const TierList& tiers, int M_cap, int* __restrict__ cu_seqlens, int* __restrict__ ptok,
+    int* __restrict__ preq, int* __restrict__ pslot, int* __restrict__ totals) {
+  const int tid = threadIdx.x, G = gamma + 1, M = R * G;
+  for (int i = tid; i <= R; i += blockDim.x) cu_seqlens[i] = i * G;
+  for (int i = tid; i < M_cap; i += blockDim.x) {
+    if (i < M) {
+      const int req = i / G, j = i - req * G;
+      ptok[i] = j == 0 ? anchor[req] : tokens[(size_t)req * gamma + j - 1];
+      preq[i] = req;
+      pslot[i] = j;
+    } else {
+      ptok[i] = 0;
+      preq[i] = -1;
+      pslot[i] = -1;
+    }
+  }
+  if (tid == 0) {
+    int pad = -1;
+    for (int t = 0; t < tiers.n; ++t)
+      if (tiers.v[t] >= M) {
+        pad = tiers.v[t];
+        break;
+      }
+    totals[0] = M;
+    totals[1] = pad;
+  }
+}
+
 __global__ __launch_bounds__(1024) void pack_kernel(
     const int* __restrict__ anchor, const int* __restrict__ tokens, const int* __restrict__ win_len,
     int R, int gamma, TierList tiers, int M_cap, int* __restrict__ cu_seqlens,
     int* __restrict__ ptok, int* __restrict__ preq, int* __restrict__ pslot,
     int* __restrict__ totals) {
   __shared__ PackShared ps;
+  if (win_len == nullptr) {  // uniform
+    pack_full_body(anchor, tokens, R, gamma, tiers, M_cap, cu_seqlens, ptok, preq, pslot, totals);
+    return;
+  }
   pack_body(anchor, tokens, win_len, R, gamma, tiers, M_cap, cu_seqlens, ptok, preq, pslot, totals,
             ps);
 }
 
 // Schedule, then pack, in one workgroup: the windows pass through shared
 // memory. pack_windows == 0: the pack keeps every window at gamma (the static
-// and cap-accept blocks), as a pack call with win_len NULL.
+// and cap-accept blocks), as a pack call with win_len NULL; it does not depend
+// on the schedule then, so it goes first and its stores drain while the
+// scheduler sorts.
 __global__ __launch_bounds__(kSchedThreads) void schedule_pack_kernel(
     const float* __restrict__ surv, const float* __restrict__ surv_budget,
     const uint32_t* __restrict__ sps, int M_max, int R, int gamma, int B_cap, int mode, int K_fixed,
@@ -369,11 +408,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_pack_kernel(
   __shared__ SchedShared sh;
   __shared__ PackShared ps;
   __shared__ int win_s[kMaxRows / 2];
+  if (!pack_windows)  // uniform
+    pack_full_body(anchor, tokens, R, gamma, tiers, M_cap, cu_seqlens, ptok, preq, pslot, totals);
   schedule_body(surv, surv_budget, sps, M_max, R, gamma, B_cap, mode, K_fixed, win_len, K_out, sh,
                 win_s);
+  if (!pack_windows) return;
   __syncthreads();
-  pack_body(anchor, tokens, pack_windows ? win_s : nullptr, R, gamma, tiers, M_cap, cu_seqlens,
-            ptok, preq, pslot, totals, ps);
+  pack_body(anchor, tokens, win_s, R, gamma, tiers, M_cap, cu_seqlens, ptok, preq, pslot, totals,
+            ps);
 }
 
 }  // namespace dspark
