@@ -7,7 +7,9 @@ windows, K, cu_seqlens, packed tokens / requests / slots and the totals. The
 oracle parity of the fused call is covered by the chain parity tests, whose
 steps use it. Cases: the three scheduler modes, a stale budget array, full
 blocks (pack_windows off) and scheduled windows, an empty budget, the row
-limit R (gamma + 1) = 4096, and a total that exceeds every tier.
+limit R (gamma + 1) = 4096, and a total that exceeds every tier. The
+full-block pack (no window array) must also equal the scanned pack of
+windows that are all gamma.
 """
 import numpy as np
 import pytest
@@ -71,3 +73,25 @@ def test_row_limit_and_tier_overflow(dv):
     assert tot[0] <= 4096
     K, tot = _case(dv, 256, 15, 5000, 3840, 0, 0, False, False, [512, 1024, 2048], 8)
     assert tot.tolist() == [4096, -1]
+
+
+@pytest.mark.parametrize("R,gamma,extra", [(1, 1, 0), (64, 7, 0), (13, 16, 37), (256, 15, 0),
+                                           (2048, 1, 5)])
+def test_full_block_pack_equals_scanned_pack(dv, R, gamma, extra):
+    # win_len NULL takes the index-arithmetic path; an explicit array of gamma
+    # windows takes the scan-and-search path: every output must agree
+    import torch
+    rng = np.random.default_rng(R * 31 + gamma)
+    V = 5000
+    anchor = torch.from_numpy(rng.integers(0, V, R).astype(np.int32)).cuda()
+    tokens = torch.from_numpy(rng.integers(0, V, (R, gamma)).astype(np.int32)).cuda()
+    full = torch.full((R,), gamma, dtype=torch.int32, device="cuda")
+    M_cap = R * (gamma + 1) + extra
+    tiers = [8, 64, 512, 4096]
+    a = dv.pack_ragged(anchor, tokens, None, tiers, M_cap)
+    b = dv.pack_ragged(anchor, tokens, full, tiers, M_cap)
+    torch.cuda.synchronize()
+    for k in a:
+        assert np.array_equal(a[k].cpu().numpy(), b[k].cpu().numpy()), k
+    assert a["totals"].cpu().numpy().tolist()[0] == R * (gamma + 1)
+    log(f"[pack] full blocks R={R} gamma={gamma} M_cap={M_cap}: index path == scanned path")
