@@ -509,7 +509,7 @@ struct AcceptEpi {
   struct St {
     const T* trow;
     const T* urow;
-    float lse_t, lse_d;
+    float bt, bd;  // exp_shift of the slot's target and draft log-sum-exps
     int ng;
     bool active;
   };
@@ -527,8 +527,8 @@ struct AcceptEpi {
     s.active = n < R && jobs.out[s.ng] >= 0;
     s.trow = target + (size_t)jobs.trow[s.ng] * V;
     s.urow = U + (size_t)jobs.urow[s.ng] * V;
-    s.lse_t = jobs.lse_t[s.ng];
-    s.lse_d = jobs.lse_d[s.ng];
+    s.bt = exp_shift(jobs.lse_t[s.ng]);
+    s.bd = exp_shift(jobs.lse_d[s.ng]);
     return s;
   }
   __device__ __forceinline__ void side_work() const {}
@@ -549,7 +549,7 @@ struct AcceptEpi {
       for (int i = 0; i < 4; ++i) {
         const int idx = 4 * j + i;
         const float zd = acc[j][i] + u16[idx];
-        const float pd = __expf(zd - s.lse_d), pt = __expf(zt16[idx] - s.lse_t);
+        const float pd = shifted_exp(zd, s.bd), pt = shifted_exp(zt16[idx], s.bt);
         sm += idx < nv ? fminf(pd, pt) : 0.0f;
       }
     sm += __shfl_xor(sm, 16, kWave);
