@@ -111,9 +111,13 @@ struct MarkovEpi {
   // wave per request (workgroup b, wave j: requests b + G (j + waves i)), with
   // the wave code of the confidence kernel, so the values are the same.
   __device__ __forceinline__ void side_work() const {
-    const int q = (int)blockIdx.x * kWave + (int)threadIdx.x;
-    if (draw.u_out != nullptr && threadIdx.x < kWave && q < R)
-      draw.u_out[q] = slot_uniform(draw.seed, draw.step.get(), draw.req_ids[q], draw.k, kPurposeDraft);
+    // wave 0 of every workgroup strides over the requests, so that every
+    // request gets its uniform however few workgroups the vocabulary needs
+    if (draw.u_out != nullptr && threadIdx.x < kWave) {
+      const uint64_t stp = draw.step.get();
+      for (int q = (int)blockIdx.x * kWave + (int)threadIdx.x; q < R; q += (int)gridDim.x * kWave)
+        draw.u_out[q] = slot_uniform(draw.seed, stp, draw.req_ids[q], draw.k, kPurposeDraft);
+    }
     if (ca.h == nullptr) return;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int waves = blockDim.x / kWave, k = draw.k;

@@ -26,11 +26,14 @@ from .philox import uniforms, PURPOSE_DRAFT
 
 def widen(a: np.ndarray) -> np.ndarray:
     """Stored input -> float64. uint16 arrays are bfloat16 bit patterns (the
-    value is the top half of a float32); float32 arrays are widened exactly."""
+    value is the top half of a float32); float32 arrays are widened exactly;
+    float64 arrays (inputs a caller widened once) are returned as they are."""
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    if a.dtype in (np.float32, np.float64):
+    if a.dtype == np.float64:
+        return a                                 # already widened: no copy
+    if a.dtype == np.float32:
         return a.astype(np.float64)
     raise TypeError(f"unsupported stored dtype {a.dtype}")
 

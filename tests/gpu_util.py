@@ -57,6 +57,15 @@ class PackedView:
         return self.target[r, i - int(self.cu[r])]
 
 
+def factors64(inp):
+    """W1 and W2 widened to float64 once per input dict (the oracle widens
+    stored values exactly and passes float64 through, so its results are the
+    same; this only avoids re-widening the whole factors on every call)."""
+    if "_W64" not in inp:
+        inp["_W64"] = (oracle.widen(inp["W1"]), oracle.widen(inp["W2"]))
+    return inp["_W64"]
+
+
 def draw_ok(w: np.ndarray, t: float, g: int, o: int, tol: float = TOL) -> bool:
     """GPU id g vs oracle id o for weights w and threshold t."""
     if g == o:
@@ -75,10 +84,11 @@ def check_draft(res, inp, seed, step, reqs, label="") -> int:
     R, gamma = tokens.shape
     flips = 0
     reqs = np.asarray(reqs)
+    W1, W2 = factors64(inp)
     for k in range(1, gamma + 1):
         x_prev = inp["anchor"][reqs] if k == 1 else tokens[reqs, k - 2]
         u = [oracle.uniforms(seed, step, int(inp["req_ids"][r]), k)[oracle.PURPOSE_DRAFT] for r in reqs]
-        rec = oracle.markov_step(inp["U"][reqs, k - 1], inp["W1"], inp["W2"], x_prev, u)
+        rec = oracle.markov_step(inp["U"][reqs, k - 1], W1, W2, x_prev, u)
         for i, r in enumerate(reqs):
             g, o = int(tokens[r, k - 1]), int(rec["tokens"][i])
             assert 0 <= g < inp["U"].shape[2], (label, r, k, g)
@@ -92,7 +102,7 @@ def check_draft(res, inp, seed, step, reqs, label="") -> int:
 
 def check_confidence(res, inp, reqs, label=""):
     reqs = np.asarray(reqs)
-    ref = oracle.confidence(inp["h"][reqs], inp["W1"], inp["anchor"][reqs], res["tokens"][reqs],
+    ref = oracle.confidence(inp["h"][reqs], factors64(inp)[0], inp["anchor"][reqs], res["tokens"][reqs],
                             inp["w"], float(inp["b"]))
     np.testing.assert_allclose(res["conf"][reqs], ref["conf"], rtol=0, atol=TOL, err_msg=label)
     np.testing.assert_allclose(res["surv"][reqs], ref["surv"], rtol=0, atol=TOL, err_msg=label)
@@ -120,8 +130,9 @@ def check_verify(res, inp, target_rows, mode, win_len, seed, step, reqs, label="
     """Teacher-forced: the oracle verifies the GPU's drafts with the GPU's
     p_draft and packing. Returns the number of excused flips."""
     cu = res["cu_seqlens"]
+    W1, W2 = factors64(inp)
     ref = oracle.verify(target_rows, cu, inp["anchor"], res["tokens"], res["p_draft"], inp["U"],
-                        inp["W1"], inp["W2"], win_len, mode, seed, step, inp["req_ids"],
+                        W1, W2, win_len, mode, seed, step, inp["req_ids"],
                         requests=[int(r) for r in reqs])
     flips = 0
     for r in reqs:
@@ -151,3 +162,39 @@ def sample_requests(R: int, n: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(R, size=n - 2, replace=False).tolist()) | {0, R - 1}
     return np.array(sorted(pick))
+
+
+MODES = {"static": 0, "compact": 1, "cap_accept": 2}
+
+
+def run_and_check(dv, spec, vmode: str, smode: int = oracle.SCHED_ARGMAX, B_cap=None, K_fixed=0,
+                  sample=None, seed=0, step=0, inp=None, check_draft_conf: bool = True):
+    """One chain step on the GPU (Chain.run), then every stage teacher-forced
+    against the oracle. sample=None checks every request; check_draft_conf=
+    False skips the draft and confidence checks (a caller that already checked
+    them on the same inputs, seed and step, e.g. a budget sweep)."""
+    import torch
+    label = f"{spec.name}/{vmode}/sched{smode}/B{B_cap}"
+    log(f"[parity] {label}: R={spec.R} gamma={spec.gamma} V={spec.V} r={spec.r} dtype={spec.dtype}")
+    if inp is None:
+        inp = synth.generate(spec)
+    dev, sps = upload(inp, spec)
+    B = spec.budgets[0] if B_cap is None else B_cap
+    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B, verify_mode=MODES[vmode],
+                  sched_mode=smode, K_fixed=K_fixed, seed=seed, step=step)
+    ch.run(gather=True)
+    torch.cuda.synchronize()
+    res = ch.results()
+    reqs = np.arange(spec.R) if sample is None else sample_requests(spec.R, sample)
+    flips = 0
+    if check_draft_conf:
+        flips += check_draft(res, inp, seed, step, reqs, label)
+        check_confidence(res, inp, reqs, label)
+    ref_s = check_schedule(res, sps, B, smode, K_fixed, label)
+    full = vmode in ("static", "cap_accept")
+    check_pack(res, inp, None if full else ref_s["win_len"], spec.tiers, ch.M_cap, label)
+    rows = PackedView(inp["target"], res["cu_seqlens"])
+    flips += check_verify(res, inp, rows, MODES[vmode], res["win_len"], seed, step, reqs, label)
+    log(f"[parity] {label}: ok over {len(reqs)} requests, K={int(res['K'][0])} "
+        f"M={res['totals'].tolist()} mean A={res['accept_len'].mean():.2f} excused flips={flips}")
+    return res, ch

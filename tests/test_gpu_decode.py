@@ -15,7 +15,7 @@ import pytest
 import oracle
 import synth
 from tests.gpu_util import (log, upload, PackedView, check_draft, check_confidence,
-                            check_schedule, check_pack, check_verify, sample_requests)
+                            check_schedule, check_pack, check_verify, sample_requests, factors64)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,7 @@ def dv():
 def check_loop(steps, inp, spec, vmode, lag, seed, step0, B, reqs, label, smode=oracle.SCHED_ARGMAX):
     flips = 0
     R = spec.R
+    factors64(inp)                 # widened once; every step's view shares them
     for t, res in enumerate(steps):
         lab = f"{label}/t{t}"
         step = int(res["step"][0])
@@ -132,4 +133,4 @@ def test_decode_survives_a_lag_change(dv):
 
 @pytest.mark.parametrize("name,vmode", [("qwen3", "compact"), ("mixed", "compact")])
 def test_full_size_decode(dv, name, vmode):
-    run_loop(dv, synth.CONFIGS[name], vmode, 2, 4, sample=6)
+    run_loop(dv, synth.CONFIGS[name], vmode, 2, 4)

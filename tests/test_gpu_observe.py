@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import log, upload, PackedView, sample_requests, TOL
+from tests.gpu_util import log, upload, PackedView, sample_requests, factors64, TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +49,11 @@ def _compare_block(got, ref, label):
 
 
 def _check_cstar(steps, inp, reqs, label):
+    W1, W2 = factors64(inp)
     for t, s in enumerate(steps):
         rows = PackedView(inp["target"], s["cu_seqlens"])
         ref = oracle.analytic_acceptance(rows, s["cu_seqlens"], s["anchor"], s["tokens"], inp["U"],
-                                         inp["W1"], inp["W2"], requests=[int(r) for r in reqs])
+                                         W1, W2, requests=[int(r) for r in reqs])
         got = s["cstar"]
         for r in reqs:
             nan_g, nan_o = np.isnan(got[r]), np.isnan(ref[r])
@@ -111,4 +112,4 @@ def test_ragged_rank_and_vocab(dv):
 
 @pytest.mark.parametrize("name,vmode", [("qwen3", "cap_accept"), ("mixed", "compact")])
 def test_full_size_observed(dv, name, vmode):
-    run_observed(dv, synth.CONFIGS[name], vmode, 2, 3, sample=5, graph_check=False)
+    run_observed(dv, synth.CONFIGS[name], vmode, 2, 3, graph_check=False)

@@ -3,16 +3,15 @@ stage on the GPU's own chain outputs), through the C ABI.
 
 Small workloads span several 16-request blocks, several 64-entry vocabulary
 tiles and ragged tails in both; the five named workloads run at full size in
-the configuration bench.py times, with the oracle checking a sample of
-requests for the per-request stages and every request for schedule and pack.
+the configuration bench.py times, with the oracle checking every request of
+every stage.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import (log, upload, PackedView, check_draft, check_confidence,
-                            check_schedule, check_pack, check_verify, sample_requests, to_dev)
+from tests.gpu_util import log, upload, run_and_check, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -25,36 +24,6 @@ def dv():
     import draft_verify_sampling_markov_amd as dv
     dv.load_library()          # raises if the HIP library is missing
     return dv
-
-
-MODES = {"static": 0, "compact": 1, "cap_accept": 2}
-
-
-def run_and_check(dv, spec, vmode: str, smode: int = oracle.SCHED_ARGMAX, B_cap=None, K_fixed=0,
-                  sample=None, seed=0, step=0, inp=None):
-    import torch
-    label = f"{spec.name}/{vmode}/sched{smode}/B{B_cap}"
-    log(f"[parity] {label}: R={spec.R} gamma={spec.gamma} V={spec.V} r={spec.r} dtype={spec.dtype}")
-    if inp is None:
-        inp = synth.generate(spec)
-    dev, sps = upload(inp, spec)
-    B = spec.budgets[0] if B_cap is None else B_cap
-    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B, verify_mode=MODES[vmode],
-                  sched_mode=smode, K_fixed=K_fixed, seed=seed, step=step)
-    ch.run(gather=True)
-    torch.cuda.synchronize()
-    res = ch.results()
-    reqs = np.arange(spec.R) if sample is None else sample_requests(spec.R, sample)
-    flips = check_draft(res, inp, seed, step, reqs, label)
-    check_confidence(res, inp, reqs, label)
-    ref_s = check_schedule(res, sps, B, smode, K_fixed, label)
-    full = vmode in ("static", "cap_accept")
-    check_pack(res, inp, None if full else ref_s["win_len"], spec.tiers, ch.M_cap, label)
-    rows = PackedView(inp["target"], res["cu_seqlens"])
-    flips += check_verify(res, inp, rows, MODES[vmode], res["win_len"], seed, step, reqs, label)
-    log(f"[parity] {label}: ok, K={int(res['K'][0])} M={res['totals'].tolist()} "
-        f"mean A={res['accept_len'].mean():.2f} excused flips={flips}")
-    return res, ch
 
 
 # ---------------------------------------------------------------------------
@@ -175,9 +144,9 @@ def test_row_limit(dv):
     sp = synth.small_spec("rowlimit", R=256, gamma=15, V=700, r=32, d=16, dtype="bf16", seed=6,
                           cost=("stair_T", 2e-3, 1e-8, 0.005))
     inp = synth.generate(sp)
-    res, _ = run_and_check(dv, sp, "static", sample=10, inp=inp)
+    res, _ = run_and_check(dv, sp, "static", inp=inp)
     assert int(res["totals"][0]) == 4096
-    res, _ = run_and_check(dv, sp, "compact", sample=10, inp=inp)
+    res, _ = run_and_check(dv, sp, "compact", inp=inp, check_draft_conf=False)
     assert int(res["K"][0]) > 1000
 
 
@@ -197,20 +166,21 @@ def test_tiny_all_modes(dv):
 
 @pytest.mark.parametrize("vmode", ["static", "compact"])
 def test_qwen3(dv, vmode):
-    run_and_check(dv, synth.CONFIGS["qwen3"], vmode, sample=12)
+    run_and_check(dv, synth.CONFIGS["qwen3"], vmode)
 
 
 def test_dsv4_compact(dv):
-    run_and_check(dv, synth.CONFIGS["dsv4"], "compact", sample=12)
+    run_and_check(dv, synth.CONFIGS["dsv4"], "compact")
 
 
 @pytest.mark.parametrize("vmode", ["cap_accept", "compact"])
 def test_mixed(dv, vmode):
-    run_and_check(dv, synth.CONFIGS["mixed"], vmode, sample=12)
+    run_and_check(dv, synth.CONFIGS["mixed"], vmode)
 
 
 def test_long_budget_sweep(dv):
     sp = synth.CONFIGS["long"]
     inp = synth.generate(sp)
-    for B in sp.budgets:
-        run_and_check(dv, sp, "compact", B_cap=B, sample=8, inp=inp)
+    # the draft and confidence do not depend on the budget: checked once
+    for i, B in enumerate(sp.budgets):
+        run_and_check(dv, sp, "compact", B_cap=B, inp=inp, check_draft_conf=i == 0)

@@ -86,4 +86,4 @@ def test_ragged_rank_vocab_and_shards(dv):
 
 @pytest.mark.parametrize("name", ["qwen3", "dsv4"])
 def test_full_size_eight_way(dv, name):
-    run_sharded(dv, synth.CONFIGS[name], 8, sample=6)
+    run_sharded(dv, synth.CONFIGS[name], 8)
