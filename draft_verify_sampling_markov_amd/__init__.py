@@ -36,6 +36,8 @@ _SIGNATURES = {
     "dspark_status_string": (_c.c_char_p, [_i]),
     "dspark_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_workspace_init": (_i, [_vp, _sz, _vp]),
+    "dspark_workspace_status_offset": (_sz, [_i, _i]),
+    "dspark_set_draft_path": (_i, [_i]),
     "dspark_prepacked_w2_bytes": (_sz, [_i, _i, _i]),
     "dspark_prepack_w2": (_i, [_vp, _i, _i, _i, _vp, _sz, _vp]),
     "dspark_cost_table_prepare": (_i, [_vp, _i, _vp, _i, _i, _vp]),
@@ -160,6 +162,27 @@ def _empty(shape, dtype, device):
 
 def workspace_bytes(call: int, R: int, gamma: int, V: int, r: int) -> int:
     return int(load_library().dspark_workspace_bytes(call, R, gamma, V, r))
+
+
+DRAFT_AUTO, DRAFT_PER_SLOT, DRAFT_RESIDENT = 0, 1, 2
+
+
+def set_draft_path(path: int) -> int:
+    """Process-wide choice of draft kernels (DRAFT_AUTO: the library's choice;
+    DRAFT_PER_SLOT: per-slot launches; DRAFT_RESIDENT: the resident-W2 block
+    kernel where the shape allows it). Returns the previous choice."""
+    rc = load_library().dspark_set_draft_path(int(path))
+    _check(min(rc, 0))
+    return rc
+
+
+def draft_status(ws, R: int, V: int) -> int:
+    """The error word of a draft workspace (synchronises): 1 if a resident
+    draft's barrier wait ran out since the workspace was initialised."""
+    off = int(load_library().dspark_workspace_status_offset(R, V))
+    if off == 0 or off + 4 > ws.numel() * ws.element_size():
+        raise ValueError("workspace too small for these sizes")
+    return int(ws.view(-1)[off:off + 4].cpu().numpy().view(np.uint32)[0])
 
 
 def workspace_init(ws, stream=None):

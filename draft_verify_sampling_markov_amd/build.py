@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdspark.so")
-SOURCES = ["abi.hip", "markov.hip", "confidence.hip", "schedule.hip", "verify.hip", "decode.hip", "observe.hip",
+SOURCES = ["abi.hip", "markov.hip", "resident.hip", "confidence.hip", "schedule.hip", "verify.hip", "decode.hip", "observe.hip",
            "calibrate.hip"]
 
 HIPCC_FLAGS = [

@@ -50,3 +50,8 @@ extern "C" int dspark_workspace_init(void* ws, size_t ws_bytes, void* stream) {
                      static_cast<hipStream_t>(stream), static_cast<unsigned char*>(ws), ws_bytes);
   return launch_status();
 }
+
+extern "C" size_t dspark_workspace_status_offset(int R, int V) {
+  if (R < 1 || R > kMaxRows || V < 1) return 0;
+  return resident_bar_offset(R, V) + 10 * 256;  // the error word of the barrier block
+}

@@ -152,6 +152,25 @@ __device__ __forceinline__ void load16_clamped(const typename Elem<BF16>::T* __r
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// The value lane l ^ 16 (ROW = true) or l ^ 32 (ROW = false) holds, with the
+// gfx950 lane-swap instructions: v_permlane16_swap with both operands x gives
+// every lane the pair (row 2i, row 2i + 1) of its 32-lane half, in that
+// order, and v_permlane32_swap the pair (lanes 0-31, lanes 32-63); the partner
+// is the element that is not the lane's own. Plain VALU, where a shuffle
+// through the LDS crossbar (ds_bpermute) waits on an LDS round trip.
+template <bool ROW>
+__device__ __forceinline__ float lane_partner(float x) {
+  const unsigned u = __float_as_uint(x);
+  const unsigned lane = __lane_id();
+  if constexpr (ROW) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
 // Softmax partial of 16 masked logits (-inf = masked) merged over the four
 // lanes holding one request's 64 entries, without branches. The 16 terms are
 // 2^(z log2 e - m log2 e) with the exponent formed by one fused multiply-add
@@ -167,8 +186,9 @@ __device__ __forceinline__ void softmax16_merge4(const float z[16], float& m_out
 #pragma unroll
   for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, mb));
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+  for (int o = 0; o < 2; ++o) {  // partners l ^ 16, then l ^ 32
+    const float m2 = o == 0 ? lane_partner<true>(m) : lane_partner<false>(m);
+    const float s2 = o == 0 ? lane_partner<true>(s) : lane_partner<false>(s);
     const float mm = fmaxf(m, m2);
     const float mr = (mm == -INFINITY) ? 0.0f : mm;
     const float sa = (m == -INFINITY) ? 0.0f : s * __expf(m - mr);

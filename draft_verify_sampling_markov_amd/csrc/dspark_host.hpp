@@ -84,6 +84,21 @@ inline int check_sizes(int R, int gamma, int V, int r, int dt) {
 
 // Workspace layout pieces (bytes, 256-aligned).
 size_t markov_ws_bytes(int R, int V);
+// Barrier block of a draft workspace (resident-W2 kernel): 11 words, each on
+// its own 256-byte line.
+constexpr size_t kResidentBarBytes = 11 * 256;
+size_t resident_bar_offset(int R, int V);
+
+// The resident-W2 draft (resident.hip): whether a call of these sizes,
+// pointers and dtype takes it, and the launch (bfloat16, rank chunk count 8).
+struct StepArg;
+struct ConfArgs;
+bool resident_draft_eligible(const void* U, const void* W1, int R, int gamma, int V, int r,
+                             int dtype);
+int resident_draft_launch(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
+                          uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
+                          int V, int r, int32_t* tokens, float* p_draft, float* lse_draft,
+                          void* ws, const ConfArgs& ca, hipStream_t s);
 // 16-byte load flags of the confidence head's two dot products (alignment and
 // lengths of h, the W1 rows and the weight vector)
 void confidence_vec_flags(const void* h, const void* W1, const float* w, int d, int r, int dtype,

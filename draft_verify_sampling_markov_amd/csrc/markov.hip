@@ -449,7 +449,8 @@ static size_t markov_queue_offset(int R, int V) { return markov_junk_offset(R, V
 static size_t markov_u_offset(int R, int V) {
   return markov_queue_offset(R, V) + (size_t)queue_groups(R) * kQueueWordsPerGroup * 4;
 }
-size_t markov_ws_bytes(int R, int V) { return markov_u_offset(R, V) + align_up((size_t)R * 4, 256); }
+size_t resident_bar_offset(int R, int V) { return markov_u_offset(R, V) + align_up((size_t)R * 4, 256); }
+size_t markov_ws_bytes(int R, int V) { return resident_bar_offset(R, V) + kResidentBarBytes; }
 static float* markov_u(float2* part, int R, int V) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(part) + markov_u_offset(R, V));
 }
@@ -696,6 +697,9 @@ static int markov_dispatch(const void* U, const void* W1, const void* W2p, const
                            uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                            int V, int r, int dtype, int32_t* tokens, float* p, float* lse,
                            float2* part, const ConfArgs& ca, hipStream_t s) {
+  if (resident_draft_eligible(U, W1, R, gamma, V, r, dtype))
+    return resident_draft_launch(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, tokens,
+                                 p, lse, part, ca, s);
   if (dtype == DSPARK_BF16) {
     DSPARK_KC_DISPATCH(true, launch_markov, U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V,
                        r, tokens, p, lse, part, ca, s)
@@ -747,7 +751,8 @@ extern "C" int dspark_markov_draft_confidence(
     return DSPARK_EINVAL;
   if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!conf_in_prologue(R, V, dtype == DSPARK_BF16)) {
+  const bool resident = resident_draft_eligible(U, W1, R, gamma, V, r, dtype);
+  if (!resident && !conf_in_prologue(R, V, dtype == DSPARK_BF16)) {
     // every GEMM workgroup would carry a request: the head as a launch of its own
     st = markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
                          r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws),

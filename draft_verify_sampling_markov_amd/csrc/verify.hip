@@ -330,10 +330,10 @@ struct ResidualEpi {
       sq += q[i];
       sp += pt[i];
     }
-    sq += __shfl_xor(sq, 16, kWave);
-    sp += __shfl_xor(sp, 16, kWave);
-    sq += __shfl_xor(sq, 32, kWave);
-    sp += __shfl_xor(sp, 32, kWave);
+    sq += lane_partner<true>(sq);
+    sp += lane_partner<true>(sp);
+    sq += lane_partner<false>(sq);
+    sp += lane_partner<false>(sp);
     float2* dst =
         ((lane >> 4) == 0 && s.active) ? rpart + (size_t)s.ng * ldn + part_pos(t, c) : junk;
     *dst = make_float2(sq, sp);
@@ -552,8 +552,8 @@ struct AcceptEpi {
         const float pd = shifted_exp(zd, s.bd), pt = shifted_exp(zt16[idx], s.bt);
         sm += idx < nv ? fminf(pd, pt) : 0.0f;
       }
-    sm += __shfl_xor(sm, 16, kWave);
-    sm += __shfl_xor(sm, 32, kWave);
+    sm += lane_partner<true>(sm);
+    sm += lane_partner<false>(sm);
     float* dst = ((lane >> 4) == 0 && s.active) ? cpart + (size_t)s.ng * ldn + part_pos(t, c) : junk;
     *dst = sm;
   }

@@ -95,6 +95,17 @@ typedef enum {
   DSPARK_SCHED_FIXED = 2   /* K given by the caller                              */
 } dspark_sched_mode;
 
+/* Which kernels dspark_markov_draft and dspark_markov_draft_confidence use
+ * (dspark_set_draft_path). */
+typedef enum {
+  DSPARK_DRAFT_AUTO = 0,     /* the library's choice: the faster of the two
+                                measured on MI355X for the shape             */
+  DSPARK_DRAFT_PER_SLOT = 1, /* always the per-slot GEMM + select launches   */
+  DSPARK_DRAFT_RESIDENT = 2  /* the resident-W2 block kernel where the shape
+                                allows it (see dspark_markov_draft), else
+                                per-slot launches                            */
+} dspark_draft_path;
+
 /* Selector for dspark_workspace_bytes. */
 typedef enum {
   DSPARK_CALL_MARKOV_DRAFT = 0,
@@ -123,6 +134,20 @@ size_t dspark_workspace_bytes(int call, int R, int gamma, int V, int r);
  * memset, so it may be captured in a graph). DSPARK_EINVAL for a null ws,
  * DSPARK_EHIP if the launch fails. */
 int dspark_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Device offset, in bytes, of the error word of a draft workspace for R and V:
+ * a uint32 that a resident draft sets to 1 when one of its barrier waits ran
+ * out (see dspark_markov_draft); 0 otherwise. dspark_workspace_init clears it.
+ * Returns 0 for invalid sizes. */
+size_t dspark_workspace_status_offset(int R, int V);
+
+/* Process-wide choice of draft kernels (dspark_draft_path; default AUTO).
+ * Both give outputs within the same tolerance of the definition; they are
+ * not bit-identical (their partial sums merge in different orders). For
+ * tests and measurement. Returns the previous choice, or DSPARK_EINVAL for
+ * an unknown value (the choice is then unchanged). Not thread-safe against
+ * concurrent draft calls. */
+int dspark_set_draft_path(int path);
 
 /* Bytes of the pre-packed W2 buffer for rank r, vocabulary V and dtype. */
 size_t dspark_prepacked_w2_bytes(int r, int V, int dtype);
@@ -168,7 +193,19 @@ int dspark_cost_table_prepare(const double* raw_step_time_s, int M_max, const in
  *   lse_draft[R, gamma] f32    out: log-sum-exp of the slot's draft logits
  *   ws       workspace of dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, ...)
  * Sampling: inverse CDF over ascending ids with a strict comparison,
- * x = min{v : C_v > u S}, on the draft uniform of slot k. */
+ * x = min{v : C_v > u S}, on the draft uniform of slot k.
+ *
+ * Kernels (dspark_set_draft_path). Per slot: two launches, the GEMM pass
+ * with the softmax partials and the draw. Resident: for bfloat16 with
+ * 224 < r <= 256 (r a multiple of 8), R <= 256, V a multiple of 8, at most 10
+ * vocabulary tiles of 64 per compute unit and 16-byte aligned U and W1, the
+ * whole block is one launch with W2 held on chip for all gamma slots (one
+ * workgroup per compute unit, grid-wide waits between a slot's products and
+ * its draws); other shapes fall back to per-slot launches. A resident call
+ * must not overlap another resident draft on the same device (their
+ * workgroups would wait on each other); a wait that runs out sets an error
+ * word in the workspace (dspark_workspace_status_offset) and the call
+ * finishes with undefined outputs. */
 int dspark_markov_draft(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
                         uint64_t seed, uint64_t step, const uint64_t* step_dev,
                         const uint32_t* req_ids, int R, int gamma,

@@ -31,10 +31,24 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
+
+
+def test_draft_path_switch_and_status_offset():
+    dv, lib = _lib()
+    prev = lib.dspark_set_draft_path(dv.DRAFT_PER_SLOT)
+    assert prev == dv.DRAFT_AUTO
+    assert lib.dspark_set_draft_path(7) == -1            # unknown value: DSPARK_EINVAL
+    assert lib.dspark_set_draft_path(dv.DRAFT_RESIDENT) == dv.DRAFT_PER_SLOT
+    assert lib.dspark_set_draft_path(dv.DRAFT_AUTO) == dv.DRAFT_RESIDENT
+    R, V = 64, 151936
+    off = lib.dspark_workspace_status_offset(R, V)
+    ws = dv.workspace_bytes(dv.CALL_MARKOV_DRAFT, R, 7, V, 256)
+    assert 0 < off and off % 256 == 0 and off + 4 <= ws
+    assert lib.dspark_workspace_status_offset(0, V) == 0
 
 
 def test_status_strings():
