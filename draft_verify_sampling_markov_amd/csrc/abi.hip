@@ -53,5 +53,5 @@ extern "C" int dspark_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 
 extern "C" size_t dspark_workspace_status_offset(int R, int V) {
   if (R < 1 || R > kMaxRows || V < 1) return 0;
-  return resident_bar_offset(R, V) + 10 * 256;  // the error word of the barrier block
+  return resident_bar_offset(R, V) + kResidentErrByte;  // the resident kernel's error word
 }

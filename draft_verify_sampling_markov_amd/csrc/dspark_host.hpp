@@ -84,9 +84,10 @@ inline int check_sizes(int R, int gamma, int V, int r, int dt) {
 
 // Workspace layout pieces (bytes, 256-aligned).
 size_t markov_ws_bytes(int R, int V);
-// Barrier block of a draft workspace (resident-W2 kernel): 11 words, each on
-// its own 256-byte line.
-constexpr size_t kResidentBarBytes = 11 * 256;
+// Hand-off block of a draft workspace (resident-W2 kernel): call epoch, exit
+// counter and error word, per-unit ready words and per-request tagged tokens.
+constexpr size_t kResidentBarBytes = 4096;
+constexpr size_t kResidentErrByte = 512;  // the error word's offset in the block
 size_t resident_bar_offset(int R, int V);
 
 // The resident-W2 draft (resident.hip): whether a call of these sizes,

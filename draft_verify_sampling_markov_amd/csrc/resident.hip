@@ -22,24 +22,31 @@
 //           matrix cores, U_k is added, and each (request, tile) forms its
 //           softmax partial (max, sum of exp), kept in LDS until the phase
 //           ends and then written out at once;
-//   barrier every compute unit's partials are complete;
+//   hand-off each compute unit marks its partials ready (a per-unit word);
 //   select  request n on workgroup n mod G: merge the request's partials,
 //           draw u S with the slot's Philox uniform, find the crossing tile,
 //           recompute it (its W2 tile staged through LDS) with the same
 //           matrix-core order, finish the inverse-CDF search;
-//   barrier every token x_k is written (the next slot gathers W1[x_k]).
+//   hand-off the token goes out with the slot's tag in one word, which the
+//           next slot's staging waits on before it gathers W1[x_k].
 //
 // After the last slot, each workgroup scores its own requests with the
 // confidence head (slot k needs only x_{k-1}, which it drew itself).
 //
 // The U_k loads run two block-steps ahead of the products and continue
 // across phases and slots. Data that one compute unit writes and another
-// reads within the launch (partials, tokens) goes through agent-scope
-// accesses, which reach the point of coherence across the XCDs' L2 caches
-// without a whole-cache write-back. The grid barrier counts arrivals per
-// workgroup group and then once per group; every wait is bounded, and a wait
-// that runs out sets an error word in the workspace and lets the launch
-// finish.
+// reads within the launch (partials, ready words, tagged tokens) goes through
+// agent-scope accesses, which reach the point of coherence across the XCDs'
+// L2 caches without a whole-cache write-back. Instead of grid-wide barriers,
+// each reader polls just the words it needs: select thread p waits for unit
+// p's ready word and then reads unit p's partials; staging thread n waits for
+// request n's tagged token. Tags are epoch * 32 + slot, with a per-call
+// epoch the last workgroup advances, so a word left by an earlier slot or
+// call never satisfies a wait and nothing needs clearing between calls. No
+// buffer is rewritten while a reader may still need it: a unit rewrites
+// request n's partials only after it has seen request n's next token, which
+// its select writes after reading them. Every wait is bounded; a wait that
+// runs out sets an error word in the workspace and lets the launch finish.
 #include "dspark_device.hpp"
 #include "dspark_host.hpp"
 
@@ -61,7 +68,7 @@ constexpr int kResLdsTiles = 2;              // W2 tiles in LDS (when a unit nee
 constexpr int kResPhaseReq = 128;            // requests whose W1 rows one phase stages
 constexpr int kResLdw = kResKC * kChunkK + kLdsPad;  // staged row stride (elements)
 constexpr int kResCMax = 10;                 // tiles per unit, and per select thread
-constexpr int kSpinLimit = 1 << 17;          // polls before a barrier wait gives up
+constexpr int kSpinLimit = 1 << 17;          // polls before a wait gives up
 
 constexpr size_t kResTileBytes = (size_t)kResTileFrags * sizeof(Frag);
 constexpr size_t kResStageBytes = (size_t)kResPhaseReq * kResLdw * sizeof(uint16_t);
@@ -105,58 +112,46 @@ __device__ __forceinline__ unsigned ld_coh(const unsigned* p) {
 
 }  // namespace
 
-// Barrier words in the draft workspace, 64 words (256 bytes) apart: arrival
-// counters of the eight workgroup groups (b mod 8), the group counter, the
-// exit counter and the error word. Zero at rest: the last workgroup to leave
-// a launch puts the counters back (the error word stays set until the
-// workspace is initialised again).
-constexpr int kBarGroups = 8;
-constexpr int kBarStride = 64;
-constexpr int kBarAll = kBarGroups * kBarStride;
-constexpr int kBarDone = kBarAll + kBarStride;
-constexpr int kBarErr = kBarDone + kBarStride;
-static_assert((size_t)(kBarErr + kBarStride) * 4 == kResidentBarBytes, "barrier block size");
+// Hand-off words in the draft workspace (byte offsets in its resident block):
+// the call epoch, the exit counter and the error word on lines of their own,
+// then one ready word per unit (up to 256) and one tagged token word per
+// request (up to 256: token in the low half, tag in the high half).
+constexpr int kHoEpoch = 0, kHoDone = 64, kHoErr = 128;   // words
+constexpr int kHoReady = 192;                              // words, 256 of them
+constexpr size_t kHoTokByte = 2048;                        // 8-byte words, 256 of them
+static_assert(kHoTokByte + 256 * 8 == kResidentBarBytes, "hand-off block size");
+static_assert(kHoErr * 4 == kResidentErrByte, "error word offset");
 
 namespace {
 
-// Every workgroup's earlier stores are visible (agent scope) to every
-// workgroup once this returns. gen counts the launch's barriers from 1.
-__device__ __forceinline__ void grid_sync(unsigned* bar, unsigned gen) {
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int G = gridDim.x, x = blockIdx.x % kBarGroups;
-    const unsigned gx = G / kBarGroups + (x < G % kBarGroups ? 1u : 0u);
-    const unsigned ngroups = G < kBarGroups ? (unsigned)G : (unsigned)kBarGroups;
-    const unsigned old = __hip_atomic_fetch_add(bar + x * kBarStride, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1u == gen * gx)  // the group's last arrival announces the group
-      __hip_atomic_fetch_add(bar + kBarAll, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int spins = 0;
-    while (ld_coh(bar + kBarAll) < gen * ngroups) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(bar + kBarErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
+// The bounded wait: poll *p (agent scope) until it is at least `want`.
+__device__ __forceinline__ unsigned wait_at_least(const unsigned* p, unsigned want, unsigned* err) {
+  unsigned v = ld_coh(p);
+  int spins = 0;
+  while (v < want) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
+    v = ld_coh(p);
   }
-  __syncthreads();
+  return v;
 }
-
-// After the launch's last barrier: the last workgroup through puts the
-// counters back to zero (no workgroup reads them any more).
-__device__ __forceinline__ void grid_release(unsigned* bar) {
-  if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(bar + kBarDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1u == gridDim.x) {
-      for (int x = 0; x < kBarGroups; ++x)
-        __hip_atomic_store(bar + x * kBarStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(bar + kBarAll, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(bar + kBarDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned long long wait_tag(const unsigned long long* p, unsigned want,
+                                                       unsigned* err) {
+  unsigned long long v =
+      __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int spins = 0;
+  while ((unsigned)(v >> 32) < want) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  return v;
 }
 
 }  // namespace
@@ -301,6 +296,12 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
   const int lo = (int)((long long)n_t * cu / G), hi = (int)((long long)n_t * (cu + 1) / G);
   const uint64_t stp = a.step.get();
   const Frag* w2f = reinterpret_cast<const Frag*>(a.W2p);
+  unsigned* const ho = a.bar;  // hand-off words
+  unsigned* const ready = ho + kHoReady;
+  unsigned long long* const tok_tag =
+      reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ho) + kHoTokByte);
+  unsigned* const err = ho + kHoErr;
+  const unsigned tag0 = ld_coh(ho + kHoEpoch) * 32u;  // slot k's tag: tag0 + k
 
   // ---- resident W2: tile lo + wave in registers, LT tiles in LDS ----
   const int t_own = lo + wave;
@@ -407,7 +408,6 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
   issue(0, pa);
   issue(1, pb);
   long long s_next = 2;  // the step the next issue() fetches
-  unsigned gen = 0;
   const int nph = (R + kResPhaseReq - 1) / kResPhaseReq;
 
   for (int k = 1; k <= gamma; ++k) {
@@ -421,7 +421,8 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
       // few lines, which bypass the L2) and shared through LDS.
       if (tid < kResPhaseReq) {
         const int n = base + min(tid, count - 1);
-        s_tok[tid] = clamp_token(k == 1 ? a.anchor[n] : ld_coh(a.tokens + (size_t)n * gamma + k - 2), V);
+        const int x = k == 1 ? a.anchor[n] : (int)(unsigned)wait_tag(tok_tag + n, tag0 + k - 1, err);
+        s_tok[tid] = clamp_token(x, V);
       }
       __syncthreads();
       constexpr int kVecRow = kResKC * kChunkK / 8;  // 32 16-byte pieces per row
@@ -471,7 +472,10 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
                lds_p[i * kResPhaseReq + nloc]);
       }
     }
-    grid_sync(a.bar, ++gen);
+    // this unit's partials of slot k are out: mark them ready
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(ready + cu, tag0 + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     issue(s_next++, pa);  // the next slot's first steps (clamped after the last slot)
     issue(s_next++, pb);
 
@@ -482,10 +486,14 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
       const int pu = min(tid, G - 1);
       const int t0 = (int)((long long)n_t * pu / G);
       const int cnt = tid < G ? (int)((long long)n_t * (pu + 1) / G) - t0 : 0;
+      wait_at_least(ready + pu, tag0 + k, err);  // unit pu's partials of slot k
       float2 pv[kResCMax];
 #pragma unroll
       for (int i = 0; i < kResCMax; ++i) pv[i] = ld_coh(prow + min(i, a.c - 1) * kSelThreads + pu);
-      const int xp = clamp_token(k == 1 ? a.anchor[n] : ld_coh(a.tokens + (size_t)n * gamma + k - 2), V);
+      const int xp = clamp_token(
+          k == 1 ? a.anchor[n]
+                 : (int)(unsigned)__hip_atomic_load(tok_tag + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+          V);
       Frag bsel[kResKC];
       load_b_row<true, kResKC, true>(a.W1 + (size_t)xp * r, r, lane, bsel);
       const float u = slot_uniform(a.seed, stp, a.req_ids[n], k, kPurposeDraft);
@@ -521,16 +529,28 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
         const float esel = readlane_f(e, sel);
         if (lane == 0) {
           const size_t o = (size_t)n * gamma + k - 1;
-          st_coh(a.tokens + o, t * kTileV + sel);
+          const int x = t * kTileV + sel;
+          __hip_atomic_store(tok_tag + n,
+                             ((unsigned long long)(tag0 + k) << 32) | (unsigned)x,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          st_coh(a.tokens + o, x);  // the confidence head reads it back at agent scope
           a.p_draft[o] = esel / ws.S;
           a.lse_draft[o] = m + __logf(ws.S);
         }
       }
       __syncthreads();  // the LDS tile is reused by the next request or slot
     }
-    if (k < gamma) grid_sync(a.bar, ++gen);
   }
-  grid_release(a.bar);
+  // the last workgroup out advances the call epoch (every workgroup has read
+  // it at its start)
+  if (tid == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(ho + kHoDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == (unsigned)G) {
+      __hip_atomic_store(ho + kHoDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(ho + kHoEpoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   // ================= confidence head =================
   // c_k = sigmoid(z inv_temp_k), z = w . [h_k ; W1[x_{k-1}]] + b, and the
@@ -542,7 +562,7 @@ __global__ __launch_bounds__(kResThreads) void resident_draft_kernel(ResArgs a) 
     for (int n = cu; n < R; n += G) {  // workgroup-uniform
       for (int k = 1 + wave; k <= gamma; k += kResWaves) {
         const size_t o = (size_t)n * gamma + k - 1;
-        const int xp = clamp_token(k == 1 ? a.anchor[n] : ld_coh(a.tokens + o - 1), V);
+        const int xp = clamp_token(k == 1 ? a.anchor[n] : ld_coh(a.tokens + o - 1), V);  // drawn here
         float z = conf_logit<true>(static_cast<const uint16_t*>(a.ca.h) + o * a.ca.d,
                                    a.W1 + (size_t)xp * r, a.ca.w, a.ca.b, a.ca.d, r, a.ca.vec_h,
                                    a.ca.vec_w1, lane);
@@ -612,7 +632,7 @@ bool resident_draft_eligible(const void* U, const void* W1, int R, int gamma, in
   if (!rows_vec_ok(U, (long long)gamma * V, V, 8) || !w1_vec_ok(W1, r)) return false;
   if (part_chunk(V) > kResCMax) return false;
   const int G = device_cu_count();
-  if (G < kBarGroups || G > kSelThreads) return false;
+  if (G > kSelThreads) return false;
   const int LT = res_lds_tiles(V, G);
   if (LT < 0) return false;
   // a unit's tiles sit at [i * 256 + unit] of a request's partial row
