@@ -9,12 +9,18 @@ part of the chain; its output (the packed target logits) is prepared once
 before timing -- every timed step processes the same batch, so the schedule
 and pack are the same each step, and this is checked after timing.
 
-Prints one JSON line: the metric (verified draft slots per second), the
-roofline of the dominant kernel (the per-slot bias GEMM + softmax-partials
-pass, timed with HIP events on the chain's stream), and the CPU oracle timed
-on a bounded sample of the same workload on this host.
+The headline workload is the largest one: mixed traffic (R = 256, gamma = 7,
+V = 151936) in cap-accept verify, every block verified whole (1792 verified
+draft slots per step). Prints one JSON line: the metric (verified draft
+slots per second over exactly --steps steps), per-step statistics over
+individually timed steps (median, p10, p90; warm and after a 512 MiB cache
+flush), the roofline of the dominant kernel (the per-slot bias GEMM +
+softmax-partials pass, timed with HIP events on the chain's stream) with its
+algorithmic bytes counting W2 once per block, the same figures for the other
+named workloads, and the CPU oracle timed on a bounded sample of the headline
+workload on this host.
 
-    python bench.py [--steps K] [--warmup W] [--config qwen3] [--mode static]
+    python bench.py [--steps K] [--warmup W] [--config mixed] [--mode cap_accept]
 """
 from __future__ import annotations
 
@@ -53,13 +59,11 @@ PMC_SOURCES = ("draft_verify_sampling_markov_amd/csrc/markov.hip",
                "draft_verify_sampling_markov_amd/csrc/dspark_device.hpp")
 
 
-def measured_traffic(config_name: str):
-    """HBM bytes per launch of the draft GEMM kernel from the committed rocprofv3
-    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a 256 MiB copy), or
-    None when no summary exists for this workload or the kernel's sources have
-    changed since the counters were taken."""
+def _pmc_fields(config_name: str):
+    """The key: value lines of the committed counter summary of the draft GEMM
+    kernel for this workload, or None (no summary, or sources changed since)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"markov_partials_{config_name}_static_pmc.md")
+    path = os.path.join(ROOT, "profiles", f"markov_partials_{config_name}_pmc.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -71,39 +75,69 @@ def measured_traffic(config_name: str):
     for f in PMC_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+    if fields.get("source_sha256") != h.hexdigest():
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return fields
 
 
-def cpu_baseline(spec, inp, mode_name: str, budget_s: float = 12.0, n_req: int = 8):
-    """The oracle as it stands, on the first n_req requests of the workload."""
+def measured_traffic(config_name: str):
+    """HBM bytes per launch of the draft GEMM kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a 256 MiB copy), or
+    None when no summary exists for this workload or the kernel's sources have
+    changed since the counters were taken."""
+    f = _pmc_fields(config_name)
+    if f is None or "traffic_bytes_per_launch" not in f:
+        return None
+    return int(f["traffic_bytes_per_launch"])
+
+
+def measured_mfma_busy(config_name: str):
+    """Matrix-core busy fraction of the draft GEMM kernel from the same counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES over the kernel's SIMD cycles), or None."""
+    f = _pmc_fields(config_name)
+    if f is None or "mfma_busy_frac" not in f:
+        return None
+    return float(f["mfma_busy_frac"])
+
+
+def cpu_baseline(spec, inp, mode_name: str, n_req: int = 8, runs: int = 3, target_s: float = 3.5):
+    """The oracle as it stands, on the first n requests of the workload: one
+    sizing step on n_req requests, n scaled so that a step takes about
+    target_s seconds (at most R), then `runs` timed chain steps, the median
+    reported (about 10 s of CPU work in all)."""
     import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    n = min(n_req, spec.R)
-    sub = {k: inp[k][:n] for k in ("U", "target", "h", "anchor", "req_ids")}
-    sub.update({k: inp[k] for k in ("W1", "W2", "w", "b", "raw_T")})
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
     vmode = {"static": oracle.VERIFY_STATIC, "compact": oracle.VERIFY_COMPACT,
              "cap_accept": oracle.VERIFY_CAP_ACCEPT}[mode_name]
-    slots, reps = 0, 0
-    t0 = time.perf_counter()
-    while True:
+
+    def step(n):
+        sub = {k: inp[k][:n] for k in ("U", "target", "h", "anchor", "req_ids")}
+        sub.update({k: inp[k] for k in ("W1", "W2", "w", "b", "raw_T")})
+        t0 = time.perf_counter()
         out = oracle.chain(sub, tiers=spec.tiers, staircase=spec.staircase,
                            B_cap=min(spec.budgets[0], n * spec.gamma), verify_mode=vmode)
-        reps += 1
-        slots += n * spec.gamma if vmode != oracle.VERIFY_COMPACT else int(out["sched"]["K"])
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": slots / dt, "unit": "slots/s", "cores": int(threads), "kind": "oracle",
+        dt = time.perf_counter() - t0
+        return dt, (n * spec.gamma if vmode != oracle.VERIFY_COMPACT else int(out["sched"]["K"]))
+
+    n = min(n_req, spec.R)
+    t_size, _ = step(n)
+    n = int(min(spec.R, max(n, round(n * target_s / max(t_size, 1e-3)))))
+    times, slots = [], 0
+    for _ in range(runs):
+        dt, slots = step(n)
+        times.append(dt)
+    dt = float(np.median(times))
+    return {"value": slots / dt, "unit": "slots/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of {spec.R} requests of the {spec.name} workload, full "
-                      f"vocabulary V={spec.V}, {mode_name} verify; {reps} oracle chain steps in "
-                      f"{dt:.1f} s (float64 numpy, BLAS threads={threads})"}
+                      f"vocabulary V={spec.V}, {mode_name} verify; median of {runs} oracle chain "
+                      f"steps ({', '.join(f'{t:.1f}' for t in times)} s; float64 numpy, "
+                      f"{cores} cores in the affinity mask, BLAS threads={blas})"}
 
 
 def measure_decode(dv, dev, inp, spec, B_cap: int, steps: int, lag: int):
@@ -287,17 +321,254 @@ def measure_shards(dv, dev, spec, G: int, reps: int):
     return out
 
 
+def _spec_bytes(spec):
+    return 2 if spec.dtype == "bf16" else 4
+
+
+def draft_algorithmic(spec):
+    """The Markov draft's algorithmic work per step: U_k streamed for every
+    slot, W2 once per block, the gathered W1 rows per slot (bytes); the bias
+    GEMM's 2 R r V flops per slot."""
+    b = _spec_bytes(spec)
+    R, g, V, r = spec.R, spec.gamma, spec.V, spec.r
+    return {"bytes": g * R * V * b + r * V * b + g * R * r * b, "flops": 2 * g * R * r * V}
+
+
+def _stats(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
+def measure_chain(dv, spec, mode_name: str, B_cap: int, *, steps: int, warmup: int, samples: int,
+                  cold_samples: int, profile_steps: int, stages: bool = True,
+                  resident_compare: bool = True):
+    """One workload: the whole-chain step time (exactly `steps` steps, eager
+    launches and replays of one captured graph; the faster counts), per-step
+    statistics over `samples` individually timed replays (warm) and
+    `cold_samples` replays each after a 512 MiB write that evicts the caches,
+    per-stage event times, and the roofline of the dominant kernel."""
+    import numpy as np
+    import torch
+    import synth
+    mode = dv.VERIFY_MODES[mode_name]
+    t0 = time.time()
+    inp = synth.generate(spec)
+    log(f"[bench] generated {spec.name} inputs in {time.time() - t0:.1f} s")
+    dev = {k: to_dev(inp[k]) for k in ("U", "W1", "W2", "target", "h", "anchor", "w", "req_ids")}
+    sps = dv.cost_table_prepare(inp["raw_T"], spec.tiers, spec.staircase)
+    dev["sps_milli"] = to_dev(sps)
+    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B_cap, verify_mode=mode)
+
+    # one step with the target stand-in, to lay out the packed target rows
+    ch.run(gather=True)
+    torch.cuda.synchronize()
+    first = ch.results()
+    if first["totals"][1] < 0:
+        raise RuntimeError(f"packed total {first['totals'][0]} exceeds every tier")
+    K_sel = int(first["K"][0])
+    slots_per_step = spec.R * spec.gamma if mode != dv.VERIFY_COMPACT else K_sel
+
+    for _ in range(warmup):
+        ch.run(gather=False)
+    torch.cuda.synchronize()
+
+    # ---- timed region 1: exactly `steps` steps, eager launches ----
+    t_e = time.perf_counter()
+    for _ in range(steps):
+        ch.run(gather=False)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t_e) * 1e3 / steps
+
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_graph):
+        ch.run(gather=False)
+    step_graph.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region 2: exactly `steps` steps, graph replays ----
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step_graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t_start) * 1e3 / steps
+    use_graph = graph_ms <= eager_ms
+    ms_per_step = graph_ms if use_graph else eager_ms
+
+    # per-step statistics: individually timed replays, warm and cache-cold
+    def replay_times(n, flush=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i, (e0, e1) in enumerate(ev):
+            if flush is not None:
+                flush.fill_(i & 255)
+            e0.record()
+            step_graph.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    warm = replay_times(samples)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = replay_times(cold_samples, flush)
+    del flush
+    after = ch.results()
+    for key in ("win_len", "cu_seqlens", "totals", "tokens", "p_draft", "accept_len", "out_tokens"):
+        if not np.array_equal(first[key], after[key]):
+            raise RuntimeError(f"{key} changed between steps: the pre-laid target rows are stale")
+    value = slots_per_step / (ms_per_step * 1e-3)
+    log(f"[bench] {spec.name}/{mode_name}: {steps} steps, graph replays {graph_ms:.4f} ms/step, "
+        f"eager {eager_ms:.4f} ms/step; warm median {np.median(warm):.4f}, cache-cold median "
+        f"{np.median(cold):.4f} ms")
+    out = {"value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
+           "graph_ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(eager_ms, 4),
+           "step_timing": ("replays of one captured HIP graph of the whole step" if use_graph else
+                           "eager launches of the whole step (faster than graph replays here)"),
+           "step_ms": _stats(warm), "step_ms_cache_cold": _stats(cold),
+           "cache_flush_bytes": 512 << 20,
+           "slots_per_step": slots_per_step, "packed_total": int(first["totals"][0]),
+           "tier": int(first["totals"][1]),
+           "accepted_tokens_per_s": round(float(first["n_out"].sum()) / (ms_per_step * 1e-3), 1),
+           "mean_accept_len": round(float(first["accept_len"].mean()), 3)}
+
+    # ---- per-stage event timing on the chain's stream ----
+    P = profile_steps
+    g = spec.gamma
+    if stages:
+        stage_names = ["draft", "confidence", "schedule", "pack", "verify"]
+        st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
+                 for _ in range(P)]
+        for s in range(P):
+            ev = st_ev[s]
+            ev[0].record()
+            ch.draft_split()
+            ev[1].record()
+            ch.confidence()
+            ev[2].record()
+            ch.schedule()
+            ev[3].record()
+            ch.pack()
+            ev[4].record()
+            ch.verify()
+            ev[5].record()
+        torch.cuda.synchronize()
+        out["stages_ms"] = {n: round(float(np.mean([st_ev[s][i].elapsed_time(st_ev[s][i + 1])
+                                                     for s in range(P)])), 4)
+                            for i, n in enumerate(stage_names)}
+        prof = ch.results()
+        if not np.array_equal(prof["tokens"], first["tokens"]):
+            raise RuntimeError("the per-slot draft differs from the draft call")
+
+    # ---- the draft call alone, per kernel choice (graph of one call) ----
+    def draft_call_ms(reps):
+        ch.draft_confidence()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            ch.draft_confidence()
+        gr.replay()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            gr.replay()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / reps
+
+    alg = draft_algorithmic(spec)
+    drafts = {"per_slot_ms": round(draft_call_ms(P), 4)}
+    if resident_compare:
+        prev = dv.set_draft_path(dv.DRAFT_RESIDENT)
+        try:
+            drafts["resident_ms"] = round(draft_call_ms(P), 4)
+            drafts["resident_status"] = dv.draft_status(ch.ws_draft, spec.R, spec.V)
+        finally:
+            dv.set_draft_path(prev)
+    for k_ in [k_ for k_ in drafts if k_.endswith("_ms")]:
+        drafts[k_.replace("_ms", "_gbs")] = round(alg["bytes"] / (drafts[k_] * 1e-3) / 1e9, 1)
+    drafts["algorithmic_bytes_per_step"] = alg["bytes"]
+    drafts["note"] = ("whole draft call (gamma slots, draws, confidence head), graph-replayed; "
+                      "GB/s = the draft's algorithmic bytes (W2 once per block) / call time")
+    out["draft_call"] = drafts
+
+    # ---- the dominant kernel: replays of a graph of 4 gamma GEMM launches
+    # (slot k = 1..gamma in turn, its own U_k and previous tokens), each on a
+    # workspace of its own whose tile-queue counters are put back to zero
+    # between replays, outside the timed intervals (in the chain the select
+    # does that) ----
+    n_gemm = 4 * g
+    wss = [dv.new_workspace(dv.CALL_MARKOV_DRAFT, spec.R, g, spec.V, spec.r, dev["U"].device)
+           for _ in range(n_gemm)]
+    Uf, tf = dev["U"].view(-1), ch.draft_out[0].view(-1)
+
+    def gemm_launches():
+        for j in range(n_gemm):
+            k = 1 + j % g
+            x_prev, xs = (ch.anchor, 1) if k == 1 else (tf[k - 2:], g)
+            dv.markov_partials(Uf[(k - 1) * spec.V:], g * spec.V, dev["W1"], ch.W2p, x_prev, xs,
+                               R=spec.R, V=spec.V, r=spec.r, part=wss[j])
+
+    gemm_launches()
+    gr = torch.cuda.CUDAGraph()
+    for w_ in wss:
+        dv.workspace_init(w_)
+    with torch.cuda.graph(gr):
+        gemm_launches()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(P)]
+    for e0, e1 in ev:
+        for w_ in wss:
+            dv.workspace_init(w_)
+        e0.record()
+        gr.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / (P * n_gemm)
+    del wss
+
+    b = _spec_bytes(spec)
+    R, V, r = spec.R, spec.V, spec.r
+    bytes_per_launch = alg["bytes"] / g           # W2 once per block, spread over the gamma launches
+    flops_per_launch = alg["flops"] / g
+    achieved_gbs = bytes_per_launch / (gemm_ms * 1e-3) / 1e9
+    achieved_tfs = flops_per_launch / (gemm_ms * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFS
+    traffic = measured_traffic(f"{spec.name}_{mode_name}")
+    busy = measured_mfma_busy(f"{spec.name}_{mode_name}")
+    out["roofline"] = {
+        "kernel": "markov_partials_kernel (per-slot bias GEMM + U add + softmax partials)",
+        "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "traffic_over_algorithmic": None if traffic is None else round(traffic / bytes_per_launch, 3),
+        "algorithmic_bytes_per_launch": int(round(bytes_per_launch)),
+        "algorithmic_bytes": "gamma R V b + r V b + gamma R r b per step (U_k every slot, W2 once "
+                             "per block, W1 rows every slot), divided over the gamma launches",
+        "avg_launch_us": round(gemm_ms * 1e3, 2),
+        "timing": "HIP events around replays of a graph of 4 gamma GEMM launches",
+        "launches_timed": P * n_gemm,
+        "mfma": {"achieved": round(achieved_tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                 "frac": round(achieved_tfs / mfma_peak, 4), "flops_per_launch": int(flops_per_launch),
+                 "busy_frac_counter": busy}}
+    return out, inp, dev
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="qwen3")
-    ap.add_argument("--mode", default="static", choices=["static", "compact", "cap_accept"])
+    ap.add_argument("--config", default="mixed")
+    ap.add_argument("--mode", default="cap_accept", choices=["static", "compact", "cap_accept"])
     ap.add_argument("--budget", type=int, default=None, help="cap B on selected slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-steps", type=int, default=None,
-                    help="steps of per-kernel event timing (default: --steps)")
+    ap.add_argument("--samples", type=int, default=50,
+                    help="individually timed steps for the median / p10 / p90")
+    ap.add_argument("--cold-samples", type=int, default=20,
+                    help="individually timed steps, each after a 512 MiB cache-evicting write")
+    ap.add_argument("--profile-steps", type=int, default=10,
+                    help="steps of per-stage and per-kernel event timing")
+    ap.add_argument("--other-configs", default="tiny:static,qwen3:static,dsv4:compact,long:compact",
+                    help="workload:mode list measured after the headline ('' skips)")
     ap.add_argument("--decode-steps", type=int, default=20,
                     help="steps of the multi-step decode loop (compact verify, budget from "
                          "survivals --lag steps old) timed eagerly and as graph replays; 0 skips")
@@ -317,7 +588,6 @@ def main() -> int:
               f"multi-GPU path (its sharding is a design only).", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     import synth
     import draft_verify_sampling_markov_amd as dv
@@ -327,195 +597,37 @@ def main() -> int:
         return 1
     dv.load_library()
     spec = synth.CONFIGS[args.config]
-    mode = dv.VERIFY_MODES[args.mode]
     B_cap = spec.budgets[0] if args.budget is None else args.budget
-    t0 = time.time()
-    inp = synth.generate(spec)
-    log(f"[bench] generated {spec.name} inputs in {time.time() - t0:.1f} s")
-    dev = {k: to_dev(inp[k]) for k in ("U", "W1", "W2", "target", "h", "anchor", "w", "req_ids")}
-    sps = dv.cost_table_prepare(inp["raw_T"], spec.tiers, spec.staircase)
-    dev["sps_milli"] = to_dev(sps)
-    ch = dv.Chain(dev, b=float(inp["b"]), tiers=spec.tiers, B_cap=B_cap, verify_mode=mode)
-
-    # one step with the target stand-in, to lay out the packed target rows
-    ch.run(gather=True)
-    torch.cuda.synchronize()
-    first = ch.results()
-    if first["totals"][1] < 0:
-        log(f"[bench] packed total {first['totals'][0]} exceeds every tier: failed workload")
+    try:
+        head, inp, dev = measure_chain(dv, spec, args.mode, B_cap, steps=args.steps,
+                                       warmup=args.warmup, samples=args.samples,
+                                       cold_samples=args.cold_samples,
+                                       profile_steps=args.profile_steps)
+    except RuntimeError as e:
+        log(f"[bench] {e}: failed workload")
         return 1
-    K_sel = int(first["K"][0])
-    slots_per_step = spec.R * spec.gamma if mode != dv.VERIFY_COMPACT else K_sel
-
-    for _ in range(args.warmup):
-        ch.run(gather=False)
-    torch.cuda.synchronize()
-
-    # ---- timed region 1: exactly K steps, eager launches (the ctypes calls of
-    # a step take about as long as its GPU work, so a slow or busy host shows
-    # here as gaps between kernels) ----
-    t_e = time.perf_counter()
-    for _ in range(args.steps):
-        ch.run(gather=False)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t_e) * 1e3 / args.steps
-
-    # the step as a serving loop runs it: one captured HIP graph of the whole
-    # chain (every launch of the step, same buffers), replayed
-    step_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(step_graph):
-        ch.run(gather=False)
-    step_graph.replay()
-    torch.cuda.synchronize()
-
-    # ---- timed region 2: exactly K steps, graph replays ----
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step_graph.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    graph_step_ms = wall * 1e3 / args.steps
-    # the step's throughput is its faster launch mechanism on this host: the
-    # same work either way (both runs time exactly K whole steps)
-    use_graph = graph_step_ms <= eager_ms
-    ms_per_step = graph_step_ms if use_graph else eager_ms
-    after = ch.results()
-    for key in ("win_len", "cu_seqlens", "totals", "tokens", "p_draft", "accept_len", "out_tokens"):
-        if not np.array_equal(first[key], after[key]):
-            log(f"[bench] {key} changed between steps: the pre-laid target rows are stale")
-            return 1
-    value = slots_per_step / (ms_per_step * 1e-3)
-    log(f"[bench] {args.steps} steps: graph replays {graph_step_ms:.4f} ms/step, eager launches "
-        f"{eager_ms:.4f} ms/step -> {ms_per_step:.4f} ms/step")
-
-    # ---- per-kernel / per-stage event timing on the chain's stream ----
-    P = args.profile_steps or args.steps
-    g = spec.gamma
-    gemm_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(g)] for _ in range(P)]
-    stage_names = ["draft", "confidence", "schedule", "pack", "verify"]
-    st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
-             for _ in range(P)]
-    for s in range(P):
-        ev = st_ev[s]
-        ev[0].record()
-        ch.draft_split(gemm_ev[s])
-        ev[1].record()
-        ch.confidence()
-        ev[2].record()
-        ch.schedule()
-        ev[3].record()
-        ch.pack()
-        ev[4].record()
-        ch.verify()
-        ev[5].record()
-    torch.cuda.synchronize()
-    gemm_ms = [a.elapsed_time(b) for row in gemm_ev for (a, b) in row]
-    gemm_avg_ms = float(np.mean(gemm_ms))
-    stages = {n: float(np.mean([st_ev[s][i].elapsed_time(st_ev[s][i + 1]) for s in range(P)]))
-              for i, n in enumerate(stage_names)}
-    prof = ch.results()
-    if not np.array_equal(prof["tokens"], first["tokens"]):
-        log("[bench] the per-slot draft differs from the draft call")
-        return 1
-
-    # ---- the GEMM's duration without per-launch event gaps: replays of a
-    # captured graph of the slot's GEMM launches alone (gamma of them back to
-    # back, each slot's own U_k and previous tokens); for context also the
-    # difference per slot between graphs of the split draft (gamma GEMM +
-    # select pairs) and of its selects alone ----
-    def graph_ms(passes, reps):
-        ch.draft_split(passes=passes)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            ch.draft_split(passes=passes)
-        gr.replay()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record()
-        for _ in range(reps):
-            gr.replay()
-        e[1].record()
-        torch.cuda.synchronize()
-        return e[0].elapsed_time(e[1]) / reps
-
-    pair_ms = graph_ms(("partials", "select"), P)
-    sel_ms = graph_ms(("select",), P)
-    gemm_pair_ms = (pair_ms - sel_ms) / g
-
-    # the GEMM launches alone: one graph of 4 gamma launches (slot k = 1..gamma
-    # in turn, its own U_k and previous tokens), each on a workspace of its own
-    # whose tile-queue counters are put back to zero between replays, outside
-    # the timed intervals (in the chain the select does that)
-    n_gemm = 4 * g
-    wss = [dv.new_workspace(dv.CALL_MARKOV_DRAFT, spec.R, g, spec.V, spec.r, dev["U"].device)
-           for _ in range(n_gemm)]
-    Uf, tf = dev["U"].view(-1), ch.draft_out[0].view(-1)
-
-    def gemm_launches():
-        for j in range(n_gemm):
-            k = 1 + j % g
-            x_prev, xs = (ch.anchor, 1) if k == 1 else (tf[k - 2:], g)
-            dv.markov_partials(Uf[(k - 1) * spec.V:], g * spec.V, dev["W1"], ch.W2p, x_prev, xs,
-                               R=spec.R, V=spec.V, r=spec.r, part=wss[j])
-
-    gemm_launches()
-    gr = torch.cuda.CUDAGraph()
-    for w in wss:
-        dv.workspace_init(w)
-    with torch.cuda.graph(gr):
-        gemm_launches()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(P)]
-    for e0, e1 in ev:
-        for w in wss:
-            dv.workspace_init(w)
-        e0.record()
-        gr.replay()
-        e1.record()
-    torch.cuda.synchronize()
-    gemm_graph_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / (P * n_gemm)
-    del wss
-
-    # ---- roofline of the dominant kernel (one slot's GEMM + softmax partials) ----
-    b = 2 if spec.dtype == "bf16" else 4
-    R, V, r = spec.R, spec.V, spec.r
-    n_t = -(-V // 64)
-    bytes_per_launch = R * V * b + r * V * b + R * r * b + n_t * R * 8
-    flops_per_launch = 2 * R * r * V
-    achieved_gbs = bytes_per_launch / (gemm_graph_ms * 1e-3) / 1e9
-    achieved_tfs = flops_per_launch / (gemm_graph_ms * 1e-3) / 1e12
-    mfma_peak = MFMA_BF16_PEAK_TFS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFS
-    roofline = {"kernel": "markov_partials_kernel (per-slot bias GEMM + U add + softmax partials)",
-                "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(spec.name),
-                "bytes_per_launch": bytes_per_launch,
-                "avg_launch_us": round(gemm_graph_ms * 1e3, 2),
-                "timing": "HIP events around replays of a graph of 4 gamma GEMM launches",
-                "launches_timed": P * n_gemm,
-                "avg_launch_us_pairs_minus_selects": round(gemm_pair_ms * 1e3, 2),
-                "avg_launch_us_event_pairs": round(gemm_avg_ms * 1e3, 2),
-                "mfma": {"achieved": round(achieved_tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
-                         "frac": round(achieved_tfs / mfma_peak, 4), "flops_per_launch": flops_per_launch}}
-
+    R, g, V, r = spec.R, spec.gamma, spec.V, spec.r
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "slots/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "step_timing": ("replays of one captured HIP graph of the whole step" if use_graph else
-                        "eager launches of the whole step (faster than graph replays on this host)"),
-        "graph_ms_per_step": round(graph_step_ms, 4),
-        "eager_ms_per_step": round(eager_ms, 4),
+        "metric": METRIC, "value": head["value"], "unit": "slots/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "step_timing": head["step_timing"],
+        "graph_ms_per_step": head["graph_ms_per_step"], "eager_ms_per_step": head["eager_ms_per_step"],
+        "step_ms": head["step_ms"], "step_ms_cache_cold": head["step_ms_cache_cold"],
+        "cache": ("value and step_ms: inputs resident and re-read every step (the 256 MB "
+                  "Infinity Cache may hold part of them); step_ms_cache_cold: each step after a "
+                  "512 MiB write"),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": spec.dtype, "data": "synthetic",
         "config": {"workload": f"{spec.name}: R={R} gamma={g} V={V} r={r} d={spec.d} {spec.dtype}, "
                                f"{args.mode} verify, B={B_cap}",
                    "R": R, "gamma": g, "V": V, "r": r, "d": spec.d, "mode": args.mode,
-                   "B_cap": B_cap, "verified_slots_per_step": slots_per_step,
-                   "packed_total": int(first["totals"][0]), "tier": int(first["totals"][1])},
-        "accepted_tokens_per_s": round(float(first["n_out"].sum()) / (ms_per_step * 1e-3), 1),
-        "mean_accept_len": round(float(first["accept_len"].mean()), 3),
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
-        "roofline": roofline,
+                   "B_cap": B_cap, "verified_slots_per_step": head["slots_per_step"],
+                   "packed_total": head["packed_total"], "tier": head["tier"]},
+        "accepted_tokens_per_s": head["accepted_tokens_per_s"],
+        "mean_accept_len": head["mean_accept_len"],
+        "stages_ms": head.get("stages_ms"),
+        "draft_call": head["draft_call"],
+        "roofline": head["roofline"],
     }
     if args.decode_steps > 0:
         line["decode"] = measure_decode(dv, dev, inp, spec, B_cap, args.decode_steps, args.lag)
@@ -531,9 +643,38 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         line["calibration_copy_bytes"] = n
+    cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(spec, inp, args.mode)
+        cpu = cpu_baseline(spec, inp, args.mode)
+    del dev, inp
+    torch.cuda.empty_cache()
+
+    others = {}
+    for item in [x for x in args.other_configs.split(",") if x]:
+        name, mode_name = item.split(":")
+        sp = synth.CONFIGS[name]
+        try:
+            o, _, _ = measure_chain(dv, sp, mode_name, sp.budgets[-1], steps=20, warmup=3,
+                                    samples=20, cold_samples=5, profile_steps=5, stages=False)
+        except RuntimeError as e:
+            log(f"[bench] {name}/{mode_name}: {e}")
+            continue
+        rl = o["roofline"]
+        others[f"{name}:{mode_name}"] = {
+            "workload": f"{name}: R={sp.R} gamma={sp.gamma} V={sp.V} r={sp.r} {sp.dtype}, "
+                        f"{mode_name} verify, B={sp.budgets[-1]}",
+            "value": o["value"], "unit": "slots/s", "ms_per_step": o["ms_per_step"],
+            "step_ms": o["step_ms"], "step_ms_cache_cold": o["step_ms_cache_cold"],
+            "slots_per_step": o["slots_per_step"], "draft_call": o["draft_call"],
+            "gemm_roofline": {k: rl[k] for k in ("achieved", "peak", "unit", "frac",
+                                                 "avg_launch_us", "traffic",
+                                                 "traffic_over_algorithmic")},
+            "gemm_mfma_frac": rl["mfma"]["frac"]}
+        torch.cuda.empty_cache()
+    line["other_workloads"] = others
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     return 0
 

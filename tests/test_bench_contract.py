@@ -30,8 +30,10 @@ def test_json_line_contract():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "tiny",
-                        "--steps", "3", "--warmup", "1", "--decode-steps", "2",
-                        "--observe-calls", "1", "--no-cpu-baseline"],
+                        "--mode", "static", "--steps", "3", "--warmup", "1", "--decode-steps", "2",
+                        "--observe-calls", "1", "--no-cpu-baseline", "--samples", "5",
+                        "--cold-samples", "2", "--profile-steps", "2",
+                        "--other-configs", "tiny:compact"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
@@ -51,3 +53,11 @@ def test_json_line_contract():
     assert abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
     assert min(d["graph_ms_per_step"], d["eager_ms_per_step"]) == pytest.approx(d["ms_per_step"],
                                                                                abs=1e-4)
+    # algorithmic bytes count W2 once per block: per launch R V b + r V b / gamma + R r b
+    R, g, V, r, b = 4, 7, 1024, 32, 4
+    assert rl["algorithmic_bytes_per_launch"] == round((g * R * V * b + r * V * b + g * R * r * b) / g)
+    for key in ("step_ms", "step_ms_cache_cold"):
+        st = d[key]
+        assert st["p10"] <= st["median"] <= st["p90"] and st["n"] > 0
+    assert "tiny:compact" in d["other_workloads"]
+    assert d["draft_call"]["per_slot_ms"] > 0
