@@ -43,6 +43,9 @@ _SIGNATURES = {
     "dspark_cost_table_prepare": (_i, [_vp, _i, _vp, _i, _i, _vp]),
     "dspark_markov_draft": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i, _i, _i,
                                  _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dspark_markov_draft_noalloc": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i, _i,
+                                         _i, _vp, _vp, _vp, _vp]),
+    "dspark_noalloc_scratch_bytes": (_sz, []),
     "dspark_confidence": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _vp, _vp]),
     "dspark_markov_draft_confidence": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i,
@@ -257,6 +260,29 @@ def markov_draft(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0, st
         R, gamma, V, r, dt, _dev(tokens, "tokens", torch.int32, (R, gamma)),
         _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
         _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return tokens, p, lse
+
+
+def markov_draft_noalloc(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int = 0,
+                         step_dev=None, req_ids=None, out=None, stream=None):
+    """markov_draft on the library's own device scratch array (no workspace,
+    no allocation in the library). Returns (tokens, p_draft, lse_draft)."""
+    torch = _torch()
+    R, gamma, V = U.shape
+    dev = U.device
+    if req_ids is None:
+        req_ids = torch.arange(R, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (_empty((R, gamma), torch.int32, dev), _empty((R, gamma), torch.float32, dev),
+               _empty((R, gamma), torch.float32, dev))
+    tokens, p, lse = out
+    _check(load_library().dspark_markov_draft_noalloc(
+        _dev(U, "U"), _dev(W1, "W1", U.dtype, (V, r)), _dev(W2p, "W2p", U.dtype),
+        _dev(anchor, "anchor", torch.int32, (R,)), seed, step,
+        _opt(step_dev, "step_dev", torch.int64, (1,)), _dev(req_ids, "req_ids", None, (R,)),
+        R, gamma, V, r, _dtype_code(U), _dev(tokens, "tokens", torch.int32, (R, gamma)),
+        _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
+        _stream(stream)))
     return tokens, p, lse
 
 

@@ -41,14 +41,18 @@ __global__ void workspace_zero_kernel(unsigned char* __restrict__ p, size_t n) {
     p[i] = 0;
 }
 
+int dspark::zero_fill(void* p, size_t n, hipStream_t s) {
+  if (n == 0) return DSPARK_OK;
+  const size_t per_block = 256 * 16;
+  const int grid = (int)std::min<size_t>((n + per_block - 1) / per_block, 4096);
+  hipLaunchKernelGGL(workspace_zero_kernel, dim3(grid), dim3(256), 0, s,
+                     static_cast<unsigned char*>(p), n);
+  return launch_status();
+}
+
 extern "C" int dspark_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws) return DSPARK_EINVAL;
-  if (ws_bytes == 0) return DSPARK_OK;
-  const size_t per_block = 256 * 16;
-  const int grid = (int)std::min<size_t>((ws_bytes + per_block - 1) / per_block, 4096);
-  hipLaunchKernelGGL(workspace_zero_kernel, dim3(grid), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<unsigned char*>(ws), ws_bytes);
-  return launch_status();
+  return zero_fill(ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t dspark_workspace_status_offset(int R, int V) {

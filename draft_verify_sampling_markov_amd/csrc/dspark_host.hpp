@@ -84,6 +84,11 @@ inline int check_sizes(int R, int gamma, int V, int r, int dt) {
 
 // Workspace layout pieces (bytes, 256-aligned).
 size_t markov_ws_bytes(int R, int V);
+// Start of the draft workspace's bookkeeping tail (junk slot, tile-queue
+// counters, draft uniforms, hand-off block); the tile partials lie before it.
+size_t markov_junk_offset(int R, int V);
+// Zero-fill n bytes at p on stream s (the kernel behind dspark_workspace_init).
+int zero_fill(void* p, size_t n, hipStream_t s);
 // Hand-off block of a draft workspace (resident-W2 kernel): call epoch, exit
 // counter and error word, per-unit ready words and per-request tagged tokens.
 constexpr size_t kResidentBarBytes = 4096;
@@ -96,6 +101,11 @@ struct StepArg;
 struct ConfArgs;
 bool resident_draft_eligible(const void* U, const void* W1, int R, int gamma, int V, int r,
                              int dtype);
+// dspark_markov_draft after its argument checks (ws: a draft workspace for R, V).
+int markov_draft_checked(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
+                         uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
+                         int V, int r, int dtype, int32_t* tokens, float* p_draft, float* lse_draft,
+                         void* ws, hipStream_t s);
 int resident_draft_launch(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
                           uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
                           int V, int r, int32_t* tokens, float* p_draft, float* lse_draft,

@@ -442,7 +442,7 @@ int device_cu_count() {
 // part_pos(t, c)), a 256-byte junk slot masked lanes write to, then the GEMM's
 // tile-queue counters (one block of kQueueWordsPerGroup words per request
 // group).
-static size_t markov_junk_offset(int R, int V) {
+size_t markov_junk_offset(int R, int V) {
   return align_up((size_t)R * part_ld(V) * sizeof(float2), 256);
 }
 static size_t markov_queue_offset(int R, int V) { return markov_junk_offset(R, V) + 256; }
@@ -711,6 +711,16 @@ static int markov_dispatch(const void* U, const void* W1, const void* W2p, const
   }
 }
 
+namespace dspark {
+int markov_draft_checked(const void* U, const void* W1, const void* W2p, const int32_t* anchor,
+                         uint64_t seed, StepArg step, const uint32_t* req_ids, int R, int gamma,
+                         int V, int r, int dtype, int32_t* tokens, float* p_draft, float* lse_draft,
+                         void* ws, hipStream_t s) {
+  return markov_dispatch(U, W1, W2p, anchor, seed, step, req_ids, R, gamma, V, r, dtype, tokens,
+                         p_draft, lse_draft, static_cast<float2*>(ws), ConfArgs{}, s);
+}
+}  // namespace dspark
+
 extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2p,
                                    const int32_t* anchor, uint64_t seed, uint64_t step,
                                    const uint64_t* step_dev, const uint32_t* req_ids, int R, int gamma, int V, int r,
@@ -721,9 +731,9 @@ extern "C" int dspark_markov_draft(const void* U, const void* W1, const void* W2
   if (!U || !W1 || !W2p || !anchor || !req_ids || !tokens || !p_draft || !lse_draft)
     return DSPARK_EINVAL;
   if (!ws || ws_bytes < markov_ws_bytes(R, V)) return DSPARK_EWORKSPACE;
-  return markov_dispatch(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma, V,
-                         r, dtype, tokens, p_draft, lse_draft, static_cast<float2*>(ws),
-                         ConfArgs{}, static_cast<hipStream_t>(stream));
+  return markov_draft_checked(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma,
+                              V, r, dtype, tokens, p_draft, lse_draft, ws,
+                              static_cast<hipStream_t>(stream));
 }
 
 // The confidence head rides in the GEMM prologue (one wave per request, in

@@ -212,6 +212,26 @@ int dspark_markov_draft(const void* U, const void* W1, const void* W2p, const in
                         int V, int r, int dtype, int32_t* tokens, float* p_draft,
                         float* lse_draft, void* ws, size_t ws_bytes, void* stream);
 
+/* dspark_markov_draft without a workspace argument, for callers that cannot
+ * allocate (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). The workspace is a device array of the library
+ * (dspark_noalloc_scratch_bytes(): 8 MiB, one per device, held until the
+ * process ends); the call allocates nothing. Arguments and outputs as in
+ * dspark_markov_draft, bit for bit. Sizes whose draft workspace
+ * (dspark_workspace_bytes(DSPARK_CALL_MARKOV_DRAFT, ...)) exceeds the array
+ * return DSPARK_EWORKSPACE before anything is launched; DSPARK_EHIP if the
+ * array's address cannot be found. Each call first clears the workspace's
+ * counters with a small kernel on `stream`. All calls on one device share the
+ * array: calls that overlap on one device race and give undefined outputs. */
+int dspark_markov_draft_noalloc(const void* U, const void* W1, const void* W2p,
+                                const int32_t* anchor, uint64_t seed, uint64_t step,
+                                const uint64_t* step_dev, const uint32_t* req_ids, int R,
+                                int gamma, int V, int r, int dtype, int32_t* tokens,
+                                float* p_draft, float* lse_draft, void* stream);
+
+/* Bytes of the device array behind dspark_markov_draft_noalloc. */
+size_t dspark_noalloc_scratch_bytes(void);
+
 /* Confidence head and prefix survival ([digest] "Verification scheduling
  * (system side)"): c_k = sigmoid((w . [h_k ; W1[x_{k-1}]] + b) * inv_temp_k),
  * a_{r,k} = a_{r,k-1} * c_k in float32, a_{r,0} = 1.

@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names
