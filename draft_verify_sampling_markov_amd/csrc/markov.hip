@@ -161,7 +161,8 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
   const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk, draw, ca, W1, xprev, xstride,
                                  r, gamma};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
-                                         R, V, r, n_t, epi, queue, w1_rows);
+                                         R, V, r, n_t, epi, queue, w1_rows, (int)gridDim.x,
+                                         (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -15,12 +15,10 @@
 // consumes the partials, before it reads them. The 16-request blocks of the request group
 // are dealt to the waves round-robin, NB per wave; a wave keeps the gathered
 // W1 rows of its blocks (the B operand) in registers for the whole kernel. The
-// pre-packed W2 tile (the A operand) is staged in LDS, double buffered, and
-// fetched two tiles ahead into two rotating register sets; the epilogue's
-// per-request rows (U, target) are also fetched two tiles ahead. The
-// steady-state loop is straight-line code: prefetch addresses are clamped to
-// valid tiles instead of guarded, so no branch forces the compiler to drain
-// the loads early. Every accumulator receives its rank chunks in increasing
+// pre-packed W2 tile (the A operand) is staged in LDS, double buffered; each
+// step issues the next tile's W2 and epilogue rows (U, target) before it
+// multiplies, and prefetch addresses are clamped to valid tiles instead of
+// guarded. Every accumulator receives its rank chunks in increasing
 // order, exactly as tile_mma() / tile_mma_regs() in dspark_device.hpp do, so
 // a later recompute of one tile gives bit-identical logits.
 //
@@ -31,7 +29,7 @@
 //   void load(const St&, int v0, int nvalid, Pre&)            // issue loads
 //   void finish(const St&, int v0, int nvalid, const f32x4 acc[4],
 //               const Pre&, int t, int lane)                  // consume, write
-//   void side_work()                // once, in the prologue, loads in flight
+//   void side_work()                // once, in the prologue
 #pragma once
 
 #include "dspark_device.hpp"
@@ -99,146 +97,140 @@ constexpr int kStaticTiles = 3;   // tiles per workgroup dealt before the queue
 struct XcdShare {
   int lo, hi, gx, j;
 };
-__device__ __forceinline__ XcdShare xcd_share(int n_t) {
-  const int G = gridDim.x, x = blockIdx.x % kNumXcd;
+__device__ __forceinline__ XcdShare xcd_share(int n_t, int G, int b) {
+  const int x = b % kNumXcd;
   const int first = x * (G / kNumXcd) + min(x, G % kNumXcd);
   XcdShare s;
   s.gx = G / kNumXcd + (x < G % kNumXcd ? 1 : 0);
-  s.j = blockIdx.x / kNumXcd;
+  s.j = b / kNumXcd;
   s.lo = (int)((long long)n_t * first / G);
   s.hi = (int)((long long)n_t * (first + s.gx) / G);
   return s;
 }
 
-// One step of the pipelined tile loop, straight-line code (no branch around
-// any load, so the compiler's in-order load counters let the prefetches stay
-// in flight): issue W2 of tile t2 into `w_issue`; multiply tile t out of `cur`;
-// hand the epilogue its rows for t (prefetched two steps ago into `u`); issue
-// the rows of t2 into `u`; store `w_ready` (W2 issued one step ago) into
-// `nxt`. The caller ends the step with a barrier. t2 is the tile two steps
-// ahead, clamped into the range.
-template <bool BF16, int KC, int NW, int NB, class Epi>
-__device__ __forceinline__ void engine_step(
-    int t, int t2, int V, const typename Elem<BF16>::Frag* __restrict__ src,
-    const typename Elem<BF16>::Frag* cur, typename Elem<BF16>::Frag* nxt,
-    typename Elem<BF16>::Frag (&w_ready)[EngineGeom<BF16, KC, NW>::kPer],
-    typename Elem<BF16>::Frag (&w_issue)[EngineGeom<BF16, KC, NW>::kPer],
-    typename Epi::Pre (&u)[NB], const typename Elem<BF16>::Frag (&b)[NB][KC],
-    const typename Epi::St (&st)[NB], const Epi& epi) {
-  typedef EngineGeom<BF16, KC, NW> Geo;
-  typedef typename Elem<BF16>::Frag Frag;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int g = lane >> 4;
-  {
-    const Frag* s = src + (size_t)t2 * Geo::kTileFrags;
-#pragma unroll
-    for (int k = 0; k < Geo::kPer; ++k) w_issue[k] = s[Geo::slot(k, tid)];
-  }
-  f32x4 acc[NB][4];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    Frag a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = cur[(kc * 4 + j) * kWave + lane];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mma_step<BF16>(acc[nb][j], a[j], b[nb][kc]);
-  }
-  const int v0 = t * kTileV + 16 * g;
-  const int v0n = t2 * kTileV + 16 * g;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    epi.finish(st[nb], v0, min(16, V - v0), acc[nb], u[nb], t, lane);
-    epi.load(st[nb], v0n, min(16, V - v0n), u[nb]);
-  }
-#pragma unroll
-  for (int k = 0; k < Geo::kPer; ++k) nxt[Geo::slot(k, tid)] = w_ready[k];
+// s_waitcnt with only the vector-memory count set: wait until at most n of
+// this wave's vector memory operations are outstanding (they retire in issue
+// order). The other counters are left at their maximum.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-// queue: this launch's kQueueWordsPerGroup counters (zero on entry). w1_rows:
+// queue: this engine's kQueueWordsPerGroup counters (zero on entry). w1_rows:
 // rows of W1 (token ids are clamped into them); V: vocabulary columns of this
 // launch (fewer than w1_rows for one shard of a vocabulary-sharded draft).
+// G workgroups run this engine, gb is this one's index among them; workgroup
+// gb runs on XCD gb % 8 (the launch keeps gb and blockIdx.x equal modulo 8).
+//
+// The loop is one step per tile, all of whose global loads go out at the
+// step's start: the W2 tile and the epilogue rows of the NEXT tile, and the
+// queue claim of the tile after it. The step then multiplies the current tile
+// out of LDS and runs its epilogue (one global store per block), waits until
+// only those stores are outstanding, moves the next tile's W2 into the other
+// LDS buffer and its rows into the epilogue's registers, and ends with a
+// barrier. Nothing a step loads is still in flight when the next one starts,
+// so the loads of a step overlap its own multiply and epilogue.
 template <bool BF16, int KC, int NW, int NB, bool VEC, class Epi, typename TokFn>
 __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __restrict__ W1,
                                                 const typename Elem<BF16>::T* __restrict__ W2p,
                                                 TokFn tok, int R, int V, int r, int n_t,
                                                 const Epi& epi, unsigned* __restrict__ queue,
-                                                int w1_rows) {
+                                                int w1_rows, int G, int gb) {
   typedef EngineGeom<BF16, KC, NW> Geo;
   typedef typename Elem<BF16>::Frag Frag;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_grab[2];
-  Frag* buf0 = reinterpret_cast<Frag*>(smem);
-  Frag* buf1 = buf0 + Geo::kTileFrags;
+  Frag* cur = reinterpret_cast<Frag*>(smem);
+  Frag* nxt = cur + Geo::kTileFrags;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int g = lane >> 4, nl = lane & 15;
   const Frag* src = reinterpret_cast<const Frag*>(W2p);
-  const XcdShare xs = xcd_share(n_t);  // hi > lo: the grid has at most n_t workgroups
-  unsigned* counter = queue + (blockIdx.x % kNumXcd) * kQueueStride;
+  const XcdShare xs = xcd_share(n_t, G, gb);  // hi > lo: at most n_t workgroups per engine
+  unsigned* counter = queue + (gb % kNumXcd) * kQueueStride;
   const int qbase = xs.lo + kStaticTiles * xs.gx;  // first tile the queue hands out
   auto clampt = [&](int t) { return min(t, xs.hi - 1); };
   int tc = xs.lo + xs.j, tn = tc + xs.gx, tnn = tn + xs.gx;  // current, next, next-but-one
   if (tc >= xs.hi) return;  // workgroup-uniform; no barrier passed yet
 
-  // prologue: tile tc into LDS, W2 of tn and the rows of tc and tn in flight;
-  // the first tile's loads go out before the (token -> W1 row) gather
-  Frag wA[Geo::kPer], wB[Geo::kPer];
-  typename Epi::Pre uA[NB], uB[NB];
-  Frag first[Geo::kPer];
+  // prologue: W2 and rows of tile tc, then the (token -> W1 row) gather
+  Frag wq[Geo::kPer];
+  typename Epi::Pre uc[NB], un[NB];
   {
     const Frag* s = src + (size_t)tc * Geo::kTileFrags;
 #pragma unroll
-    for (int i = 0; i < Geo::kPer; ++i) first[i] = s[Geo::slot(i, tid)];
+    for (int i = 0; i < Geo::kPer; ++i) wq[i] = s[Geo::slot(i, tid)];
   }
   Frag b[NB][KC];
   gather_b<BF16, KC, NB, VEC>(W1, tok, R, r, w1_rows, wave, NW, lane, b);
   typename Epi::St st[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st[nb] = epi.prepare((wave + NW * nb) * kTileN + nl);
-#pragma unroll
-  for (int i = 0; i < Geo::kPer; ++i) buf0[Geo::slot(i, tid)] = first[i];
   {
-    const Frag* s = src + (size_t)clampt(tn) * Geo::kTileFrags;
+    const int v0 = tc * kTileV + 16 * g;
 #pragma unroll
-    for (int i = 0; i < Geo::kPer; ++i) wA[i] = s[Geo::slot(i, tid)];
-  }
-  {
-    const int v0 = tc * kTileV + 16 * g, v1 = clampt(tn) * kTileV + 16 * g;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      epi.load(st[nb], v0, min(16, V - v0), uA[nb]);
-      epi.load(st[nb], v1, min(16, V - v1), uB[nb]);
-    }
+    for (int nb = 0; nb < NB; ++nb) epi.load(st[nb], v0, min(16, V - v0), uc[nb]);
   }
   epi.side_work();
+  wait_vm<0>();
+#pragma unroll
+  for (int i = 0; i < Geo::kPer; ++i) cur[Geo::slot(i, tid)] = wq[i];
   __syncthreads();
 
-  // steady state: each step claims the tile three steps ahead (the atomic
+  // steady state. Each step claims the tile three steps ahead (the atomic
   // returns while the step multiplies) and publishes it before the barrier.
   // A workgroup's tiles increase, so the first one past the range ends it.
+  int par = 0;
   for (;;) {
     unsigned grab = 0;
     if (tid == 0) grab = atomicAdd(counter, 1u);
-    engine_step<BF16, KC, NW, NB>(tc, clampt(tnn), V, src, buf0, buf1, wA, wB, uA, b, st, epi);
-    if (tid == 0) s_grab[0] = qbase + (int)grab;
+    {
+      const int tl = clampt(tn);
+      const Frag* s = src + (size_t)tl * Geo::kTileFrags;
+#pragma unroll
+      for (int k = 0; k < Geo::kPer; ++k) wq[k] = s[Geo::slot(k, tid)];
+      const int v0n = tl * kTileV + 16 * g;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) epi.load(st[nb], v0n, min(16, V - v0n), un[nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiply
+
+    f32x4 acc[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      Frag a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = cur[(kc * 4 + j) * kWave + lane];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma_step<BF16>(acc[nb][j], a[j], b[nb][kc]);
+    }
+    const int v0 = tc * kTileV + 16 * g;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) epi.finish(st[nb], v0, min(16, V - v0), acc[nb], uc[nb], tc, lane);
+
+    // the step's loads (and the claim) are in once at most its NB stores are
+    // outstanding
+    wait_vm<NB>();
+#pragma unroll
+    for (int k = 0; k < Geo::kPer; ++k) nxt[Geo::slot(k, tid)] = wq[k];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) uc[nb] = un[nb];
+    if (tid == 0) s_grab[par] = qbase + (int)grab;
     __syncthreads();
+    Frag* t_ = cur;
+    cur = nxt;
+    nxt = t_;
     tc = tn;
     tn = tnn;
-    tnn = max(s_grab[0], tn + 1);
-    if (tc >= xs.hi) break;
-    if (tid == 0) grab = atomicAdd(counter, 1u);
-    engine_step<BF16, KC, NW, NB>(tc, clampt(tnn), V, src, buf1, buf0, wB, wA, uB, b, st, epi);
-    if (tid == 0) s_grab[1] = qbase + (int)grab;
-    __syncthreads();
-    tc = tn;
-    tn = tnn;
-    tnn = max(s_grab[1], tn + 1);
+    tnn = max(s_grab[par], tn + 1);
+    par ^= 1;
     if (tc >= xs.hi) break;
   }
 }

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
     int c, float2* __restrict__ junk, unsigned* __restrict__ queue) {
   const ResidualEpi<BF16, VEC, NB == 1> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c, junk};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
-                                         r, n_t, epi, queue, V);
+                                         r, n_t, epi, queue, V, (int)gridDim.x, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(NW * 64) void accept_partials_kernel(
     int c, float* __restrict__ junk, unsigned* __restrict__ queue) {
   const AcceptEpi<BF16, VEC> epi{target, U, V, R, g0, jobs, cpart, ldn, c, junk};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
-                                         r, n_t, epi, queue, V);
+                                         r, n_t, epi, queue, V, (int)gridDim.x, (int)blockIdx.x);
 }
 
 // One 256-thread workgroup per job: the tile sums in a fixed order. The
