@@ -171,31 +171,45 @@ __device__ __forceinline__ float lane_partner(float x) {
   }
 }
 
-// Softmax partial of 16 masked logits (-inf = masked) merged over the four
-// lanes holding one request's 64 entries, without branches. The 16 terms are
-// 2^(z log2 e - m log2 e) with the exponent formed by one fused multiply-add
-// (v_exp_f32 computes 2^x); m log2 e is rounded once per tile, which scales
-// the tile's terms alike by at most 2^(ulp(m log2 e) / 2).
+// Reduce x over the lane pair {l, l ^ 16} (ROW) or {l, l ^ 32}: both lanes
+// get the same value, formed in the same operand order (the lower lane's
+// value first), so sums are bit-identical across the pair.
+template <bool ROW>
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = ROW ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <bool ROW>
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = ROW ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Softmax partial (m, s) of one request's 64 tile entries, 16 masked logits
+// (-inf = masked) in each of the four lanes l, l ^ 16, l ^ 32, l ^ 48, without
+// branches: m is the max over the 64 entries (over the lane's 16, then over
+// the four lanes), s = sum of 2^(z log2 e - m log2 e) over the lane's 16 with
+// the exponent formed by one fused multiply-add (v_exp_f32 computes 2^x), then
+// summed over the four lanes; m log2 e is rounded once per tile, which scales
+// the tile's terms alike by at most 2^(ulp(m log2 e) / 2). All four lanes end
+// with the same (m, s). m = -inf (all masked) gives s = 0.
 __device__ __forceinline__ void softmax16_merge4(const float z[16], float& m_out, float& s_out) {
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, z[i]);
+  m = pair_max<true>(m);
+  m = pair_max<false>(m);
   const float mref = (m == -INFINITY) ? 0.0f : m;
   const float mb = -mref * kLog2e;
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, mb));
-#pragma unroll
-  for (int o = 0; o < 2; ++o) {  // partners l ^ 16, then l ^ 32
-    const float m2 = o == 0 ? lane_partner<true>(m) : lane_partner<false>(m);
-    const float s2 = o == 0 ? lane_partner<true>(s) : lane_partner<false>(s);
-    const float mm = fmaxf(m, m2);
-    const float mr = (mm == -INFINITY) ? 0.0f : mm;
-    const float sa = (m == -INFINITY) ? 0.0f : s * __expf(m - mr);
-    const float sb = (m2 == -INFINITY) ? 0.0f : s2 * __expf(m2 - mr);
-    s = sa + sb;
-    m = mm;
-  }
+  s = pair_sum<true>(s);
+  s = pair_sum<false>(s);
   m_out = m;
   s_out = s;
 }

@@ -71,10 +71,9 @@ struct DrawArgs {
 };
 
 // Epilogue of the draft pass: z = bias + U_k, then the tile's softmax partial
-// (max, sum of exp(z - max)) per request, merged over the lane's four groups
-// in a fixed butterfly order, stored at part[n * ldn + part_pos(t, c)]. Lanes
-// that must not write (other groups, requests past R) store to a junk slot
-// instead of branching.
+// (max, sum of exp(z - max)) per request over the four lanes holding its 64
+// entries, stored at part[n * ldn + part_pos(t, c)] by the first of them
+// (requests past R store nothing).
 template <bool BF16, bool VEC>
 struct MarkovEpi {
   typedef typename Elem<BF16>::T T;
@@ -146,8 +145,7 @@ struct MarkovEpi {
     tile_logits<BF16>(acc, u16, nvalid, s.active, z);
     float m, sm;
     softmax16_merge4(z, m, sm);
-    float2* dst = ((lane >> 4) == 0 && s.active) ? part + (size_t)s.n * ldn + part_pos(t, c) : junk;
-    *dst = make_float2(m, sm);
+    if ((lane >> 4) == 0 && s.active) part[(size_t)s.n * ldn + part_pos(t, c)] = make_float2(m, sm);
   }
 };
 

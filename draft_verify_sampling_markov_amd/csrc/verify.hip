@@ -330,13 +330,9 @@ struct ResidualEpi {
       sq += q[i];
       sp += pt[i];
     }
-    sq += lane_partner<true>(sq);
-    sp += lane_partner<true>(sp);
-    sq += lane_partner<false>(sq);
-    sp += lane_partner<false>(sp);
-    float2* dst =
-        ((lane >> 4) == 0 && s.active) ? rpart + (size_t)s.ng * ldn + part_pos(t, c) : junk;
-    *dst = make_float2(sq, sp);
+    sq = pair_sum<false>(pair_sum<true>(sq));
+    sp = pair_sum<false>(pair_sum<true>(sp));
+    if ((lane >> 4) == 0 && s.active) rpart[(size_t)s.ng * ldn + part_pos(t, c)] = make_float2(sq, sp);
   }
 };
 
@@ -552,10 +548,8 @@ struct AcceptEpi {
         const float pd = shifted_exp(zd, s.bd), pt = shifted_exp(zt16[idx], s.bt);
         sm += idx < nv ? fminf(pd, pt) : 0.0f;
       }
-    sm += lane_partner<true>(sm);
-    sm += lane_partner<false>(sm);
-    float* dst = ((lane >> 4) == 0 && s.active) ? cpart + (size_t)s.ng * ldn + part_pos(t, c) : junk;
-    *dst = sm;
+    sm = pair_sum<false>(pair_sum<true>(sm));
+    if ((lane >> 4) == 0 && s.active) cpart[(size_t)s.ng * ldn + part_pos(t, c)] = sm;
   }
 };
 
