@@ -57,9 +57,12 @@ struct EngineGeom {
 // VEC (W1 16-byte aligned, r a multiple of 8) the loads are unconditional:
 // addresses are clamped into the row and out-of-range values zeroed after the
 // load, so the prologue has no branch that would drain the loads in flight.
-template <bool BF16, int KC, int NB, bool VEC, typename TokFn>
-__device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restrict__ W1, TokFn tok,
-                                         int R, int r, int w1_rows, int wave, int nw, int lane,
+// xtok[nb]: the token of the lane's request in block nb (read beforehand, so
+// that the row loads wait on the token loads alone).
+template <bool BF16, int KC, int NB, bool VEC>
+__device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restrict__ W1,
+                                         const int (&xtok)[NB], int R, int r, int w1_rows,
+                                         int wave, int nw, int lane,
                                          typename Elem<BF16>::Frag b[NB][KC]) {
   typedef typename Elem<BF16>::T T;
   typedef typename Elem<BF16>::Frag Frag;
@@ -67,7 +70,7 @@ __device__ __forceinline__ void gather_b(const typename Elem<BF16>::T* __restric
   for (int nb = 0; nb < NB; ++nb) {
     const int n = (wave + nw * nb) * kTileN + (lane & 15);
     const bool ok = n < R;
-    const int x = clamp_token(tok(min(n, R - 1)), w1_rows);
+    const int x = clamp_token(xtok[nb], w1_rows);
     const T* row = W1 + (size_t)x * r;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -154,7 +157,11 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
   int tc = xs.lo + xs.j, tn = tc + xs.gx, tnn = tn + xs.gx;  // current, next, next-but-one
   if (tc >= xs.hi) return;  // workgroup-uniform; no barrier passed yet
 
-  // prologue: W2 and rows of tile tc, then the (token -> W1 row) gather
+  // prologue: the lane's tokens, then W2 and rows of tile tc, then the
+  // (token -> W1 row) gather, which waits on the token loads alone
+  int xtok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) xtok[nb] = tok(min((wave + NW * nb) * kTileN + nl, R - 1));
   Frag wq[Geo::kPer];
   typename Epi::Pre uc[NB], un[NB];
   {
@@ -162,8 +169,6 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
 #pragma unroll
     for (int i = 0; i < Geo::kPer; ++i) wq[i] = s[Geo::slot(i, tid)];
   }
-  Frag b[NB][KC];
-  gather_b<BF16, KC, NB, VEC>(W1, tok, R, r, w1_rows, wave, NW, lane, b);
   typename Epi::St st[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st[nb] = epi.prepare((wave + NW * nb) * kTileN + nl);
@@ -172,6 +177,8 @@ __device__ __forceinline__ void run_tile_engine(const typename Elem<BF16>::T* __
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) epi.load(st[nb], v0, min(16, V - v0), uc[nb]);
   }
+  Frag b[NB][KC];
+  gather_b<BF16, KC, NB, VEC>(W1, xtok, R, r, w1_rows, wave, NW, lane, b);
   epi.side_work();
   wait_vm<0>();
 #pragma unroll
