@@ -84,9 +84,9 @@ inline int check_sizes(int R, int gamma, int V, int r, int dt) {
 
 // Workspace layout pieces (bytes, 256-aligned).
 size_t markov_ws_bytes(int R, int V);
-// Start of the draft workspace's bookkeeping tail (junk slot, tile-queue
-// counters, draft uniforms, hand-off block); the tile partials lie before it.
-size_t markov_junk_offset(int R, int V);
+// Start of the draft workspace's bookkeeping tail (tile-queue counters, draft
+// uniforms, hand-off block); the tile partials lie before it.
+size_t markov_tail_offset(int R, int V);
 // Zero-fill n bytes at p on stream s (the kernel behind dspark_workspace_init).
 int zero_fill(void* p, size_t n, hipStream_t s);
 // Hand-off block of a draft workspace (resident-W2 kernel): call epoch, exit

@@ -88,7 +88,6 @@ struct MarkovEpi {
   int R, V;
   float2* part;
   int ldn, c;
-  float2* junk;
   DrawArgs draw;
   ConfArgs ca;     // ca.h == nullptr: the slot is not scored here
   const T* W1;     // for the head's W1-row dot product
@@ -154,9 +153,9 @@ __global__ __launch_bounds__(NW * 64) void markov_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ U, long long ldU,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     const int* __restrict__ xprev, int xstride, int R, int V, int r, int n_t, int w1_rows,
-    float2* __restrict__ part, int ldn, int c, float2* __restrict__ junk,
+    float2* __restrict__ part, int ldn, int c,
     unsigned* __restrict__ queue, DrawArgs draw, ConfArgs ca, int gamma) {
-  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, junk, draw, ca, W1, xprev, xstride,
+  const MarkovEpi<BF16, VEC> epi{U, ldU, R, V, part, ldn, c, draw, ca, W1, xprev, xstride,
                                  r, gamma};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return xprev[(size_t)n * xstride]; },
                                          R, V, r, n_t, epi, queue, w1_rows, (int)gridDim.x,
@@ -438,13 +437,13 @@ int device_cu_count() {
 
 // Draft workspace: the request-major tile partials [R, ldn] (float2,
 // ldn = 256 c, c = ceil(n_t / 256), tile t of request n at n * ldn +
-// part_pos(t, c)), a 256-byte junk slot masked lanes write to, then the GEMM's
-// tile-queue counters (one block of kQueueWordsPerGroup words per request
-// group).
-size_t markov_junk_offset(int R, int V) {
+// part_pos(t, c)), then the bookkeeping tail: the GEMM's tile-queue counters
+// (one block of kQueueWordsPerGroup words per group of 128 requests), the
+// draft uniforms and the resident kernel's hand-off block.
+size_t markov_tail_offset(int R, int V) {
   return align_up((size_t)R * part_ld(V) * sizeof(float2), 256);
 }
-static size_t markov_queue_offset(int R, int V) { return markov_junk_offset(R, V) + 256; }
+static size_t markov_queue_offset(int R, int V) { return markov_tail_offset(R, V); }
 static size_t markov_u_offset(int R, int V) {
   return markov_queue_offset(R, V) + (size_t)queue_groups(R) * kQueueWordsPerGroup * 4;
 }
@@ -474,7 +473,7 @@ template <bool BF16, int KC, int NW, int NB>
 static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, bool vec,
                                const typename Elem<BF16>::T* W1, const typename Elem<BF16>::T* W2p,
                                const int32_t* xprev, int xstride, int Rg, int V, int r,
-                               int w1_rows, float2* part, float2* junk, unsigned* queue,
+                               int w1_rows, float2* part, unsigned* queue,
                                DrawArgs draw, const ConfArgs& ca, int gamma, hipStream_t s) {
   typedef EngineGeom<BF16, KC, NW> G;
   const int n_t = n_vtiles(V);
@@ -483,11 +482,11 @@ static int launch_partials_cfg(const typename Elem<BF16>::T* Uk, long long ldU, 
   if (vec)
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, true>), dim3(grid), dim3(NW * kWave),
                        G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r, n_t, w1_rows,
-                       part, ldn, c, junk, queue, draw, ca, gamma);
+                       part, ldn, c, queue, draw, ca, gamma);
   else
     hipLaunchKernelGGL((markov_partials_kernel<BF16, KC, NW, NB, false>), dim3(grid),
                        dim3(NW * kWave), G::kLdsBytes, s, Uk, ldU, W1, W2p, xprev, xstride, Rg, V, r,
-                       n_t, w1_rows, part, ldn, c, junk, queue, draw, ca, gamma);
+                       n_t, w1_rows, part, ldn, c, queue, draw, ca, gamma);
   return launch_status();
 }
 
@@ -499,7 +498,6 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
                            const int32_t* xprev, int xstride, int R, int V, int r, int w1_rows,
                            float2* part, DrawArgs draw, const ConfArgs& ca, int gamma,
                            hipStream_t s) {
-  float2* junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) + markov_junk_offset(R, V));
   unsigned* queue = markov_queue(part, R, V);
   const int ldn = part_ld(V);
   for (int g0 = 0; g0 < R; g0 += req_group<BF16>()) {
@@ -523,11 +521,11 @@ static int launch_partials(const typename Elem<BF16>::T* Uk, long long ldU, bool
     }
     int st;
     if (partials_waves(Rg) == 4)
-      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
+      st = launch_partials_cfg<BF16, KC, 4, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, qg, dg, cg, gamma, s);
     else if (blocks <= 8)
-      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
+      st = launch_partials_cfg<BF16, KC, 8, 1>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, qg, dg, cg, gamma, s);
     else if constexpr (BF16)
-      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, junk, qg, dg, cg, gamma, s);
+      st = launch_partials_cfg<BF16, KC, 8, 2>(Ug, ldU, vec, W1, W2p, xg, xstride, Rg, V, r, w1_rows, pg, qg, dg, cg, gamma, s);
     else
       st = DSPARK_ESIZE;  // unreachable: float32 groups hold at most 8 blocks
     if (st) return st;

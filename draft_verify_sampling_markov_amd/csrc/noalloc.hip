@@ -59,7 +59,7 @@ extern "C" int dspark_markov_draft_noalloc(const void* U, const void* W1, const 
   void* ws = scratch_ptr();
   if (ws == nullptr) return DSPARK_EHIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t tail = markov_junk_offset(R, V);
+  const size_t tail = markov_tail_offset(R, V);
   st = zero_fill(static_cast<char*>(ws) + tail, need - tail, s);
   if (st) return st;
   return markov_draft_checked(U, W1, W2p, anchor, seed, StepArg{step, step_dev}, req_ids, R, gamma,

@@ -267,7 +267,6 @@ struct ResArgs {
   float* lse_draft;        // [R, gamma]
   float2* part;            // [R, ldn] tile partials (part_pos order)
   int ldn, c;
-  float2* junk;
   unsigned* bar;
   ConfArgs ca;             // ca.h == nullptr: no confidence head
 };
@@ -668,8 +667,6 @@ int resident_draft_launch(const void* U, const void* W1, const void* W2p, const 
   a.part = part;
   a.ldn = part_ld(V);
   a.c = part_chunk(V);
-  a.junk = reinterpret_cast<float2*>(reinterpret_cast<char*>(part) +
-                                     align_up((size_t)R * part_ld(V) * sizeof(float2), 256));
   a.bar = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(part) + resident_bar_offset(R, V));
   a.ca = ca;
   const size_t lds = res_lds_bytes(LT);

@@ -299,7 +299,6 @@ struct ResidualEpi {
   Jobs jobs;
   float2* rpart;
   int ldn, c;
-  float2* junk;
 
   __device__ __forceinline__ St prepare(int n) const {
     St s;
@@ -341,8 +340,8 @@ __global__ __launch_bounds__(NW * 64) void residual_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     Jobs jobs, int g0, int R, int gamma, int V, int r, int n_t, float2* __restrict__ rpart, int ldn,
-    int c, float2* __restrict__ junk, unsigned* __restrict__ queue) {
-  const ResidualEpi<BF16, VEC, NB == 1> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c, junk};
+    int c, unsigned* __restrict__ queue) {
+  const ResidualEpi<BF16, VEC, NB == 1> epi{target, U, gamma, V, R, g0, jobs, rpart, ldn, c};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
                                          r, n_t, epi, queue, V, (int)gridDim.x, (int)blockIdx.x);
 }
@@ -515,7 +514,6 @@ struct AcceptEpi {
   AcceptJobs jobs;
   float* cpart;
   int ldn, c;
-  float* junk;
 
   __device__ __forceinline__ St prepare(int n) const {
     St s;
@@ -558,8 +556,8 @@ __global__ __launch_bounds__(NW * 64) void accept_partials_kernel(
     const typename Elem<BF16>::T* __restrict__ target, const typename Elem<BF16>::T* __restrict__ U,
     const typename Elem<BF16>::T* __restrict__ W1, const typename Elem<BF16>::T* __restrict__ W2p,
     AcceptJobs jobs, int g0, int R, int V, int r, int n_t, float* __restrict__ cpart, int ldn,
-    int c, float* __restrict__ junk, unsigned* __restrict__ queue) {
-  const AcceptEpi<BF16, VEC> epi{target, U, V, R, g0, jobs, cpart, ldn, c, junk};
+    int c, unsigned* __restrict__ queue) {
+  const AcceptEpi<BF16, VEC> epi{target, U, V, R, g0, jobs, cpart, ldn, c};
   run_tile_engine<BF16, KC, NW, NB, VEC>(W1, W2p, [&](int n) { return jobs.xprev[g0 + n]; }, R, V,
                                          r, n_t, epi, queue, V, (int)gridDim.x, (int)blockIdx.x);
 }
@@ -590,7 +588,6 @@ __global__ __launch_bounds__(kSelThreads) void accept_reduce_kernel(
 struct VerifyWs {
   float2* rowpart;
   float2* rpart;  // request-major residual tile partials [R, part_ld(V)]
-  float2* junk;   // write target of masked lanes
   unsigned* queue;  // tile-queue counters of the residual GEMM, per request group
   Jobs jobs;
 };
@@ -606,7 +603,6 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
   };
   const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
   const size_t o_rp = take((size_t)R * part_ld(V) * sizeof(float2));
-  const size_t o_junk = take(256);
   const size_t o_q = take((size_t)queue_groups(R) * kQueueWordsPerGroup * 4);
   size_t o_j[7];
   for (int i = 0; i < 7; ++i) o_j[i] = take((size_t)R * 4);
@@ -614,7 +610,6 @@ static size_t carve(VerifyWs* w, void* base, int R, int gamma, int V) {
     char* b = static_cast<char*>(base);
     w->rowpart = reinterpret_cast<float2*>(b + o_row);
     w->rpart = reinterpret_cast<float2*>(b + o_rp);
-    w->junk = reinterpret_cast<float2*>(b + o_junk);
     w->queue = reinterpret_cast<unsigned*>(b + o_q);
     w->jobs.kind = reinterpret_cast<int*>(b + o_j[0]);
     w->jobs.slot = reinterpret_cast<int*>(b + o_j[1]);
@@ -679,11 +674,11 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
       if (vec_engine)                                                                              \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, true>), grid,             \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk, qg);                       \
+                           gamma, V, r, n_t, ws.rpart, ldn, c, qg);                               \
       else                                                                                         \
         hipLaunchKernelGGL((residual_partials_kernel<BF16, KC, NW_, NB_, false>), grid,            \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           gamma, V, r, n_t, ws.rpart, ldn, c, ws.junk, qg);                       \
+                           gamma, V, r, n_t, ws.rpart, ldn, c, qg);                               \
     }
     if (blocks <= 4) DSPARK_RES_LAUNCH(4, 1, 2)
     else if (blocks <= 8) DSPARK_RES_LAUNCH(8, 1, 1)
@@ -721,11 +716,10 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
 }
 
 // Analytic-acceptance workspace: row partials and jobs for R * (gamma + 1)
-// packed rows, their tile sums, the junk slot and the tile-queue counters.
+// packed rows, their tile sums and the tile-queue counters.
 struct AcceptWs {
   float2* rowpart;
   float* cpart;
-  float* junk;
   unsigned* queue;
   AcceptJobs jobs;
 };
@@ -740,7 +734,6 @@ static size_t carve_accept(AcceptWs* w, void* base, int R, int gamma, int V) {
   };
   const size_t o_row = take((size_t)rows_ws * n_row_chunks(V) * sizeof(float2));
   const size_t o_cp = take((size_t)rows_ws * part_ld(V) * sizeof(float));
-  const size_t o_junk = take(256);
   const size_t o_q = take((size_t)queue_groups(rows_ws) * kQueueWordsPerGroup * 4);
   size_t o_j[6];
   for (int i = 0; i < 6; ++i) o_j[i] = take((size_t)rows_ws * 4);
@@ -748,7 +741,6 @@ static size_t carve_accept(AcceptWs* w, void* base, int R, int gamma, int V) {
     char* b = static_cast<char*>(base);
     w->rowpart = reinterpret_cast<float2*>(b + o_row);
     w->cpart = reinterpret_cast<float*>(b + o_cp);
-    w->junk = reinterpret_cast<float*>(b + o_junk);
     w->queue = reinterpret_cast<unsigned*>(b + o_q);
     w->jobs.out = reinterpret_cast<int*>(b + o_j[0]);
     w->jobs.urow = reinterpret_cast<int*>(b + o_j[1]);
@@ -801,11 +793,11 @@ static int launch_accept(const void* target, const int32_t* cu, const int32_t* a
       if (vec)                                                                                     \
         hipLaunchKernelGGL((accept_partials_kernel<BF16, KC, NW_, NB_, true>), grid,               \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           V, r, n_t, ws.cpart, ldn, c, ws.junk, qg);                              \
+                           V, r, n_t, ws.cpart, ldn, c, qg);                                      \
       else                                                                                         \
         hipLaunchKernelGGL((accept_partials_kernel<BF16, KC, NW_, NB_, false>), grid,              \
                            dim3(NW_ * kWave), G::kLdsBytes, s, tg, Ub, W1b, W2b, ws.jobs, g0, Rg,  \
-                           V, r, n_t, ws.cpart, ldn, c, ws.junk, qg);                              \
+                           V, r, n_t, ws.cpart, ldn, c, qg);                                      \
     }
     if (blocks <= 4) DSPARK_ACC_LAUNCH(4, 1, 2)
     else if (blocks <= 8) DSPARK_ACC_LAUNCH(8, 1, 1)
