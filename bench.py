@@ -552,6 +552,56 @@ def measure_chain(dv, spec, mode_name: str, B_cap: int, *, steps: int, warmup: i
     return out, inp, dev
 
 
+def measure_peaks(dv):
+    """What this GPU reaches, beside the published peaks the rooflines use:
+    streaming reads of a 2 GiB buffer (eight times the Infinity Cache, so from
+    HBM), re-reads of one 77.8 MB buffer (the size of a slot's U_k or of W2,
+    which the Infinity Cache can hold; a launch this short also pays its
+    ramp), and the bf16 matrix-core rate of a loop of independent 16x16x32
+    products, 32 waves per CU. Each is the median of HIP-event
+    timed launches on the current stream."""
+    import numpy as np
+    import torch
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    big = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    small = torch.ones(77_791_232, dtype=torch.uint8, device="cuda")
+    for b in (big, small):
+        dv.probe_read(b, sink)
+    torch.cuda.synchronize()
+    t_big = timed(lambda: dv.probe_read(big, sink), 9)
+    t_small = timed(lambda: dv.probe_read(small, sink), 21)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid, iters = 8 * cus, 512
+    flops = dv.probe_mfma(sink, grid=grid, iters=iters)
+    torch.cuda.synchronize()
+    t_mfma = timed(lambda: dv.probe_mfma(sink, grid=grid, iters=iters), 9)
+    del big, small
+    torch.cuda.empty_cache()
+    out = {"hbm_read_GBs": round((2 << 30) / t_big / 1e9, 1),
+           "reread_77MB_GBs": round(77_791_232 / t_small / 1e9, 1),
+           "mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+           "published": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFS},
+           "note": ("dspark_probe_read / dspark_probe_mfma: 16-byte nontemporal grid-stride "
+                    "reads of 2 GiB, 4 workgroups of 512 threads per CU; 8 independent "
+                    "v_mfma_f32_16x16x32_bf16 chains per wave, 32 waves per CU; medians of "
+                    "event-timed launches; rooflines stay priced against the published peaks")}
+    log(f"[bench] measured peaks: HBM read {out['hbm_read_GBs']} GB/s (2 GiB), re-read of 77.8 MB "
+        f"{out['reread_77MB_GBs']} GB/s, bf16 MFMA {out['mfma_bf16_TFLOPs']} TFLOP/s")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,6 +629,8 @@ def main() -> int:
                          "only the full-vocabulary GEMM launches)")
     ap.add_argument("--observe-calls", type=int, default=10,
                     help="timed calls of each observability pass on a cap-accept step; 0 skips")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the peak probes (streaming read, matrix-core loop)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one 256 MiB device-to-device copy (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -635,6 +687,8 @@ def main() -> int:
         line["vocab_shards"] = measure_shards(dv, dev, spec, args.shards, 20)
     if args.observe_calls > 0:
         line["observability"] = measure_observability(dv, dev, inp, spec, B_cap, args.observe_calls)
+    if not args.no_peaks:
+        line["peaks_measured"] = measure_peaks(dv)
     if args.calibrate_copy:
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -46,6 +46,9 @@ _SIGNATURES = {
     "dspark_markov_draft_noalloc": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i, _i,
                                          _i, _vp, _vp, _vp, _vp]),
     "dspark_noalloc_scratch_bytes": (_sz, []),
+    "dspark_probe_read": (_i, [_vp, _sz, _vp, _vp]),
+    "dspark_probe_mfma": (_i, [_vp, _i, _i, _vp]),
+    "dspark_probe_mfma_flops": (_c.c_double, [_i, _i]),
     "dspark_confidence": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i,
                                _vp, _vp, _vp, _vp]),
     "dspark_markov_draft_confidence": (_i, [_vp, _vp, _vp, _vp, _u64, _u64, _vp, _vp, _i, _i, _i,
@@ -284,6 +287,20 @@ def markov_draft_noalloc(U, W1, W2p, anchor, *, r: int, seed: int = 0, step: int
         _dev(p, "p_draft", torch.float32, (R, gamma)), _dev(lse, "lse_draft", torch.float32, (R, gamma)),
         _stream(stream)))
     return tokens, p, lse
+
+
+def probe_read(buf, sink, stream=None):
+    """One streaming-read sweep over ``buf`` (dspark_probe_read); bytes read =
+    buf.numel() * element size."""
+    _check(load_library().dspark_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                            _dev(sink, "sink"), _stream(stream)))
+
+
+def probe_mfma(sink, *, grid: int, iters: int, stream=None) -> float:
+    """One matrix-core loop launch (dspark_probe_mfma); returns its FLOP."""
+    lib = load_library()
+    _check(lib.dspark_probe_mfma(_dev(sink, "sink"), int(grid), int(iters), _stream(stream)))
+    return float(lib.dspark_probe_mfma_flops(int(grid), int(iters)))
 
 
 def markov_draft_confidence(U, W1, W2p, anchor, h, w, b: float, *, r: int, inv_temp=None,

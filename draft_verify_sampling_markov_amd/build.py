@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdspark.so")
 SOURCES = ["abi.hip", "markov.hip", "resident.hip", "confidence.hip", "schedule.hip", "verify.hip", "decode.hip", "observe.hip",
-           "calibrate.hip", "noalloc.hip"]
+           "calibrate.hip", "noalloc.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",

@@ -232,6 +232,21 @@ int dspark_markov_draft_noalloc(const void* U, const void* W1, const void* W2p,
 /* Bytes of the device array behind dspark_markov_draft_noalloc. */
 size_t dspark_noalloc_scratch_bytes(void);
 
+/* Peak probes for the measurement (not part of the method): what this GPU
+ * reaches beside the published peaks the rooflines are priced against.
+ * dspark_probe_read: one grid-stride sweep of 16-byte nontemporal loads over
+ *   src [bytes] (16-byte aligned, a multiple of 16 bytes), 4 workgroups of
+ *   512 threads per CU; sink [1] uint32 scratch, written only on a constant
+ *   the sweep never produces. Bytes read = bytes.
+ * dspark_probe_mfma: grid workgroups of 4 waves, each wave iters rounds of 8
+ *   independent v_mfma_f32_16x16x32_bf16; sink [256] float scratch as above.
+ *   dspark_probe_mfma_flops(grid, iters) = the FLOP the launch performs.
+ * Both enqueue one launch on `stream`; DSPARK_EINVAL / DSPARK_ESIZE for bad
+ * arguments, before anything is launched. */
+int dspark_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+int dspark_probe_mfma(void* sink, int grid, int iters, void* stream);
+double dspark_probe_mfma_flops(int grid, int iters);
+
 /* Confidence head and prefix survival ([digest] "Verification scheduling
  * (system side)"): c_k = sigmoid((w . [h_k ; W1[x_{k-1}]] + b) * inv_temp_k),
  * a_{r,k} = a_{r,k-1} * c_k in float32, a_{r,0} = 1.

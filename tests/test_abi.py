@@ -31,7 +31,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     dv, lib = _lib()
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(dv.EXPORTS) == names

@@ -61,3 +61,7 @@ def test_json_line_contract():
         assert st["p10"] <= st["median"] <= st["p90"] and st["n"] > 0
     assert "tiny:compact" in d["other_workloads"]
     assert d["draft_call"]["per_slot_ms"] > 0
+    pk = d["peaks_measured"]
+    # plausible for one MI355X: well above a tenth of the published peaks, not above them
+    assert 800 < pk["hbm_read_GBs"] <= 8000 and 800 < pk["reread_77MB_GBs"] < 20000
+    assert 250 < pk["mfma_bf16_TFLOPs"] <= 2600
