@@ -96,6 +96,20 @@ def test_host_validation_rejects_before_launch():
     assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, None, p, 0.0, None, 64, p, p, p, p, p, None, p, 1 << 30, None) == EINVAL
     assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, None, None, p, 1 << 30, None) == EINVAL
     assert dc(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 0, p, p, 0.0, None, 64, p, p, p, p, p, None, p, 8, None) == EWS
+    # no-allocation draft: the draft's checks, then the array's size, before any device call
+    na = lib.dspark_markov_draft_noalloc
+    assert na(p, p, p, p, 0, 0, None, p, 4, 7, 1024, 32, 5, p, p, p, None) == EDTYPE
+    assert na(p, p, p, p, 0, 0, None, p, 4, 17, 1024, 32, 0, p, p, p, None) == ESIZE
+    assert na(p, p, p, p, 0, 0, None, None, 4, 7, 1024, 32, 0, p, p, p, None) == EINVAL
+    assert na(p, p, p, p, 0, 0, None, p, 2048, 1, 151936, 256, 1, p, p, p, None) == EWS  # bf16
+    # peak probes
+    assert lib.dspark_probe_read(None, 1024, p, None) == EINVAL
+    assert lib.dspark_probe_read(p, 1000, p, None) == ESIZE
+    assert lib.dspark_probe_read(ctypes.c_void_p(24), 1024, p, None) == ESIZE
+    assert lib.dspark_probe_mfma(None, 8, 8, None) == EINVAL
+    assert lib.dspark_probe_mfma(p, 0, 8, None) == ESIZE
+    assert lib.dspark_probe_mfma(p, 8, 0, None) == ESIZE
+    assert lib.dspark_probe_mfma_flops(256, 512) == 256 * 4 * 512 * 8 * 16384
     # schedule + pack in one launch: the checks of both
     sp = lib.dspark_schedule_pack
     tiers = (ctypes.c_int32 * 2)(16, 32)
