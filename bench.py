@@ -688,7 +688,13 @@ def main() -> int:
     if args.observe_calls > 0:
         line["observability"] = measure_observability(dv, dev, inp, spec, B_cap, args.observe_calls)
     if not args.no_peaks:
-        line["peaks_measured"] = measure_peaks(dv)
+        pk = measure_peaks(dv)
+        line["peaks_measured"] = pk
+        # the dominant kernel also against what this GPU reaches (reported beside frac)
+        rl = line["roofline"]
+        rl["frac_of_measured_peak"] = round(rl["achieved"] / pk["hbm_read_GBs"], 4)
+        if spec.dtype == "bf16":   # the probe measures the bf16 matrix rate
+            rl["mfma"]["frac_of_measured_peak"] = round(rl["mfma"]["achieved"] / pk["mfma_bf16_TFLOPs"], 4)
     if args.calibrate_copy:
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

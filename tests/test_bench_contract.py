@@ -65,3 +65,4 @@ def test_json_line_contract():
     # plausible for one MI355X: well above a tenth of the published peaks, not above them
     assert 800 < pk["hbm_read_GBs"] <= 8000 and 800 < pk["reread_77MB_GBs"] < 20000
     assert 250 < pk["mfma_bf16_TFLOPs"] <= 2600
+    assert rl["frac_of_measured_peak"] == pytest.approx(rl["achieved"] / pk["hbm_read_GBs"], abs=1e-3)
