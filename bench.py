@@ -17,8 +17,9 @@ individually timed steps (median, p10, p90; warm and after a 512 MiB cache
 flush), the roofline of the dominant kernel (the per-slot bias GEMM +
 softmax-partials pass, timed with HIP events on the chain's stream) with its
 algorithmic bytes counting W2 once per block, the same figures for the other
-named workloads, and the CPU oracle timed on a bounded sample of the headline
-workload on this host.
+named workloads, the bandwidth and matrix rate this GPU reaches (two probe
+kernels of the library), and the CPU oracle timed on a bounded sample of the
+headline workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--config mixed] [--mode cap_accept]
 """

@@ -128,7 +128,7 @@ __device__ __forceinline__ void wait_vm() {
 //
 // The loop is one step per tile, all of whose global loads go out at the
 // step's start: the W2 tile and the epilogue rows of the NEXT tile, and the
-// queue claim of the tile after it. The step then multiplies the current tile
+// queue claim of the tile three steps ahead. The step then multiplies the current tile
 // out of LDS and runs its epilogue (one global store per block), waits until
 // only those stores are outstanding, moves the next tile's W2 into the other
 // LDS buffer and its rows into the epilogue's registers, and ends with a
