@@ -98,8 +98,9 @@ typedef enum {
 /* Which kernels dspark_markov_draft and dspark_markov_draft_confidence use
  * (dspark_set_draft_path). */
 typedef enum {
-  DSPARK_DRAFT_AUTO = 0,     /* the library's choice: the faster of the two
-                                measured on MI355X for the shape             */
+  DSPARK_DRAFT_AUTO = 0,     /* the library's choice: the per-slot launches,
+                                which measured faster on MI355X at every
+                                workload shape                               */
   DSPARK_DRAFT_PER_SLOT = 1, /* always the per-slot GEMM + select launches   */
   DSPARK_DRAFT_RESIDENT = 2  /* the resident-W2 block kernel where the shape
                                 allows it (see dspark_markov_draft), else
