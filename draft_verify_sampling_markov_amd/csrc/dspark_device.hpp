@@ -119,7 +119,9 @@ __device__ __forceinline__ void load16_raw(const typename Elem<BF16>::T* __restr
 // v0 + VEC * min(i, words_valid - 1), and a lane past the end reads from the
 // row start; without VEC each element is read from min(v0 + i, V - 1). Entries
 // at or beyond nvalid hold arbitrary row values and must be masked by the
-// caller.
+// caller. The loads carry no nontemporal hint: these rows are read once, but
+// on MI355X the plain cached loads measured faster here, as the tile
+// pipeline issues them beside the re-read W2 stream.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void load16_clamped(const typename Elem<BF16>::T* __restrict__ row,
                                                int v0, int nvalid, int V, Raw16<BF16>& r) {
@@ -130,7 +132,7 @@ __device__ __forceinline__ void load16_clamped(const typename Elem<BF16>::T* __r
     const int nv = nvalid > 0 ? min(W, (nvalid + PER - 1) / PER) : 1;
     const u32x4* q = reinterpret_cast<const u32x4*>(row + base);
 #pragma unroll
-    for (int i = 0; i < W; ++i) r.w[i] = __builtin_nontemporal_load(q + min(i, nv - 1));
+    for (int i = 0; i < W; ++i) r.w[i] = q[min(i, nv - 1)];
   } else {
     uint32_t bits[4 * W];
     if constexpr (BF16) {
