@@ -21,6 +21,11 @@ named workloads, the bandwidth and matrix rate this GPU reaches (two probe
 kernels of the library), and the CPU oracle timed on a bounded sample of the
 headline workload on this host.
 
+Each timed region follows W untimed steps (default 200, about 0.1 s): on
+MI355X the step time drifts by about 5% over the first few dozen steps of
+sustained load before it settles, and a serving loop runs at the settled
+rate.
+
     python bench.py [--steps K] [--warmup W] [--config mixed] [--mode cap_accept]
 """
 from __future__ import annotations
@@ -385,7 +390,8 @@ def measure_chain(dv, spec, mode_name: str, B_cap: int, *, steps: int, warmup: i
     step_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(step_graph):
         ch.run(gather=False)
-    step_graph.replay()
+    for _ in range(max(warmup, 1)):
+        step_graph.replay()
     torch.cuda.synchronize()
 
     # ---- timed region 2: exactly `steps` steps, graph replays ----
@@ -515,6 +521,10 @@ def measure_chain(dv, spec, mode_name: str, B_cap: int, *, steps: int, warmup: i
         dv.workspace_init(w_)
     with torch.cuda.graph(gr):
         gemm_launches()
+    for _ in range(max(1, warmup // 4)):  # untimed, as the steps before a timed region
+        for w_ in wss:
+            dv.workspace_init(w_)
+        gr.replay()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(P)]
     for e0, e1 in ev:
@@ -607,7 +617,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before each timed region; under sustained load the "
+                         "GPU's step time settles after a few dozen steps")
     ap.add_argument("--config", default="mixed")
     ap.add_argument("--mode", default="cap_accept", choices=["static", "compact", "cap_accept"])
     ap.add_argument("--budget", type=int, default=None, help="cap B on selected slots")
@@ -716,7 +728,7 @@ def main() -> int:
         name, mode_name = item.split(":")
         sp = synth.CONFIGS[name]
         try:
-            o, _, _ = measure_chain(dv, sp, mode_name, sp.budgets[-1], steps=20, warmup=3,
+            o, _, _ = measure_chain(dv, sp, mode_name, sp.budgets[-1], steps=20, warmup=args.warmup,
                                     samples=20, cold_samples=5, profile_steps=5, stages=False)
         except RuntimeError as e:
             log(f"[bench] {name}/{mode_name}: {e}")
