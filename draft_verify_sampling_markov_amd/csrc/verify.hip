@@ -240,34 +240,43 @@ __device__ __forceinline__ float corr_weight(float zt, float zd, float bt, float
   return fmaxf(pt - pd, 0.0f);
 }
 
-// q and p_t for the 16 entries a lane holds (invalid entries: 0). FAST: take
-// an unmasked path when every lane of the wave holds 16 valid entries (it
-// costs registers, which the two-block engine shape does not have to spare).
+// Sums over the 16 entries a lane holds of q (max(0, p_t - p_d) for a
+// residual, p_t for a bonus) and of p_t, added in entry order (invalid
+// entries: 0). Each entry takes exactly corr_weight's operations, and is
+// added as soon as it is formed, which keeps few values live. FAST: take an
+// unmasked path when every lane of the wave holds 16 valid entries (it costs
+// registers, which the two-block engine shape does not have to spare).
 template <bool BF16, bool FAST>
-__device__ __forceinline__ void corr_tile_values(const f32x4 acc[4], const float zt16[16],
-                                                 const float u16[16], int nvalid, float bt,
-                                                 float bd, bool residual, float q[16],
-                                                 float pt[16]) {
+__device__ __forceinline__ void corr_tile_sums(const f32x4 acc[4], const float zt16[16],
+                                               const float u16[16], int nvalid, float bt,
+                                               float bd, bool residual, float& sq, float& sp) {
+  sq = 0.0f;
+  sp = 0.0f;
   if (FAST && __all(nvalid >= 16)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = 4 * j + i;
-        q[idx] = corr_weight(zt16[idx], acc[j][i] + u16[idx], bt, bd, residual);
-        pt[idx] = shifted_exp(zt16[idx], bt);
+        sq += corr_weight(zt16[idx], acc[j][i] + u16[idx], bt, bd, residual);
+        sp += shifted_exp(zt16[idx], bt);
       }
     return;
   }
+  // masked entries get the exponent -inf, so both exponentials give 0 with
+  // no branch around them (a select of the result lets the compiler branch
+  // per entry)
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = 4 * j + i;
       const bool ok = idx < nvalid;
-      const float zd = acc[j][i] + u16[idx];
-      q[idx] = ok ? corr_weight(zt16[idx], zd, bt, bd, residual) : 0.0f;
-      pt[idx] = ok ? shifted_exp(zt16[idx], bt) : 0.0f;
+      const float et = ok ? fmaf(zt16[idx], kLog2e, bt) : -INFINITY;
+      const float ed = ok ? fmaf(acc[j][i] + u16[idx], kLog2e, bd) : -INFINITY;
+      const float ptv = __builtin_amdgcn_exp2f(et);
+      sq += residual ? fmaxf(ptv - __builtin_amdgcn_exp2f(ed), 0.0f) : ptv;
+      sp += ptv;
     }
 }
 
@@ -318,17 +327,12 @@ struct ResidualEpi {
   }
   __device__ __forceinline__ void finish(const St& s, int v0, int nvalid, const f32x4 acc[4],
                                          const Pre& p, int t, int lane) const {
-    float zt16[16], u16[16], q[16], pt[16];
+    float zt16[16], u16[16];
     unpack16<BF16>(p.zt, zt16);
     unpack16<BF16>(p.u, u16);
-    corr_tile_values<BF16, FAST>(acc, zt16, u16, (s.active ? nvalid : 0), s.bt, s.bd, s.residual,
-                                 q, pt);
-    float sq = 0.0f, sp = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sq += q[i];
-      sp += pt[i];
-    }
+    float sq, sp;
+    corr_tile_sums<BF16, FAST>(acc, zt16, u16, (s.active ? nvalid : 0), s.bt, s.bd, s.residual,
+                               sq, sp);
     sq = pair_sum<false>(pair_sum<true>(sq));
     sp = pair_sum<false>(pair_sum<true>(sp));
     if ((lane >> 4) == 0 && s.active) rpart[(size_t)s.ng * ldn + part_pos(t, c)] = make_float2(sq, sp);
