@@ -242,42 +242,62 @@ __device__ __forceinline__ float corr_weight(float zt, float zd, float bt, float
 
 // Sums over the 16 entries a lane holds of q (max(0, p_t - p_d) for a
 // residual, p_t for a bonus) and of p_t, added in entry order (invalid
-// entries: 0). Each entry takes exactly corr_weight's operations, and is
-// added as soon as it is formed, which keeps few values live. FAST: take an
-// unmasked path when every lane of the wave holds 16 valid entries (it costs
-// registers, which the two-block engine shape does not have to spare).
+// entries: 0); each entry takes exactly corr_weight's operations.
+// FAST (the one-block engine shape, which has registers to spare): an
+// unmasked path when every lane of the wave holds 16 valid entries, and the
+// masked one (a select after the exponentials) only on a ragged tile.
+// Otherwise (the two-block shape, where every tile takes the masked path):
+// masked entries get the exponent -inf, so both exponentials give 0 with no
+// branch around them (after a select of the result the compiler branched per
+// entry), and each entry is added as soon as it is formed, which keeps few
+// values live.
 template <bool BF16, bool FAST>
 __device__ __forceinline__ void corr_tile_sums(const f32x4 acc[4], const float zt16[16],
                                                const float u16[16], int nvalid, float bt,
                                                float bd, bool residual, float& sq, float& sp) {
   sq = 0.0f;
   sp = 0.0f;
-  if (FAST && __all(nvalid >= 16)) {
+  if constexpr (FAST) {
+    float q[16], pt[16];
+    if (__all(nvalid >= 16)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = 4 * j + i;
+          q[idx] = corr_weight(zt16[idx], acc[j][i] + u16[idx], bt, bd, residual);
+          pt[idx] = shifted_exp(zt16[idx], bt);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = 4 * j + i;
+          const bool ok = idx < nvalid;
+          q[idx] = ok ? corr_weight(zt16[idx], acc[j][i] + u16[idx], bt, bd, residual) : 0.0f;
+          pt[idx] = ok ? shifted_exp(zt16[idx], bt) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sq += q[i];
+      sp += pt[i];
+    }
+  } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = 4 * j + i;
-        sq += corr_weight(zt16[idx], acc[j][i] + u16[idx], bt, bd, residual);
-        sp += shifted_exp(zt16[idx], bt);
+        const bool ok = idx < nvalid;
+        const float et = ok ? fmaf(zt16[idx], kLog2e, bt) : -INFINITY;
+        const float ed = ok ? fmaf(acc[j][i] + u16[idx], kLog2e, bd) : -INFINITY;
+        const float ptv = __builtin_amdgcn_exp2f(et);
+        sq += residual ? fmaxf(ptv - __builtin_amdgcn_exp2f(ed), 0.0f) : ptv;
+        sp += ptv;
       }
-    return;
   }
-  // masked entries get the exponent -inf, so both exponentials give 0 with
-  // no branch around them (a select of the result lets the compiler branch
-  // per entry)
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = 4 * j + i;
-      const bool ok = idx < nvalid;
-      const float et = ok ? fmaf(zt16[idx], kLog2e, bt) : -INFINITY;
-      const float ed = ok ? fmaf(acc[j][i] + u16[idx], kLog2e, bd) : -INFINITY;
-      const float ptv = __builtin_amdgcn_exp2f(et);
-      sq += residual ? fmaxf(ptv - __builtin_amdgcn_exp2f(ed), 0.0f) : ptv;
-      sp += ptv;
-    }
 }
 
 // ---------------------------------------------------------------------------
