@@ -52,7 +52,10 @@ struct SchedShared {
   unsigned long long orig[kSchedMaxKeys];  // keys in index order
   unsigned long long a[kSchedMaxKeys];     // radix ping-pong buffers; result in a
   unsigned long long b[kSchedMaxKeys];
-  uint32_t hist[kRadixBuckets * kSchedMaxRows];  // also the prefix sums afterwards
+  // radix passes: per (row, digit) counts, row-major, then their prefix down
+  // each digit's column; the scan of the sorted values afterwards
+  uint32_t hist[kRadixBuckets * kSchedMaxRows];
+  uint32_t dbase[kRadixBuckets];  // keys of smaller digits
   uint32_t wsum[kSchedWaves];
   unsigned long long th[kSchedWaves];
   int k[kSchedWaves];
@@ -104,8 +107,11 @@ __device__ __forceinline__ void block_exclusive_scan(uint32_t* x, int n, uint32_
 
 // One stable counting pass on digit (code >> shift) & 127 of NR rows of 64
 // keys: a key's place = keys of smaller digits + keys of its digit in earlier
-// rows (digit-major histogram scan) + earlier keys of its digit in its row
-// (ballot masks).
+// rows + earlier keys of its digit in its row. The last is a ballot match; the
+// last key of each digit in a row writes the row's count of that digit (the
+// wave that owns the row clears the row's counts first). Wave 0 then runs the
+// prefix down each digit's column (lane l: digits 2l, 2l+1) and the digit
+// bases, with no workgroup-wide scan.
 __device__ __forceinline__ void radix_pass(const unsigned long long* src, unsigned long long* dst, int NR,
                            int shift, SchedShared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -122,31 +128,48 @@ __device__ __forceinline__ void radix_pass(const unsigned long long* src, unsign
     if (row < NR) {  // wave-uniform
       const unsigned long long key = src[row * kWave + lane];
       const int d = (int)((key >> (32 + shift)) & (kRadixBuckets - 1));
-      unsigned long long B[kRadixBits];
-#pragma unroll
-      for (int bt = 0; bt < kRadixBits; ++bt) B[bt] = __ballot((d >> bt) & 1);
       unsigned long long m = ~0ull;
 #pragma unroll
-      for (int bt = 0; bt < kRadixBits; ++bt) m &= ((d >> bt) & 1) ? B[bt] : ~B[bt];
-      rk[u] = __popcll(m & below);
-#pragma unroll
-      for (int h = 0; h < kRadixBuckets / kWave; ++h) {
-        const int dd = lane + kWave * h;
-        unsigned long long mm = ~0ull;
-#pragma unroll
-        for (int bt = 0; bt < kRadixBits; ++bt) mm &= ((dd >> bt) & 1) ? B[bt] : ~B[bt];
-        sh.hist[dd * NR + row] = (uint32_t)__popcll(mm);
+      for (int bt = 0; bt < kRadixBits; ++bt) {
+        const unsigned long long B = __ballot((d >> bt) & 1);
+        m &= ((d >> bt) & 1) ? B : ~B;
       }
+      rk[u] = __popcll(m & below);
+      uint32_t* h = sh.hist + row * kRadixBuckets;
+      h[lane] = 0u;
+      h[lane + kWave] = 0u;
+      if ((m >> lane) == 1ull) h[d] = (uint32_t)rk[u] + 1u;  // no later key of this digit
       kk[u] = key;
       dig[u] = d;
     }
   }
   __syncthreads();
-  block_exclusive_scan(sh.hist, kRadixBuckets * NR, sh.wsum);
+  if (wave == 0) {
+    uint32_t run0 = 0u, run1 = 0u;
+    uint2* col = reinterpret_cast<uint2*>(sh.hist) + lane;  // digits 2 lane, 2 lane + 1
+    constexpr int kBatch = 8;  // rows read before their prefixes are written
+    for (int r0 = 0; r0 < NR; r0 += kBatch) {  // uniform
+      uint2 c[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) c[i] = r0 + i < NR ? col[(r0 + i) * (kRadixBuckets / 2)] : make_uint2(0u, 0u);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (r0 + i < NR) col[(r0 + i) * (kRadixBuckets / 2)] = make_uint2(run0, run1);
+        run0 += c[i].x;
+        run1 += c[i].y;
+      }
+    }
+    const uint32_t pair = run0 + run1;
+    const uint32_t ex = wave_inclusive_scan_u32(pair) - pair;
+    sh.dbase[2 * lane] = ex;
+    sh.dbase[2 * lane + 1] = ex + run0;
+  }
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < kRowsPerWave; ++u) {
     const int row = wave + kSchedWaves * u;
-    if (row < NR) dst[sh.hist[dig[u] * NR + row] + rk[u]] = kk[u];
+    if (row < NR)
+      dst[sh.dbase[dig[u]] + sh.hist[row * kRadixBuckets + dig[u]] + rk[u]] = kk[u];
   }
   __syncthreads();
 }
@@ -222,18 +245,14 @@ __device__ __forceinline__ void schedule_body(
       sh.k[wave] = best_k;
     }
     __syncthreads();
-    unsigned long long bt = sh.th[0];
-    int bk = sh.k[0];
-    for (int w = 1; w < kSchedWaves; ++w) {
-      if (mode == DSPARK_SCHED_ARGMAX) {
-        if (sh.k[w] != 0x7fffffff &&
-            (bk == 0x7fffffff || sh.th[w] > bt || (sh.th[w] == bt && sh.k[w] < bk))) {
-          bt = sh.th[w];
-          bk = sh.k[w];
-        }
-      } else {
-        bk = min(bk, sh.k[w]);
-      }
+    // every wave reduces the waves' results itself (lanes 0..15). A wave
+    // without a candidate holds (0, INT_MAX), which no candidate loses to.
+    unsigned long long bt = lane < kSchedWaves ? sh.th[lane] : 0ull;
+    int bk = lane < kSchedWaves ? sh.k[lane] : 0x7fffffff;
+    if (mode == DSPARK_SCHED_ARGMAX) {
+      wave_argmax_u64(bt, bk);
+    } else {
+      bk = wave_min_int(bk);
     }
     if (mode == DSPARK_SCHED_GREEDY && bk == 0x7fffffff) bk = K_cap;
     if (bk == 0x7fffffff) bk = 0;
