@@ -420,38 +420,44 @@ __device__ __forceinline__ void wave_argmax_u64(unsigned long long& th, int& k) 
 }
 
 // Dot product of `len` stored elements with float weights, by one wave: 16-byte
-// loads when `vec` (len a multiple of the vector width, rows aligned), all of a
-// lane's loads issued before the sums.
+// loads when `vec` (len a multiple of the vector width, rows and weights
+// aligned). All of a lane's loads, of the elements and of their weights, go
+// out from clamped addresses before the first product (a load under a bounds
+// branch would wait for the sums before it); the products are then summed in
+// chunk and element order.
 template <bool BF16>
 __device__ __forceinline__ float wave_dot(const typename Elem<BF16>::T* __restrict__ x,
                                           const float* __restrict__ w, int len, bool vec, int lane) {
   constexpr int VEC = Elem<BF16>::kVec;
+  constexpr int WV = VEC / 4;  // weight vectors of four per chunk
   float acc = 0.0f;
   if (vec) {
     const int nv = len / VEC;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    constexpr int U = 4;
+    const f32x4* wv = reinterpret_cast<const f32x4*>(w);
+    constexpr int U = 8;  // chunks per lane and round: 4096 bfloat16 elements per wave
     for (int base = 0; base < nv; base += U * kWave) {
       u32x4 q[U];
+      f32x4 wt[U][WV];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const int c = base + i * kWave + lane;
-        q[i] = c < nv ? xv[c] : u32x4{0u, 0u, 0u, 0u};
+        const int c = min(base + i * kWave + lane, nv - 1);
+        q[i] = xv[c];
+#pragma unroll
+        for (int t = 0; t < WV; ++t) wt[i][t] = wv[(size_t)c * WV + t];
       }
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const int c = base + i * kWave + lane;
-        if (c < nv) {
-          const float* wc = w + c * VEC;
+        if (base + i * kWave + lane < nv) {
           if constexpr (BF16) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              acc += __uint_as_float(q[i][e] << 16) * wc[2 * e];
-              acc += __uint_as_float(q[i][e] & 0xFFFF0000u) * wc[2 * e + 1];
+              acc += __uint_as_float(q[i][e] << 16) * wt[i][(2 * e) / 4][(2 * e) % 4];
+              acc += __uint_as_float(q[i][e] & 0xFFFF0000u) * wt[i][(2 * e + 1) / 4][(2 * e + 1) % 4];
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc += __uint_as_float(q[i][e]) * wc[e];
+            for (int e = 0; e < 4; ++e) acc += __uint_as_float(q[i][e]) * wt[i][0][e];
           }
         }
       }
