@@ -441,10 +441,12 @@ __device__ __forceinline__ float wave_dot(const typename Elem<BF16>::T* __restri
       f32x4 wt[U][WV];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const int c = min(base + i * kWave + lane, nv - 1);
-        q[i] = xv[c];
+        if (base + i * kWave < nv) {  // wave-uniform: chunk groups past the end are not loaded
+          const int c = min(base + i * kWave + lane, nv - 1);
+          q[i] = xv[c];
 #pragma unroll
-        for (int t = 0; t < WV; ++t) wt[i][t] = wv[(size_t)c * WV + t];
+          for (int t = 0; t < WV; ++t) wt[i][t] = wv[(size_t)c * WV + t];
+        }
       }
 #pragma unroll
       for (int i = 0; i < U; ++i) {
