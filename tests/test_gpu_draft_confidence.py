@@ -11,7 +11,9 @@ bfloat16 and float32, hidden sizes and ranks that are not multiples of the
 vector width (scalar dot products), inverse temperatures on and off; both
 placements of the head (in the GEMM prologue when few of the GEMM's
 workgroups carry a request, e.g. 64 requests over a 151936 vocabulary; a launch
-of its own after the draft otherwise, e.g. 256 requests).
+of its own after the draft otherwise, e.g. 256 requests). A last test checks
+the confidence call against the oracle at hidden sizes past one round of
+the dot product's loads.
 """
 import numpy as np
 import pytest
@@ -68,3 +70,33 @@ def test_fused_equals_two_calls(dv, R, gamma, V, r, d, dtype, temps):
         assert np.array_equal(a.view(np.uint32), c.view(np.uint32)), name
     assert np.all(np.diff(got[4], axis=1) <= 0)       # survival never grows along a request
     log(f"[draft+conf] R={R} gamma={gamma} V={V}: bit-identical")
+
+
+# hidden sizes past one round of the dot product's loads (512 16-byte chunks
+# per wave): 520 (two chunk groups), 8200 (three rounds, the last with one
+# chunk), a float32 row of 4100, and 8201 (not a multiple of the vector
+# width: the scalar path)
+@pytest.mark.parametrize("d,dtype", [(520, "bf16"), (8200, "bf16"), (4100, "f32"), (8201, "bf16")])
+def test_confidence_long_hidden_rows_against_oracle(dv, d, dtype):
+    import torch
+    import oracle
+    R, gamma, V, r = 6, 3, 700, 72
+    log(f"[conf long d] R={R} gamma={gamma} d={d} {dtype}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(d)
+    h = torch.randn((R, gamma, d), generator=g).to(tdt)
+    W1 = (torch.randn((V, r), generator=g) * 0.3).to(tdt)
+    w = torch.randn((d + r,), generator=g) * 0.05
+    anchor = torch.randint(0, V, (R,), generator=g, dtype=torch.int32)
+    tokens = torch.randint(0, V, (R, gamma), generator=g, dtype=torch.int32)
+    b = -0.3
+    logit = torch.empty((R, gamma), dtype=torch.float32, device="cuda")
+    conf, surv = dv.confidence(h.cuda(), W1.cuda(), anchor.cuda(), tokens.cuda(), w.cuda(), b,
+                               logit=logit)
+    torch.cuda.synchronize()
+    ref = oracle.confidence(h.float().numpy(), W1.float().numpy(), anchor.numpy(), tokens.numpy(),
+                            w.numpy(), b)
+    # fp32 sums of d + r products of size ~0.05 against the float64 oracle
+    np.testing.assert_allclose(logit.cpu().numpy(), ref["logit"], rtol=0, atol=2e-4)
+    np.testing.assert_allclose(conf.cpu().numpy(), ref["conf"], rtol=0, atol=5e-5)
+    np.testing.assert_allclose(surv.cpu().numpy(), ref["surv"], rtol=0, atol=5e-5)
