@@ -32,8 +32,10 @@
 
 namespace dspark {
 
-constexpr int kRowChunk = 8192;  // vocabulary entries per row-partial workgroup
-constexpr int kRowThreads = 256;
+// vocabulary entries per row-partial workgroup, 32 per thread (measured on
+// MI355X: 16384 entries over 512 threads beat 8192 over 256 by 3-7%)
+constexpr int kRowChunk = 16384;
+constexpr int kRowThreads = 512;
 
 inline int n_row_chunks(int V) { return ceil_div(V, kRowChunk); }
 
@@ -676,7 +678,11 @@ static int launch_verify(const void* target, int M_cap, const int32_t* cu, const
                        tg, V, nch, cu, R, rows_ws, ws.rowpart);
   int st = launch_status();
   if (st) return st;
-  if (nch <= 32)
+  if (nch <= 16)
+    hipLaunchKernelGGL((decide_kernel<BF16, 16>), dim3(ceil_div(R, 4)), dim3(256), 0, s, tg, V, nch,
+                       ws.rowpart, cu, anchor, tokens, p_draft, lse_draft, win_len, mode, seed, step,
+                       req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
+  else if (nch <= 32)
     hipLaunchKernelGGL((decide_kernel<BF16, 32>), dim3(ceil_div(R, 4)), dim3(256), 0, s, tg, V, nch,
                        ws.rowpart, cu, anchor, tokens, p_draft, lse_draft, win_len, mode, seed, step,
                        req_ids, R, gamma, rows_ws, ws.jobs, accept_len, out_tokens, n_out, ceiling);
