@@ -33,7 +33,7 @@
 namespace dspark {
 
 // vocabulary entries per row-partial workgroup, 32 per thread (measured on
-// MI355X: 16384 entries over 512 threads beat 8192 over 256 by 3-7%)
+// MI355X: 16384 entries over 512 threads beat 8192 over 256 by 2-8%)
 constexpr int kRowChunk = 16384;
 constexpr int kRowThreads = 512;
 
