@@ -9,7 +9,9 @@ steps use it. Cases: the three scheduler modes, a stale budget array, full
 blocks (pack_windows off) and scheduled windows, an empty budget, the row
 limit R (gamma + 1) = 4096, and a total that exceeds every tier. The
 full-block pack (no window array) must also equal the scanned pack of
-windows that are all gamma.
+windows that are all gamma. A seeded randomised test checks the scheduler
+call itself against the oracle over 120 cases (ties, flat rows, NaN and
+out-of-range survivals, zero cost-table entries, all three modes).
 """
 import numpy as np
 import pytest
@@ -95,3 +97,62 @@ def test_full_block_pack_equals_scanned_pack(dv, R, gamma, extra):
         assert np.array_equal(a[k].cpu().numpy(), b[k].cpu().numpy()), k
     assert a["totals"].cpu().numpy().tolist()[0] == R * (gamma + 1)
     log(f"[pack] full blocks R={R} gamma={gamma} M_cap={M_cap}: index path == scanned path")
+
+
+def _random_survivals(rng, kind, R, gamma):
+    """Survival arrays of six kinds: products of random confidences, four
+    distinct levels (many ties), one value everywhere, zeros and ones, values
+    out of [0, 1] with NaNs, and values a few quantisation steps (2^-20) apart."""
+    if kind == 0:
+        return np.cumprod(rng.uniform(0.05, 1.0, (R, gamma)), axis=1).astype(np.float32)
+    if kind == 1:
+        lv = np.array([1.0, 0.75, 0.5, 0.25], np.float32)
+        return np.sort(lv[rng.integers(0, 4, (R, gamma))], axis=1)[:, ::-1].copy()
+    if kind == 2:
+        return np.full((R, gamma), np.float32(rng.uniform(0, 1)), np.float32)
+    if kind == 3:
+        return np.sort(rng.choice(np.array([0.0, 1.0], np.float32), (R, gamma)), axis=1)[:, ::-1].copy()
+    if kind == 4:
+        a = rng.uniform(-0.5, 1.5, (R, gamma)).astype(np.float32)
+        a[rng.random((R, gamma)) < 0.05] = np.nan
+        return a
+    return (rng.uniform(0.2, 0.9) + rng.integers(-3, 4, (R, gamma)) * 2.0 ** -20).astype(np.float32)
+
+
+def test_randomised_scheduler_against_oracle(dv):
+    """120 seeded random cases of the scheduler call against the oracle: request
+    counts up to 512 and gamma up to 16 (keys up to the 4096-row limit), the
+    three modes, random budgets, stale budget arrays, cost tables with zero
+    entries, and the survival kinds above (ties at every radix digit, flat
+    rows, NaN and out-of-range values)."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(2024)
+    for case in range(120):
+        while True:
+            gamma = int(rng.integers(1, 17))
+            R = int(rng.integers(1, 513))
+            if R * (gamma + 1) <= 4096:
+                break
+        kind = case % 6
+        surv = _random_survivals(rng, kind, R, gamma)
+        M_max = min(4096, R * (gamma + 1) + int(rng.integers(0, 64)))
+        m = np.arange(M_max + 1)
+        sps = np.maximum(1, 1e6 / (1.0 + 0.002 * m + rng.uniform(0, 0.01, M_max + 1))).astype(np.uint32)
+        if case % 7 == 0:
+            sps[rng.integers(0, M_max + 1, 5)] = 0
+        B_cap = int(rng.integers(0, R * gamma + 6))
+        mode = int(rng.integers(0, 3))
+        K_fixed = int(rng.integers(0, R * gamma + 3))
+        budget = (np.clip(surv * rng.uniform(0.5, 1.2), 0, 1).astype(np.float32)
+                  if case % 5 == 0 else None)
+        ref = oracle.schedule_topb(surv, [int(x) for x in sps], B_cap, mode, K_fixed, budget)
+        win, K = dv.schedule_topb(
+            torch.from_numpy(surv).cuda(), torch.from_numpy(sps.view(np.int32)).cuda(), B_cap=B_cap,
+            mode=mode, K_fixed=K_fixed,
+            surv_budget=None if budget is None else torch.from_numpy(budget).cuda())
+        torch.cuda.synchronize()
+        label = f"case {case}: kind {kind} R {R} gamma {gamma} mode {mode} B {B_cap}"
+        assert win.cpu().numpy().tolist() == list(ref["win_len"]), label
+        assert int(K.cpu()[0]) == ref["K"], label
+    log("[schedule] 120 random cases equal the oracle")
