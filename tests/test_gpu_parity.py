@@ -123,6 +123,44 @@ def test_step_and_seed_change_draws(dv):
                                    dict(R=1, gamma=16, V=65, r=8, d=8, dtype="bf16"),
                                    dict(R=3, gamma=2, V=64, r=32, d=16, dtype="bf16")],
                          ids=["V1-gamma1-r1", "gamma16-V65", "one-tile"])
+def _random_chain_shapes(n, seed):
+    """n seeded (R, gamma, V, r, d, dtype, verify mode, scheduler mode) draws:
+    request counts on and around the engine's 16-request blocks and its
+    one-, two- and multi-group shapes (1 .. 300), vocabularies from one tile to
+    several row-pass chunks with ragged tails (64 .. 33000), ranks from 16 to
+    256 (some not a multiple of the vector width), hidden sizes up to 520."""
+    rng = np.random.default_rng(seed)
+    modes = ["static", "compact", "cap_accept"]
+    out = []
+    for case in range(n):
+        while True:
+            R = int(rng.choice([1, 3, 17, 64, 129, 150, 200, 256, 300]))
+            gamma = int(rng.integers(1, 9))
+            if R * (gamma + 1) <= 4096:
+                break
+        V = int(rng.choice([64, 700, 1500, 2047, 3000, 16400, 33000]))
+        r = int(rng.choice([16, 32, 64, 100, 256]))
+        d = int(rng.choice([8, 40, 96, 520]))
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        if dtype == "f32" and r > 128:
+            r = 100
+        out.append(dict(R=R, gamma=gamma, V=V, r=r, d=d, dtype=dtype, vmode=modes[case % 3],
+                        smode=int(rng.integers(0, 3)), K_fixed=int(rng.integers(0, R * gamma + 1)),
+                        sseed=int(rng.integers(1, 10**6)), seed=int(rng.integers(0, 1000)),
+                        step=int(rng.integers(0, 1000))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_chain_shapes(10, 11), ids=lambda c: (
+    f"R{c['R']}-g{c['gamma']}-V{c['V']}-r{c['r']}-{c['dtype']}-{c['vmode']}-s{c['smode']}"))
+def test_random_small_chains(dv, case):
+    """Seeded random shapes, every request of every stage against the oracle."""
+    sp = synth.small_spec(f"rand{case['sseed']}", R=case["R"], gamma=case["gamma"], V=case["V"],
+                          r=case["r"], d=case["d"], dtype=case["dtype"], seed=case["sseed"])
+    run_and_check(dv, sp, case["vmode"], smode=case["smode"], K_fixed=case["K_fixed"],
+                  seed=case["seed"], step=case["step"])
+
+
 def test_degenerate_sizes(dv, shape):
     # a one-entry vocabulary (every draft is token 0 with probability 1, every
     # accept test passes), the longest block, exactly one vocabulary tile; each
