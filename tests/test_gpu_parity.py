@@ -115,14 +115,6 @@ def test_step_and_seed_change_draws(dv):
     assert not np.array_equal(a["tokens"], c["tokens"])
 
 
-# ---------------------------------------------------------------------------
-# edge cases: degenerate sizes, an empty budget, the row limit
-# ---------------------------------------------------------------------------
-
-@pytest.mark.parametrize("shape", [dict(R=1, gamma=1, V=1, r=1, d=4, dtype="f32"),
-                                   dict(R=1, gamma=16, V=65, r=8, d=8, dtype="bf16"),
-                                   dict(R=3, gamma=2, V=64, r=32, d=16, dtype="bf16")],
-                         ids=["V1-gamma1-r1", "gamma16-V65", "one-tile"])
 def _random_chain_shapes(n, seed):
     """n seeded (R, gamma, V, r, d, dtype, verify mode, scheduler mode) draws:
     request counts on and around the engine's 16-request blocks and its
@@ -161,6 +153,14 @@ def test_random_small_chains(dv, case):
                   seed=case["seed"], step=case["step"])
 
 
+# ---------------------------------------------------------------------------
+# edge cases: degenerate sizes, an empty budget, the row limit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [dict(R=1, gamma=1, V=1, r=1, d=4, dtype="f32"),
+                                   dict(R=1, gamma=16, V=65, r=8, d=8, dtype="bf16"),
+                                   dict(R=3, gamma=2, V=64, r=32, d=16, dtype="bf16")],
+                         ids=["V1-gamma1-r1", "gamma16-V65", "one-tile"])
 def test_degenerate_sizes(dv, shape):
     # a one-entry vocabulary (every draft is token 0 with probability 1, every
     # accept test passes), the longest block, exactly one vocabulary tile; each
