@@ -522,30 +522,38 @@ extern "C" int dspark_cost_table_prepare(const double* raw_step_time_s, int M_ma
   if (M_max < 0) return DSPARK_ESIZE;
   int st = check_tiers(tiers, n_tiers);
   if (st) return st;
-  // running maximum: a profiled curve is forced monotone in M
-  double* mono = new double[(size_t)M_max + 1];
-  double run = -INFINITY;
-  for (int m = 0; m <= M_max; ++m) {
-    const double t = raw_step_time_s[m];
-    if (t > run) run = t;
-    mono[m] = run;
+  // running maximum: a profiled curve is forced monotone in M. The staircase
+  // reads it at the tiers only, so those values are taken in one pass first
+  // (no buffer: nothing here allocates, so the call cannot throw)
+  double at_tier[kMaxTiers];
+  if (staircase) {
+    double run = -INFINITY;
+    int i = 0;
+    for (int m = 0; m <= M_max && i < n_tiers; ++m) {
+      const double t = raw_step_time_s[m];
+      if (t > run) run = t;
+      while (i < n_tiers && (tiers[i] < M_max ? tiers[i] : M_max) == m) at_tier[i++] = run;
+    }
   }
+  double run = -INFINITY;
   for (int m = 0; m <= M_max; ++m) {
     double T;
     if (staircase) {
       int tier = -1;
       for (int i = 0; i < n_tiers; ++i)
         if (tiers[i] >= m) {
-          tier = tiers[i];
+          tier = i;
           break;
         }
       if (tier < 0) {
         sps_milli[m] = 0;
         continue;
       }
-      T = mono[tier < M_max ? tier : M_max];
+      T = at_tier[tier];
     } else {
-      T = mono[m];
+      const double t = raw_step_time_s[m];
+      if (t > run) run = t;
+      T = run;
     }
     if (!(T > 0.0) || std::isinf(T)) {
       sps_milli[m] = 0;
@@ -556,6 +564,5 @@ extern "C" int dspark_cost_table_prepare(const double* raw_step_time_s, int M_ma
     if (v > 4294967295.0) v = 4294967295.0;
     sps_milli[m] = (uint32_t)v;
   }
-  delete[] mono;
   return DSPARK_OK;
 }

@@ -202,6 +202,24 @@ def test_cost_table_matches_oracle(name):
     assert got.shape[0] == sp.M_max + 1
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_cost_table_random_curves_match_oracle(seed):
+    """Noisy, non-monotone curves with NaN, negative and infinite entries, and
+    tier lists that reach past M_max, in both table shapes."""
+    dv, lib = _lib()
+    rng = np.random.default_rng(seed)
+    M_max = int(rng.integers(0, 300))
+    raw = rng.uniform(-1e-3, 5e-3, M_max + 1)
+    for bad in (np.nan, np.inf, -np.inf, 0.0):
+        raw[rng.integers(0, M_max + 1, 3)] = bad
+    n = int(rng.integers(1, 33))
+    tiers = np.unique(rng.integers(1, 2 * M_max + 3, n)).tolist()
+    for staircase in (False, True):
+        got = dv.cost_table_prepare(raw.tolist(), tiers, staircase)
+        ref = oracle.cost_table_prepare(raw.tolist(), tiers, staircase)
+        assert got.tolist() == ref, (seed, staircase)
+
+
 def test_cost_table_rejects_bad_tiers():
     dv, lib = _lib()
     with pytest.raises(dv.DsparkError):
