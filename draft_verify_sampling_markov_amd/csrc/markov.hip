@@ -463,7 +463,7 @@ static bool u_vec_ok(const void* U, long long ldU, int V) {
 
 // Engine shape of a GEMM launch over Rg requests: waves per workgroup (4 up to
 // four 16-request blocks, else 8) and the grid (up to two 4-wave or one
-// 8-wave workgroup per CU, as few as finish in the same number of tile rounds).
+// 8-wave workgroup per CU).
 static int partials_waves(int Rg) { return ceil_div(Rg, kTileN) <= 4 ? 4 : 8; }
 static int partials_grid(int nw, int V) {
   return engine_grid(n_vtiles(V), device_cu_count() * (nw == 4 ? 2 : 1));
