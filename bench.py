@@ -16,8 +16,9 @@ slots per second over exactly --steps steps), per-step statistics over
 individually timed steps (median, p10, p90; warm and after a 512 MiB cache
 flush), the roofline of the dominant kernel (the per-slot bias GEMM +
 softmax-partials pass, timed with HIP events on the chain's stream) with its
-algorithmic bytes counting W2 once per block, the same figures for the other
-named workloads, the bandwidth and matrix rate this GPU reaches (two probe
+algorithmic bytes counting W2 once per block, the verify stage against the
+bytes of its two passes, the same figures for the other named workloads
+(without the stage timings), the bandwidth and matrix rate this GPU reaches (two probe
 kernels of the library), and the CPU oracle timed on a bounded sample of the
 headline workload on this host.
 
@@ -340,6 +341,21 @@ def draft_algorithmic(spec):
     return {"bytes": g * R * V * b + r * V * b + g * R * r * b, "flops": 2 * g * R * r * V}
 
 
+def verify_algorithmic(spec, res):
+    """The verify's algorithmic bytes for one step's results: pass 1 reads every
+    verified packed row (M_v = the pack's total), pass 2 one target row per
+    request, the U row of each request whose correction is a residual (accept
+    length below its commit window) and W2 once."""
+    import numpy as np
+    b = _spec_bytes(spec)
+    R, g, V, r = spec.R, spec.gamma, spec.V, spec.r
+    M_v = int(res["totals"][0])
+    commit = np.clip(res["win_len"], 0, g) if res.get("win_len") is not None else np.full(R, g)
+    R_rej = int(np.sum(res["accept_len"] < commit))
+    return {"pass1": M_v * V * b, "pass2": (R + R_rej) * V * b + r * V * b, "rows": M_v,
+            "residual_requests": R_rej}
+
+
 def _stats(ms):
     import numpy as np
     a = np.asarray(ms, dtype=np.float64)
@@ -466,6 +482,19 @@ def measure_chain(dv, spec, mode_name: str, B_cap: int, *, steps: int, warmup: i
         prof = ch.results()
         if not np.array_equal(prof["tokens"], first["tokens"]):
             raise RuntimeError("the per-slot draft differs from the draft call")
+        # the verify stage against the algorithmic bytes of its two passes; the
+        # stage's time includes its latency launches (decide, residual draw)
+        va = verify_algorithmic(spec, dict(first, win_len=first["win_len"] if mode != dv.VERIFY_STATIC else None))
+        v_us = out["stages_ms"]["verify"] * 1e3
+        v_gbs = (va["pass1"] + va["pass2"]) / (v_us * 1e-6) / 1e9
+        out["verify_roofline"] = {
+            "bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(v_gbs / HBM_PEAK_GBS, 4), "stage_us": round(v_us, 2),
+            "pass1_bytes": va["pass1"], "pass2_bytes": va["pass2"], "verified_rows": va["rows"],
+            "residual_requests": va["residual_requests"],
+            "note": "whole verify stage (row pass, accept test, residual pass, residual draw) "
+                    "timed with events; bytes: every verified target row, then one target row "
+                    "per request, the U row of each residual request and W2"}
 
     # ---- the draft call alone, per kernel choice (graph of one call) ----
     def draft_call_ms(reps):
@@ -691,6 +720,7 @@ def main() -> int:
         "accepted_tokens_per_s": head["accepted_tokens_per_s"],
         "mean_accept_len": head["mean_accept_len"],
         "stages_ms": head.get("stages_ms"),
+        "verify_roofline": head.get("verify_roofline"),
         "draft_call": head["draft_call"],
         "roofline": head["roofline"],
     }

@@ -59,6 +59,17 @@ def test_json_line_contract():
     for key in ("step_ms", "step_ms_cache_cold"):
         st = d[key]
         assert st["p10"] <= st["median"] <= st["p90"] and st["n"] > 0
+    vr = d["verify_roofline"]
+    assert vr["bound"] == "hbm" and vr["unit"] == "GB/s" and vr["peak"] == 8000.0
+    assert abs(vr["frac"] - vr["achieved"] / vr["peak"]) < 1e-3
+    # static: every packed row of the full blocks, then one target row per
+    # request, the U rows of the residual requests and W2
+    assert vr["verified_rows"] == R * (g + 1)
+    assert vr["pass1_bytes"] == R * (g + 1) * V * b
+    assert vr["pass2_bytes"] == (R + vr["residual_requests"]) * V * b + r * V * b
+    assert vr["stage_us"] == pytest.approx(d["stages_ms"]["verify"] * 1e3, abs=0.1)
+    assert vr["achieved"] == pytest.approx((vr["pass1_bytes"] + vr["pass2_bytes"])
+                                           / (vr["stage_us"] * 1e-6) / 1e9, rel=2e-3)
     assert "tiny:compact" in d["other_workloads"]
     assert d["draft_call"]["per_slot_ms"] > 0
     pk = d["peaks_measured"]
