@@ -69,7 +69,7 @@ def test_json_line_contract():
     assert vr["pass2_bytes"] == (R + vr["residual_requests"]) * V * b + r * V * b
     assert vr["stage_us"] == pytest.approx(d["stages_ms"]["verify"] * 1e3, abs=0.1)
     assert vr["achieved"] == pytest.approx((vr["pass1_bytes"] + vr["pass2_bytes"])
-                                           / (vr["stage_us"] * 1e-6) / 1e9, rel=2e-3)
+                                           / (vr["stage_us"] * 1e-6) / 1e9, rel=2e-3, abs=0.06)
     assert "tiny:compact" in d["other_workloads"]
     assert d["draft_call"]["per_slot_ms"] > 0
     pk = d["peaks_measured"]
